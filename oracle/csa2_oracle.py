@@ -1,0 +1,320 @@
+"""Plain fp64 CPU oracle of the CSA2 layer hot path.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import or call this module.  It shares no code, table
+or helper with the HIP library.  Every function is the definition on the pages
+written out directly in numpy fp64: no blocking, fusion or reordering beyond
+what the definition states.  Python loops appear where the definition is a loop
+(blocks of the compressor, queries of the attention); sizes in the tests keep
+them short.
+
+Pages (cited by title and section / equation):
+  [CSA2 column]  daiw.org "CSA2：跨层共享的压缩稀疏注意力" (DeepSeek V4.1 Flash column):
+                 sections "保留了 CSA 的骨架" (skeleton), "三种模式：谁算、谁复用" (modes table),
+                 "解码器里的分层索引" (hierarchical indexer), "890 字节是怎么来的" (cache budget).
+  [Evolution blog] 0xnullpath "DeepSeek 的 Attention 演进 -【DSA、CSA、CSA2】":
+                 §2.2 (lightning indexer), §3.1 (gated pooling and overlap transform),
+                 §3.2 (sliding window), §4.1 (CSA2 compressor), §4.3 (sharing modes),
+                 §4.4 (hierarchical indexer).
+  [DSA-to-CSA notes] wineandchord "从 DSA 到 CSA/HCA：先压缩时间轴，再决定怎样寻址":
+                 eq. (9)-(12) overlapped compressor and its worked example, eq. (16)-(17)
+                 indexer and top-k, eq. (18)-(19) shared-KV MQA with its worked example,
+                 section "因果边界与短滑窗" (causal rule, window), eq. (27) sink,
+                 section "怎样验证" (checklist).
+
+Readings where the pages leave a step open (each also listed in the design notes):
+  * RoPE: theta = 10000, adjacent pairs (c-r+2u, c-r+2u+1), frequency theta^(-2u/r).
+  * Position of compressed entry i is pos0 + m*i (the first token of its block).
+  * RMSNorm: gamma = 1, eps = 1e-6, x / sqrt(mean(x^2) + eps).
+  * KV RMSNorm and RoPE happen when an entry is written; attention normalises and
+    rotates only the query, and inverse-rotates the output.
+  * Window rows for query t: positions [t-W+1, t] that the window buffer holds; no
+    de-duplication against selected entries.
+  * Top-k ties go to the lower index; -0 equals +0; output ascending, -1 padded.
+  * Hierarchical pool: the latest visible block is always selected, the other
+    n_keep-1 blocks by (score desc, block asc).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ============================================================ compressor
+def gated_pool(c_a, z_a, m, *, b_a=None, c_b=None, z_b=None, b_b=None, overlap=False):
+    """Gated per-channel softmax pooling over blocks of m tokens.
+
+    Non-overlap (CSA2, [Evolution blog] §4.1, and HCA eq. (22)-(23) of
+    [DSA-to-CSA notes]): entry i pools tokens [m*i, m*i+m); for every channel the
+    weights are a softmax over the m gate logits (Z + optional position bias B).
+
+    Overlap (CSA, [DSA-to-CSA notes] eq. (11)-(12)): entry i takes a per-channel
+    softmax over 2m candidates, the current block through (C^a, Z^a + B^a) and the
+    previous block through (C^b, Z^b + B^b).  Block 0 has no previous block: its
+    history logits are -inf and its history values 0, so they get zero weight.
+
+    Only complete blocks are pooled; a ragged tail of n % m tokens is ignored.
+    Inputs are [n, c]; biases are [m, c] or None (= 0).  Returns [n // m, c] fp64.
+    """
+    c_a = np.asarray(c_a, np.float64)
+    z_a = np.asarray(z_a, np.float64)
+    n, c = c_a.shape
+    ba = np.zeros((m, c)) if b_a is None else np.asarray(b_a, np.float64)
+    if overlap:
+        c_b = np.asarray(c_b, np.float64)
+        z_b = np.asarray(z_b, np.float64)
+        bb = np.zeros((m, c)) if b_b is None else np.asarray(b_b, np.float64)
+    out = np.zeros((n // m, c))
+    for i in range(n // m):
+        cur = slice(m * i, m * i + m)
+        logits = [z_a[cur] + ba]
+        values = [c_a[cur]]
+        if overlap:
+            if i == 0:
+                logits.append(np.full((m, c), -np.inf))
+                values.append(np.zeros((m, c)))
+            else:
+                prev = slice(m * (i - 1), m * i)
+                logits.append(z_b[prev] + bb)
+                values.append(c_b[prev])
+        lg = np.concatenate(logits, axis=0)
+        vals = np.concatenate(values, axis=0)
+        p = np.exp(lg - lg.max(axis=0))
+        p = p / p.sum(axis=0)
+        out[i] = (p * vals).sum(axis=0)
+    return out
+
+
+def gated_pool_weights(z_a, m, *, b_a=None, z_b=None, b_b=None, overlap=False):
+    """The softmax weights of `gated_pool`, [n//m, m or 2m, c]; the history half
+    (overlap) is the second m rows.  Used by the tests that check zero history mass."""
+    z_a = np.asarray(z_a, np.float64)
+    n, c = z_a.shape
+    ba = np.zeros((m, c)) if b_a is None else np.asarray(b_a, np.float64)
+    bb = np.zeros((m, c)) if b_b is None else np.asarray(b_b, np.float64)
+    out = []
+    for i in range(n // m):
+        lg = [z_a[m * i:m * i + m] + ba]
+        if overlap:
+            lg.append(np.full((m, c), -np.inf) if i == 0 else np.asarray(z_b, np.float64)[m * (i - 1):m * i] + bb)
+        lg = np.concatenate(lg, axis=0)
+        p = np.exp(lg - lg.max(axis=0))
+        out.append(p / p.sum(axis=0))
+    return np.stack(out) if out else np.zeros((0, 2 * m if overlap else m, c))
+
+
+def rms_norm(x, eps=1e-6):
+    """RMSNorm with unit gain over the last axis: x / sqrt(mean(x^2) + eps)
+    ([Evolution blog] §4.1 kv_norm; [DSA-to-CSA notes] §Shared-KV MQA, per-head norm)."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rope_angles(pos, r, theta=10000.0):
+    """Angles [..., r/2] = pos * theta^(-2u/r) for u = 0..r/2-1."""
+    u = np.arange(r // 2, dtype=np.float64)
+    freq = theta ** (-2.0 * u / r)
+    return np.asarray(pos, np.float64)[..., None] * freq
+
+
+def rope(x, pos, r, theta=10000.0, inverse=False):
+    """Rotate the last r channels of x ([..., c]) in adjacent pairs by angle pos*freq_u
+    (by -pos*freq_u if inverse).  `pos` broadcasts against x's leading axes.
+    [DSA-to-CSA notes] §Shared-KV MQA: RoPE only on the last 64 dims, and the
+    output's last dims are rotated back by the query position."""
+    x = np.array(x, np.float64, copy=True)
+    if r == 0:
+        return x
+    c = x.shape[-1]
+    ang = rope_angles(pos, r, theta)
+    if inverse:
+        ang = -ang
+    cos, sin = np.cos(ang), np.sin(ang)
+    x0 = x[..., c - r::2].copy()
+    x1 = x[..., c - r + 1::2].copy()
+    x[..., c - r::2] = x0 * cos - x1 * sin
+    x[..., c - r + 1::2] = x0 * sin + x1 * cos
+    return x
+
+
+def compress(c_a, z_a, m, *, b_a=None, c_b=None, z_b=None, b_b=None, overlap=False,
+             norm=True, eps=1e-6, rope_dims=0, theta=10000.0, pos0=0, w_ik=None):
+    """The compressor with its write-path epilogue ([Evolution blog] §4.1):
+    pool -> RMSNorm (kv_norm) -> optional indexer-K projection of the normalised,
+    not yet rotated entry -> RoPE of the main entry at position pos0 + m*i.
+    Returns (entries [n//m, c], k_index [n//m, d_I] or None)."""
+    y = gated_pool(c_a, z_a, m, b_a=b_a, c_b=c_b, z_b=z_b, b_b=b_b, overlap=overlap)
+    xh = rms_norm(y, eps) if norm else y
+    k_index = None if w_ik is None else xh @ np.asarray(w_ik, np.float64)
+    pos = pos0 + m * np.arange(xh.shape[0])
+    out = rope(xh, pos, rope_dims, theta) if rope_dims else xh
+    return out, k_index
+
+
+# ============================================================ causal rule
+def n_visible(t, n_entries, m):
+    """Compressed entry j (tokens [m*j, m*j+m)) is visible to query position t iff
+    t >= m*(j+1) ([DSA-to-CSA notes] §因果边界与短滑窗).  Returns min(N, floor(t/m))."""
+    return int(max(0, min(n_entries, t // m)))
+
+
+# ============================================================ lightning indexer
+def indexer_scores(q_idx, w, k_idx, n_vis=None):
+    """I[s] = sum_h w[h] * ReLU(q_I[h] . K_I[s]) ([DSA-to-CSA notes] eq. (16);
+    [Evolution blog] §2.2: ReLU and a signed head weight instead of a softmax).
+    q_idx [H_I, d_I], w [H_I], k_idx [N, d_I] -> scores [n_vis]."""
+    k = np.asarray(k_idx, np.float64)
+    if n_vis is not None:
+        k = k[:n_vis]
+    sim = np.asarray(q_idx, np.float64) @ k.T  # [H_I, n]
+    return (np.asarray(w, np.float64)[:, None] * np.maximum(sim, 0.0)).sum(axis=0)
+
+
+def topk_indices(scores, k):
+    """TopK of eq. (17), [DSA-to-CSA notes]: the min(k, n) largest scores, ties to the
+    lower index, returned as indices in ascending order and padded with -1 to k.
+    Done as a full stable sort by (-score, index)."""
+    s = np.asarray(scores, np.float64)
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))  # primary -s, secondary index
+    chosen = np.sort(order[:min(k, n)])
+    out = np.full(k, -1, dtype=np.int64)
+    out[:chosen.shape[0]] = chosen
+    return out
+
+
+def index_topk_full(q_idx, w, k_idx, q_pos, m, k):
+    """FULL mode for a batch: q_idx [B, T, H_I, d_I], w [B, T, H_I], k_idx [B, N, d_I],
+    q_pos [B, T] -> idx [B, T, k]."""
+    B, T = np.asarray(q_pos).shape
+    N = np.asarray(k_idx).shape[1]
+    out = np.full((B, T, k), -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(T):
+            nv = n_visible(int(q_pos[b, t]), N, m)
+            out[b, t] = topk_indices(indexer_scores(q_idx[b, t], w[b, t], k_idx[b], nv), k)
+    return out
+
+
+# ============================================================ hierarchical pool
+def block_max(scores, block=8):
+    """Block score = max over the visible positions [block*b, block*b+block)
+    ([CSA2 column] §解码器里的分层索引; [Evolution blog] §4.4)."""
+    s = np.asarray(scores, np.float64)
+    nb = -(-s.shape[0] // block)
+    return np.array([s[block * b:block * b + block].max() for b in range(nb)])
+
+
+def hier_candidates(block_scores, n_vis, n_keep=2048, block=8):
+    """Candidate pool: at most n_keep blocks, the latest visible block always kept
+    ([Evolution blog] §4.4), the others by (score desc, block asc); returns the
+    ascending visible positions of the chosen blocks."""
+    bs = np.asarray(block_scores, np.float64)
+    nb = bs.shape[0]
+    if nb == 0:
+        return np.zeros(0, dtype=np.int64)
+    last = nb - 1
+    others = np.arange(nb - 1)
+    order = others[np.lexsort((others, -bs[:nb - 1]))]
+    chosen = np.sort(np.concatenate([[last], order[:max(0, n_keep - 1)]]))
+    pos = (chosen[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return pos[pos < n_vis]
+
+
+def reindex_topk(q_idx, w, k_idx, cand, k):
+    """REINDEX ([CSA2 column] modes table; [Evolution blog] §4.4): score only the
+    candidate positions with this layer's indexer query, keep the top k by
+    (score desc, position asc); returns positions ascending, -1 padded."""
+    cand = np.asarray(cand, np.int64)
+    s = indexer_scores(q_idx, w, np.asarray(k_idx)[cand])
+    sel = topk_indices(s, k)
+    return np.where(sel >= 0, cand[np.maximum(sel, 0)], -1)
+
+
+def reindex_topk_masked(q_idx, w, k_idx, cand, n_vis, k):
+    """The same selection written as the pages describe the reference code: full
+    scores over all visible positions, non-candidates set to -inf, then top-k
+    ([Evolution blog] §4.4).  Only positions with a finite score may be returned."""
+    s = indexer_scores(q_idx, w, k_idx, n_vis)
+    masked = np.full_like(s, -np.inf)
+    cand = np.asarray(cand, np.int64)
+    masked[cand] = s[cand]
+    sel = topk_indices(masked, min(k, cand.shape[0]))
+    out = np.full(k, -1, dtype=np.int64)
+    out[:sel.shape[0]] = sel
+    return out
+
+
+def reuse(src_idx):
+    """REUSE: the indices of the upstream Full/Reindex layer, unchanged
+    ([CSA2 column] modes table)."""
+    return np.array(src_idx, copy=True)
+
+
+# ============================================================ sparse shared-KV MQA
+def window_rows(t, win_pos0, n_win_rows, window):
+    """Window buffer row numbers whose positions lie in [t-window+1, t]
+    ([CSA2 column] §保留了 CSA 的骨架: the latest 128 tokens of this layer)."""
+    lo = max(t - window + 1, win_pos0)
+    hi = min(t, win_pos0 + n_win_rows - 1)
+    return np.arange(lo - win_pos0, hi - win_pos0 + 1) if hi >= lo else np.zeros(0, np.int64)
+
+
+def attend_one(q, rows, sink, scale):
+    """Softmax over the rows plus a value-less sink logit ([DSA-to-CSA notes]
+    eq. (27)); rows are both keys and values (eq. (19)).  q [c], rows [R, c].
+    Returns (output [c], real mass)."""
+    rows = np.asarray(rows, np.float64)
+    if rows.shape[0] == 0:
+        return np.zeros(q.shape[-1]), 0.0
+    z = rows @ q * scale
+    mx = z.max() if sink is None or sink == -np.inf else max(z.max(), sink)
+    e = np.exp(z - mx)
+    den = e.sum() + (0.0 if sink is None or sink == -np.inf else math.exp(sink - mx))
+    p = e / den
+    return p @ rows, float(p.sum())
+
+
+def sparse_attn(q, q_pos, kv, idx, win=None, win_pos0=None, window=128, sink=None,
+                rope_dims=64, theta=10000.0, eps=1e-6, scale=None, q_norm=True):
+    """Shared-KV sparse MQA for a batch ([DSA-to-CSA notes] eq. (18)-(19), (27) and
+    §Shared-KV MQA).  For query t and head h:
+        q_hat = RoPE_t(RMSNorm(q_h))                      (norm optional)
+        rows  = kv[idx != -1]  ++  window rows at positions [t-W+1, t]
+        p_j   = exp(q_hat.row_j * scale) / (sum_j exp(...) + exp(sink_h))
+        o     = sum_j p_j row_j;  o's last r dims rotated by -t.
+    q [B, T, H, c]; kv [B, N, c]; idx [B, T, k]; win [B, Lw, c] or None;
+    win_pos0 [B]; sink [H] or None (no sink).  scale defaults to 1/sqrt(c).
+    Returns (out [B, T, H, c], mass [B, T, H])."""
+    q = np.asarray(q, np.float64)
+    kv = np.asarray(kv, np.float64)
+    B, T, H, c = q.shape
+    scale = 1.0 / math.sqrt(c) if not scale else scale
+    out = np.zeros((B, T, H, c))
+    mass = np.zeros((B, T, H))
+    for b in range(B):
+        for t in range(T):
+            pos = int(q_pos[b, t])
+            sel = [int(j) for j in idx[b, t] if j >= 0]
+            rows = [kv[b, sel]]
+            if win is not None and window > 0:
+                wr = window_rows(pos, int(win_pos0[b]), win.shape[1], window)
+                rows.append(np.asarray(win[b], np.float64)[wr])
+            rows = np.concatenate(rows, axis=0)
+            for h in range(H):
+                qh = rms_norm(q[b, t, h], eps) if q_norm else q[b, t, h]
+                qh = rope(qh, pos, rope_dims, theta) if rope_dims else qh
+                sk = None if sink is None else float(sink[h])
+                o, ms = attend_one(qh, rows, sk, scale)
+                out[b, t, h] = rope(o, pos, rope_dims, theta, inverse=True) if rope_dims else o
+                mass[b, t, h] = ms
+    return out, mass
+
+
+__all__ = [
+    "gated_pool", "gated_pool_weights", "rms_norm", "rope_angles", "rope", "compress",
+    "n_visible", "indexer_scores", "topk_indices", "index_topk_full", "block_max",
+    "hier_candidates", "reindex_topk", "reindex_topk_masked", "reuse", "window_rows",
+    "attend_one", "sparse_attn",
+]
