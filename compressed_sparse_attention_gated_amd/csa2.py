@@ -1,0 +1,267 @@
+"""Thin Python binding of libcsa2 (ctypes).
+
+Each function has the name of the C entry point it wraps, takes torch tensors that
+already live in device memory, fills the C descriptor with their pointers and sizes,
+allocates outputs and workspace with torch when the caller does not pass them, and
+calls the library on torch's current stream.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # loaded first: libcsa2 then binds to the HIP runtime torch already loaded
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+
+CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP, CSA2_ERR_WORKSPACE = 0, -1, -2, -3, -4
+CSA2_F32, CSA2_BF16, CSA2_FP4_E4M3, CSA2_MXFP4 = 0, 1, 2, 3
+CSA2_MODE_FULL, CSA2_MODE_REINDEX, CSA2_MODE_REUSE = 0, 1, 2
+
+_vp, _i, _f, _i64 = C.c_void_p, C.c_int, C.c_float, C.c_int64
+
+
+class CompressDesc(C.Structure):
+    _fields_ = [("B", _i), ("n", _i), ("c", _i), ("m", _i), ("overlap", _i), ("dtype", _i),
+                ("ca", _vp), ("za", _vp), ("cb", _vp), ("zb", _vp), ("ba", _vp), ("bb", _vp),
+                ("pos0", _vp), ("norm", _i), ("eps", _f), ("rope_dims", _i), ("rope_theta", _f),
+                ("out", _vp), ("out_batch_stride", _i64), ("w_ik", _vp), ("d_index", _i),
+                ("out_ik", _vp), ("out_ik_batch_stride", _i64)]
+
+
+class IndexDesc(C.Structure):
+    _fields_ = [("B", _i), ("T", _i), ("H_I", _i), ("d_I", _i), ("N", _i), ("m", _i), ("k", _i),
+                ("q_idx", _vp), ("w", _vp), ("q_pos", _vp), ("k_dtype", _i), ("k_idx", _vp),
+                ("k_codes", _vp), ("k_scales", _vp), ("cand", _vp), ("n_cand", _vp),
+                ("cand_stride", _i), ("src_idx", _vp), ("out_idx", _vp), ("out_block_max", _vp),
+                ("block", _i), ("out_scores", _vp)]
+
+
+class HierDesc(C.Structure):
+    _fields_ = [("B", _i), ("T", _i), ("N", _i), ("m", _i), ("block", _i), ("n_keep", _i),
+                ("q_pos", _vp), ("block_max", _vp), ("out_cand", _vp), ("out_count", _vp)]
+
+
+class AttnDesc(C.Structure):
+    _fields_ = [("B", _i), ("T", _i), ("H", _i), ("c", _i), ("k", _i), ("N", _i),
+                ("rope_dims", _i), ("rope_theta", _f), ("eps", _f), ("scale", _f), ("q_norm", _i),
+                ("q_dtype", _i), ("q", _vp), ("q_pos", _vp), ("kv_dtype", _i), ("kv", _vp),
+                ("kv_codes", _vp), ("kv_scales", _vp), ("idx", _vp), ("win", _vp), ("Lw", _i),
+                ("win_pos0", _vp), ("n_win", _i), ("sink", _vp), ("out", _vp), ("out_mass", _vp),
+                ("num_splits", _i)]
+
+
+class KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("ms", C.c_float)]
+
+
+EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk",
+           "csa2_hier_workspace_bytes", "csa2_hier_candidates", "csa2_attn_workspace_bytes",
+           "csa2_sparse_attn", "csa2_version", "csa2_last_error", "csa2_profile_enable",
+           "csa2_profile_collect"]
+
+_lib = None
+
+
+def lib():
+    """Load libcsa2.so (built in-tree).  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libcsa2.so not found at {LIB_PATH}; build it with "
+                           "`python -m compressed_sparse_attention_gated_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    L.csa2_compress.argtypes = [C.POINTER(CompressDesc), _vp]
+    L.csa2_index_workspace_bytes.argtypes = [C.POINTER(IndexDesc), _i]
+    L.csa2_index_workspace_bytes.restype = C.c_size_t
+    L.csa2_index_topk.argtypes = [C.POINTER(IndexDesc), _i, _vp, C.c_size_t, _vp]
+    L.csa2_hier_workspace_bytes.argtypes = [C.POINTER(HierDesc)]
+    L.csa2_hier_workspace_bytes.restype = C.c_size_t
+    L.csa2_hier_candidates.argtypes = [C.POINTER(HierDesc), _vp, C.c_size_t, _vp]
+    L.csa2_attn_workspace_bytes.argtypes = [C.POINTER(AttnDesc)]
+    L.csa2_attn_workspace_bytes.restype = C.c_size_t
+    L.csa2_sparse_attn.argtypes = [C.POINTER(AttnDesc), _vp, C.c_size_t, _vp]
+    L.csa2_last_error.restype = C.c_char_p
+    L.csa2_profile_enable.argtypes = [_i]
+    L.csa2_profile_collect.argtypes = [C.POINTER(KernelTime), _i]
+    _lib = L
+    return L
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libcsa2 error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc):
+    if rc != CSA2_OK:
+        raise Csa2Error(rc, lib().csa2_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+_DT = {torch.float32: CSA2_F32, torch.bfloat16: CSA2_BF16}
+
+
+def _ws(nbytes, device):
+    return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def last_error() -> str:
+    return lib().csa2_last_error().decode()
+
+
+def version() -> int:
+    return lib().csa2_version()
+
+
+# ---------------------------------------------------------------------------- compress
+def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, norm=True,
+                  eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None, w_ik=None, out_ik=None,
+                  stream=None):
+    """ca, za (cb, zb): [B, n, c] fp32/bf16 -> (out [B, n//m, c], out_ik [B, n//m, d_I] or None)."""
+    B, n, c = ca.shape
+    ne = n // m
+    if out is None:
+        out = torch.empty((B, ne, c), dtype=ca.dtype, device=ca.device)
+    d_index = 0
+    if w_ik is not None:
+        d_index = w_ik.shape[1]
+        if out_ik is None:
+            out_ik = torch.empty((B, ne, d_index), dtype=ca.dtype, device=ca.device)
+    d = CompressDesc(B=B, n=n, c=c, m=m, overlap=int(cb is not None), dtype=_DT[ca.dtype],
+                     ca=_p(ca), za=_p(za), cb=_p(cb), zb=_p(zb), ba=_p(ba), bb=_p(bb), pos0=_p(pos0),
+                     norm=int(norm), eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, out=_p(out),
+                     out_batch_stride=out.stride(0) if out.dim() == 3 else 0, w_ik=_p(w_ik),
+                     d_index=d_index, out_ik=_p(out_ik),
+                     out_ik_batch_stride=out_ik.stride(0) if out_ik is not None else 0)
+    _check(lib().csa2_compress(C.byref(d), _stream(stream)))
+    return out, out_ik
+
+
+# ---------------------------------------------------------------------------- index + top-k
+def _index_desc(q_idx, w, q_pos, k, m, *, k_idx=None, k_codes=None, k_scales=None, N=None,
+                cand=None, n_cand=None, src_idx=None, out_idx=None, out_block_max=None, block=8,
+                out_scores=None):
+    B, T = q_pos.shape
+    H_I, d_I = (q_idx.shape[2], q_idx.shape[3]) if q_idx is not None else (1, 32)
+    if N is None:
+        N = (k_idx.shape[1] if k_idx is not None else (k_codes.shape[1] if k_codes is not None else 0))
+    return IndexDesc(B=B, T=T, H_I=H_I, d_I=d_I, N=N, m=m, k=k, q_idx=_p(q_idx), w=_p(w),
+                     q_pos=_p(q_pos), k_dtype=CSA2_MXFP4 if k_codes is not None else CSA2_BF16,
+                     k_idx=_p(k_idx), k_codes=_p(k_codes), k_scales=_p(k_scales), cand=_p(cand),
+                     n_cand=_p(n_cand), cand_stride=cand.shape[-1] if cand is not None else 0,
+                     src_idx=_p(src_idx), out_idx=_p(out_idx), out_block_max=_p(out_block_max),
+                     block=block, out_scores=_p(out_scores))
+
+
+def csa2_index_topk(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_codes=None,
+                    k_scales=None, N=None, cand=None, n_cand=None, src_idx=None, out_idx=None,
+                    out_block_max=None, block=8, out_scores=None, workspace=None, stream=None):
+    """FULL / REINDEX / REUSE.  Returns out_idx [B, T, k] int32."""
+    B, T = q_pos.shape
+    dev = q_pos.device
+    if out_idx is None:
+        out_idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    d = _index_desc(q_idx, w, q_pos, k, m, k_idx=k_idx, k_codes=k_codes, k_scales=k_scales, N=N,
+                    cand=cand, n_cand=n_cand, src_idx=src_idx, out_idx=out_idx,
+                    out_block_max=out_block_max, block=block, out_scores=out_scores)
+    nbytes = lib().csa2_index_workspace_bytes(C.byref(d), mode)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _ws(nbytes, dev)
+    _check(lib().csa2_index_topk(C.byref(d), mode, _p(workspace), nbytes, _stream(stream)))
+    return out_idx
+
+
+def csa2_index_workspace_bytes(mode, q_pos, k, **kw):
+    d = _index_desc(kw.get("q_idx"), kw.get("w"), q_pos, k, kw.get("m", 1), k_idx=kw.get("k_idx"),
+                    k_codes=kw.get("k_codes"), k_scales=kw.get("k_scales"), N=kw.get("N"),
+                    cand=kw.get("cand"), n_cand=kw.get("n_cand"), src_idx=kw.get("src_idx"),
+                    out_idx=kw.get("out_idx"), out_block_max=kw.get("out_block_max"),
+                    block=kw.get("block", 8), out_scores=kw.get("out_scores"))
+    return lib().csa2_index_workspace_bytes(C.byref(d), mode)
+
+
+# ---------------------------------------------------------------------------- hierarchical pool
+def csa2_hier_candidates(block_max, q_pos, N, *, m=1, block=8, n_keep=2048, out_cand=None,
+                         out_count=None, workspace=None, stream=None):
+    """block_max [B, T, ceil(N/block)] -> (cand [B, T, n_keep*block], count [B, T])."""
+    B, T = q_pos.shape
+    dev = q_pos.device
+    if out_cand is None:
+        out_cand = torch.empty((B, T, n_keep * block), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty((B, T), dtype=torch.int32, device=dev)
+    d = HierDesc(B=B, T=T, N=N, m=m, block=block, n_keep=n_keep, q_pos=_p(q_pos),
+                 block_max=_p(block_max), out_cand=_p(out_cand), out_count=_p(out_count))
+    nbytes = lib().csa2_hier_workspace_bytes(C.byref(d))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _ws(nbytes, dev)
+    _check(lib().csa2_hier_candidates(C.byref(d), _p(workspace), nbytes, _stream(stream)))
+    return out_cand, out_count
+
+
+# ---------------------------------------------------------------------------- attention
+def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
+               win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0, eps=1e-6,
+               scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0):
+    B, T, H, c = q.shape
+    if N is None:
+        N = kv.shape[1] if kv is not None else (kv_codes.shape[1] if kv_codes is not None else 0)
+    kvdt = CSA2_FP4_E4M3 if kv_codes is not None else _DT[q.dtype]
+    return AttnDesc(B=B, T=T, H=H, c=c, k=idx.shape[-1] if idx is not None else 0, N=N,
+                    rope_dims=rope_dims, rope_theta=rope_theta, eps=eps, scale=scale,
+                    q_norm=int(q_norm), q_dtype=_DT[q.dtype], q=_p(q), q_pos=_p(q_pos),
+                    kv_dtype=kvdt, kv=_p(kv), kv_codes=_p(kv_codes), kv_scales=_p(kv_scales),
+                    idx=_p(idx), win=_p(win), Lw=win.shape[1] if win is not None else 0,
+                    win_pos0=_p(win_pos0), n_win=n_win if win is not None else 0, sink=_p(sink),
+                    out=_p(out), out_mass=_p(out_mass), num_splits=num_splits)
+
+
+def csa2_sparse_attn(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
+                     win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0,
+                     eps=1e-6, scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0,
+                     workspace=None, stream=None):
+    """q [B, T, H, c] -> out [B, T, H, c] (dtype of q)."""
+    if out is None:
+        out = torch.empty_like(q)
+    d = _attn_desc(q, q_pos, idx, kv=kv, kv_codes=kv_codes, kv_scales=kv_scales, N=N, win=win,
+                   win_pos0=win_pos0, n_win=n_win, sink=sink, rope_dims=rope_dims,
+                   rope_theta=rope_theta, eps=eps, scale=scale, q_norm=q_norm, out=out,
+                   out_mass=out_mass, num_splits=num_splits)
+    nbytes = lib().csa2_attn_workspace_bytes(C.byref(d))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _ws(nbytes, q.device)
+    _check(lib().csa2_sparse_attn(C.byref(d), _p(workspace), nbytes, _stream(stream)))
+    return out
+
+
+def csa2_attn_workspace_bytes(q, q_pos, idx, **kw):
+    d = _attn_desc(q, q_pos, idx, **kw)
+    return lib().csa2_attn_workspace_bytes(C.byref(d))
+
+
+# ---------------------------------------------------------------------------- kernel timing
+def csa2_profile_enable(on: bool = True):
+    _check(lib().csa2_profile_enable(int(on)))
+
+
+def csa2_profile_collect(max_records: int = 4096):
+    """Wait for the recorded events; return [(kernel name, ms)] in launch order."""
+    buf = (KernelTime * max_records)()
+    n = lib().csa2_profile_collect(buf, max_records)
+    if n < 0:
+        _check(n)
+    return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]

@@ -1,0 +1,343 @@
+// Host side of the libcsa2 C ABI: argument validation (all of it before any launch),
+// workspace sizing, mode dispatch, the thread-local last-error string and the optional
+// per-kernel event timing.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/csa2.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int ok() {
+  g_err.clear();
+  return CSA2_OK;
+}
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSA2_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool pow2_upto(int v, int hi) { return v >= 1 && v <= hi && (v & (v - 1)) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// --------------------------------------------------------------- kernel timing
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+  hipStream_t s;
+};
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfRec> g_prof;
+thread_local std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace csa2 {
+void prof_begin(hipStream_t s, const char* name) {
+  if (!g_prof_on) return;
+  ProfRec r{name, take_event(), take_event(), s};
+  if (r.a) hipEventRecord(r.a, s);
+  g_prof.push_back(r);
+}
+void prof_end(hipStream_t s) {
+  if (!g_prof_on || g_prof.empty()) return;
+  ProfRec& r = g_prof.back();
+  if (r.b) hipEventRecord(r.b, s);
+}
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" {
+
+int csa2_version(void) { return CSA2_VERSION; }
+const char* csa2_last_error(void) { return g_err.c_str(); }
+
+int csa2_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return CSA2_OK;
+}
+
+int csa2_profile_collect(csa2_kernel_time* out, int max) {
+  int n = 0;
+  int rc = CSA2_OK;
+  for (ProfRec& r : g_prof) {
+    float ms = -1.f;
+    if (r.a && r.b && hipEventSynchronize(r.b) == hipSuccess) {
+      if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) ms = -1.f;
+    } else {
+      rc = CSA2_ERR_HIP;
+    }
+    if (out && n < max) {
+      std::memset(out[n].name, 0, sizeof out[n].name);
+      std::strncpy(out[n].name, r.name.c_str(), sizeof out[n].name - 1);
+      out[n].ms = ms;
+      ++n;
+    }
+    if (r.a) g_event_pool.push_back(r.a);
+    if (r.b) g_event_pool.push_back(r.b);
+  }
+  g_prof.clear();
+  if (rc != CSA2_OK) return fail(rc, "profile: an event could not be synchronised");
+  ok();
+  return n;
+}
+
+// --------------------------------------------------------------- compress
+static int check_compress(const csa2_compress_desc* d) {
+  if (!d) return fail(CSA2_ERR_INVALID, "compress: null descriptor");
+  if (d->B < 0 || d->n < 0 || d->m < 1) return fail(CSA2_ERR_INVALID, "compress: need B >= 0, n >= 0, m >= 1");
+  if (d->c < 8 || d->c > 512 || d->c % 8 != 0 || !pow2_upto(d->c / 8, 64))
+    return fail(CSA2_ERR_UNSUPPORTED, "compress: c=%d unsupported (c/8 must be a power of two, 8 <= c <= 512)", d->c);
+  if (d->dtype != CSA2_F32 && d->dtype != CSA2_BF16)
+    return fail(CSA2_ERR_UNSUPPORTED, "compress: dtype must be F32 or BF16");
+  if (d->overlap != 0 && d->overlap != 1) return fail(CSA2_ERR_INVALID, "compress: overlap must be 0 or 1");
+  if (d->rope_dims < 0 || d->rope_dims > d->c || d->rope_dims % 2)
+    return fail(CSA2_ERR_INVALID, "compress: rope_dims must be even and in [0, c]");
+  if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return fail(CSA2_ERR_INVALID, "compress: rope_theta must be > 0");
+  if (d->norm && !(d->eps >= 0.f)) return fail(CSA2_ERR_INVALID, "compress: eps must be >= 0");
+  const long long n_ent = (long long)d->B * (d->n / d->m);
+  if (n_ent == 0) return CSA2_OK;
+  if (!d->ca || !d->za || !d->out) return fail(CSA2_ERR_INVALID, "compress: ca, za and out are required");
+  if (d->overlap && (!d->cb || !d->zb)) return fail(CSA2_ERR_INVALID, "compress: overlap needs cb and zb");
+  if (d->w_ik) {
+    if (!d->out_ik) return fail(CSA2_ERR_INVALID, "compress: w_ik needs out_ik");
+    if (d->d_index != 32 && d->d_index != 64 && d->d_index != 128)
+      return fail(CSA2_ERR_UNSUPPORTED, "compress: d_index must be 32, 64 or 128");
+  }
+  const int64_t n_per = d->n / d->m;
+  if (d->out_batch_stride != 0 && d->out_batch_stride < n_per * d->c)
+    return fail(CSA2_ERR_INVALID, "compress: out_batch_stride smaller than (n/m)*c");
+  if (d->w_ik && d->out_ik_batch_stride != 0 && d->out_ik_batch_stride < n_per * d->d_index)
+    return fail(CSA2_ERR_INVALID, "compress: out_ik_batch_stride smaller than (n/m)*d_index");
+  return CSA2_OK;
+}
+
+int csa2_compress(const csa2_compress_desc* d, void* stream) {
+  int rc = check_compress(d);
+  if (rc != CSA2_OK) return rc;
+  if ((long long)d->B * (d->n / d->m) == 0) return ok();
+  return hip_status(launch_compress(*d, (hipStream_t)stream), "compress");
+}
+
+// --------------------------------------------------------------- index + top-k
+static int check_index(const csa2_index_desc* d, csa2_mode mode) {
+  if (!d) return fail(CSA2_ERR_INVALID, "index: null descriptor");
+  if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
+    return fail(CSA2_ERR_INVALID, "index: unknown mode %d", (int)mode);
+  if (d->B < 0 || d->T < 0) return fail(CSA2_ERR_INVALID, "index: need B, T >= 0");
+  if (d->k < 1) return fail(CSA2_ERR_INVALID, "index: k must be >= 1");
+  if (d->k > 4096) return fail(CSA2_ERR_UNSUPPORTED, "index: k > 4096");
+  const long long rows = (long long)d->B * d->T;
+  if (mode == CSA2_MODE_REUSE) {
+    if (rows && (!d->src_idx || !d->out_idx)) return fail(CSA2_ERR_INVALID, "index: REUSE needs src_idx and out_idx");
+    return CSA2_OK;
+  }
+  if (d->H_I < 1 || d->H_I > 64) return fail(CSA2_ERR_UNSUPPORTED, "index: H_I must be in [1, 64]");
+  if (d->d_I != 32 && d->d_I != 64 && d->d_I != 128) return fail(CSA2_ERR_UNSUPPORTED, "index: d_I must be 32, 64 or 128");
+  if (d->N < 0 || d->m < 1) return fail(CSA2_ERR_INVALID, "index: need N >= 0, m >= 1");
+  if (d->k_dtype != CSA2_BF16 && d->k_dtype != CSA2_MXFP4)
+    return fail(CSA2_ERR_UNSUPPORTED, "index: K_I dtype must be BF16 or MXFP4");
+  if (rows == 0) return CSA2_OK;
+  if (!d->q_idx || !d->w || !d->q_pos || !d->out_idx) return fail(CSA2_ERR_INVALID, "index: q_idx, w, q_pos, out_idx are required");
+  if (d->N > 0) {
+    if (d->k_dtype == CSA2_BF16 && !d->k_idx) return fail(CSA2_ERR_INVALID, "index: k_idx required for BF16 K_I");
+    if (d->k_dtype == CSA2_MXFP4 && (!d->k_codes || !d->k_scales))
+      return fail(CSA2_ERR_INVALID, "index: k_codes and k_scales required for MXFP4 K_I");
+  }
+  if (mode == CSA2_MODE_FULL && d->out_block_max && !pow2_upto(d->block, 32))
+    return fail(CSA2_ERR_UNSUPPORTED, "index: block must be a power of two <= 32");
+  if (mode == CSA2_MODE_REINDEX) {
+    if (!d->cand || !d->n_cand || d->cand_stride < 1) return fail(CSA2_ERR_INVALID, "index: REINDEX needs cand, n_cand, cand_stride >= 1");
+    if (d->N == 0) return fail(CSA2_ERR_INVALID, "index: REINDEX with N == 0");
+  }
+  if ((long long)d->N * 1 > (1LL << 30)) return fail(CSA2_ERR_UNSUPPORTED, "index: N too large");
+  return CSA2_OK;
+}
+
+static size_t index_ws(const csa2_index_desc* d, csa2_mode mode) {
+  const size_t rows = (size_t)d->B * d->T;
+  if (mode == CSA2_MODE_REUSE || rows == 0) return 0;
+  const int len = mode == CSA2_MODE_FULL ? d->N : d->cand_stride;
+  size_t bytes = 0;
+  if (!d->out_scores) bytes += align256(rows * (size_t)len * sizeof(float));
+  bytes += align256(topk_workspace_bytes((int)rows, d->k, len));
+  return bytes;
+}
+
+size_t csa2_index_workspace_bytes(const csa2_index_desc* d, csa2_mode mode) {
+  if (check_index(d, mode) != CSA2_OK) return 0;
+  return index_ws(d, mode);
+}
+
+int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_index(d, mode);
+  if (rc != CSA2_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const long long rows = (long long)d->B * d->T;
+  if (rows == 0) return ok();
+  if (mode == CSA2_MODE_REUSE) {
+    if (d->src_idx == d->out_idx) return ok();
+    return hip_status(launch_copy_idx(d->src_idx, d->out_idx, (size_t)rows * d->k, s), "index/reuse");
+  }
+  const size_t need = index_ws(d, mode);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSA2_ERR_WORKSPACE, "index: workspace of %zu bytes required, %zu given", need, ws_bytes);
+  const int len = mode == CSA2_MODE_FULL ? d->N : d->cand_stride;
+  char* wp = (char*)ws;
+  float* scores = d->out_scores;
+  if (!scores) {
+    scores = (float*)wp;
+    wp += align256((size_t)rows * len * sizeof(float));
+  }
+  void* tk_ws = wp;
+  const size_t tk_bytes = topk_workspace_bytes((int)rows, d->k, len);
+
+  if (len > 0) {
+    ScanArgs a{};
+    a.B = d->B; a.T = d->T; a.H_I = d->H_I; a.d_I = d->d_I; a.N = d->N; a.m = d->m;
+    a.block = d->block > 0 ? d->block : 1;
+    a.q_idx = d->q_idx; a.w = d->w; a.q_pos = d->q_pos; a.k_dtype = d->k_dtype; a.k_idx = d->k_idx;
+    a.k_codes = d->k_codes; a.k_scales = d->k_scales;
+    a.cand = mode == CSA2_MODE_REINDEX ? d->cand : nullptr;
+    a.n_cand = mode == CSA2_MODE_REINDEX ? d->n_cand : nullptr;
+    a.cand_stride = d->cand_stride;
+    a.scores = scores; a.row_stride = len;
+    a.block_max = mode == CSA2_MODE_FULL ? d->out_block_max : nullptr;
+    a.nblk = (d->N + a.block - 1) / a.block;
+    hipError_t e = launch_index_scan(a, s);
+    if (e != hipSuccess) return hip_status(e, "index/scan");
+  }
+  TopkArgs t{};
+  t.rows = (int)rows; t.k = d->k; t.scores = scores; t.row_stride = len;
+  t.out_idx = d->out_idx;
+  if (mode == CSA2_MODE_FULL) {
+    t.q_pos = d->q_pos; t.N = d->N; t.m = d->m;
+  } else {
+    t.counts = d->n_cand; t.idx_map = d->cand; t.idx_map_stride = d->cand_stride;
+  }
+  t.len_div = 1;
+  t.max_len = len;
+  t.ws = tk_ws; t.ws_bytes = tk_bytes;
+  return hip_status(launch_topk(t, s), "index/topk");
+}
+
+// --------------------------------------------------------------- hierarchical pool
+static int check_hier(const csa2_hier_desc* d) {
+  if (!d) return fail(CSA2_ERR_INVALID, "hier: null descriptor");
+  if (d->B < 0 || d->T < 0 || d->N < 0 || d->m < 1) return fail(CSA2_ERR_INVALID, "hier: need B, T, N >= 0, m >= 1");
+  if (!pow2_upto(d->block, 32)) return fail(CSA2_ERR_UNSUPPORTED, "hier: block must be a power of two <= 32");
+  if (d->n_keep < 1 || d->n_keep > 4096) return fail(CSA2_ERR_UNSUPPORTED, "hier: n_keep must be in [1, 4096]");
+  if ((long long)d->B * d->T == 0) return CSA2_OK;
+  if (!d->q_pos || !d->block_max || !d->out_cand || !d->out_count)
+    return fail(CSA2_ERR_INVALID, "hier: q_pos, block_max, out_cand, out_count are required");
+  return CSA2_OK;
+}
+
+static size_t hier_ws(const csa2_hier_desc* d) {
+  const size_t rows = (size_t)d->B * d->T;
+  if (rows == 0) return 0;
+  const int nblk = (d->N + d->block - 1) / d->block;
+  return align256(rows * d->n_keep * sizeof(int32_t)) + align256(topk_workspace_bytes((int)rows, d->n_keep, nblk));
+}
+
+size_t csa2_hier_workspace_bytes(const csa2_hier_desc* d) {
+  if (check_hier(d) != CSA2_OK) return 0;
+  return hier_ws(d);
+}
+
+int csa2_hier_candidates(const csa2_hier_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_hier(d);
+  if (rc != CSA2_OK) return rc;
+  const long long rows = (long long)d->B * d->T;
+  if (rows == 0) return ok();
+  const size_t need = hier_ws(d);
+  if (!ws || ws_bytes < need) return fail(CSA2_ERR_WORKSPACE, "hier: workspace of %zu bytes required, %zu given", need, ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const int nblk = (d->N + d->block - 1) / d->block;
+  int32_t* sel = (int32_t*)ws;
+  char* tk_ws = (char*)ws + align256((size_t)rows * d->n_keep * sizeof(int32_t));
+  TopkArgs t{};
+  t.rows = (int)rows; t.k = d->n_keep; t.scores = d->block_max; t.row_stride = nblk;
+  t.q_pos = d->q_pos; t.N = d->N; t.m = d->m; t.len_div = d->block; t.force_last = 1;
+  t.out_idx = sel; t.max_len = nblk; t.ws = tk_ws;
+  t.ws_bytes = topk_workspace_bytes((int)rows, d->n_keep, nblk);
+  hipError_t e = launch_topk(t, s);
+  if (e != hipSuccess) return hip_status(e, "hier/topk");
+  return hip_status(launch_hier_expand((int)rows, d->n_keep, d->block, sel, d->q_pos, d->N, d->m, d->out_cand,
+                                       d->out_count, s),
+                    "hier/expand");
+}
+
+// --------------------------------------------------------------- attention
+static int check_attn(const csa2_attn_desc* d) {
+  if (!d) return fail(CSA2_ERR_INVALID, "attn: null descriptor");
+  if (d->B < 0 || d->T < 0 || d->H < 0 || d->k < 0 || d->N < 0) return fail(CSA2_ERR_INVALID, "attn: negative size");
+  if (d->c < 16 || d->c % 16 != 0) return fail(CSA2_ERR_INVALID, "attn: c must be a positive multiple of 16");
+  if (d->c > 512) return fail(CSA2_ERR_UNSUPPORTED, "attn: c > 512");
+  if (d->rope_dims < 0 || d->rope_dims > d->c || d->rope_dims % 2) return fail(CSA2_ERR_INVALID, "attn: rope_dims must be even and in [0, c]");
+  if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return fail(CSA2_ERR_INVALID, "attn: rope_theta must be > 0");
+  if (d->q_norm && !(d->eps >= 0.f)) return fail(CSA2_ERR_INVALID, "attn: eps must be >= 0");
+  if (d->q_dtype != CSA2_F32 && d->q_dtype != CSA2_BF16) return fail(CSA2_ERR_UNSUPPORTED, "attn: q dtype must be F32 or BF16");
+  if (d->kv_dtype != d->q_dtype && !(d->kv_dtype == CSA2_FP4_E4M3 && d->q_dtype == CSA2_BF16))
+    return fail(CSA2_ERR_UNSUPPORTED, "attn: kv dtype must equal q dtype, or be FP4 with bf16 q");
+  if (d->num_splits < 0) return fail(CSA2_ERR_INVALID, "attn: num_splits must be >= 0");
+  if ((long long)d->B * d->T * d->H == 0) return CSA2_OK;
+  if (!d->q || !d->q_pos || !d->out) return fail(CSA2_ERR_INVALID, "attn: q, q_pos and out are required");
+  if (d->k > 0 && !d->idx) return fail(CSA2_ERR_INVALID, "attn: idx required when k > 0");
+  if (d->k > 0 && d->N > 0) {
+    if (d->kv_dtype == CSA2_FP4_E4M3 && (!d->kv_codes || !d->kv_scales))
+      return fail(CSA2_ERR_INVALID, "attn: FP4 kv needs kv_codes and kv_scales");
+    if (d->kv_dtype != CSA2_FP4_E4M3 && !d->kv) return fail(CSA2_ERR_INVALID, "attn: kv required");
+  }
+  if (d->win) {
+    if (!d->win_pos0 || d->Lw < 0 || d->n_win < 0) return fail(CSA2_ERR_INVALID, "attn: window needs win_pos0, Lw >= 0, n_win >= 0");
+  }
+  return CSA2_OK;
+}
+
+size_t csa2_attn_workspace_bytes(const csa2_attn_desc* d) {
+  if (check_attn(d) != CSA2_OK) return 0;
+  return attn_workspace_bytes(*d);
+}
+
+int csa2_sparse_attn(const csa2_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_attn(d);
+  if (rc != CSA2_OK) return rc;
+  if ((long long)d->B * d->T * d->H == 0) return ok();
+  const size_t need = attn_workspace_bytes(*d);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSA2_ERR_WORKSPACE, "attn: workspace of %zu bytes required, %zu given", need, ws_bytes);
+  return hip_status(launch_attn(*d, ws, ws_bytes, (hipStream_t)stream), "attn");
+}
+
+}  // extern "C"

@@ -1,0 +1,365 @@
+// Lightning-indexer scan: I[t,s] = sum_h w[t,h] * ReLU(q_I[t,h] . K_I[s])
+// ([DSA-to-CSA notes] eq. (16); [Evolution blog] §2.2), over the visible entries
+// s < n_vis(t) = min(N, floor(t/m)) ([DSA-to-CSA notes] "因果边界与短滑窗"), or over a
+// candidate list (Reindex, [Evolution blog] §4.4).  Optional block maxima over `block`
+// consecutive entries ([CSA2 column] "解码器里的分层索引").
+//
+// The head contraction is a dense GEMM q_I[H_I x d_I] x K_I^T[d_I x 32 entries] on the
+// bf16 MFMA v_mfma_f32_32x32x16_bf16: A = 32 heads x 16 dims (held in registers for the
+// whole scan), B = 16 dims x 32 entries loaded straight from HBM into registers (lane l
+// reads 16 bytes of entry l%32), C = 32x32 fp32.  In C each lane holds 16 head-rows of one
+// entry column, so the ReLU, the signed head weight and the head sum are an in-lane
+// epilogue plus one swap between the two half-waves.  No LDS: every K_I byte is read
+// exactly once per query.  MXFP4 rows (E2M1 codes + E8M0 scale per 32) are dequantised
+// into the B registers (exact in bf16).
+//
+// Two variants:
+//  * scan_private: one query per workgroup slice; the 4 waves split the entry range.
+//    Used for decode (one query per sequence) and Reindex.
+//  * scan_shared: prefill - a workgroup takes 8 consecutive queries of one sequence (one
+//    per wave) and streams the K_I tiles they share through LDS, so each tile is read from
+//    L2 once per 8 queries; the causal limit is per query.
+
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kPrivThreads = 64 * kWaves;
+
+struct Dev {
+  int T, H_I, N, m, block, cand_stride, nblk;
+  const uint16_t* q_idx;
+  const float* w;
+  const int32_t* q_pos;
+  const uint16_t* k_idx;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const int32_t* cand;
+  const int32_t* n_cand;
+  float* scores;
+  int64_t row_stride;
+  float* block_max;
+};
+
+// Dimension order inside one 16-wide k-step.  For bf16 rows, lane half h holds dims
+// 16*ks + 8h .. +7.  For MXFP4 rows lane half h holds dims (DI/2)*h + 8*ks .. +7, so a
+// lane's codes are one contiguous run of DI/4 bytes.  A and B use the same order, so the
+// dot product is unchanged.
+template <int DI, int KF>
+__device__ __forceinline__ int dim_of(int ks, int h) {
+  return KF == 0 ? 16 * ks + 8 * h : (DI / 2) * h + 8 * ks;
+}
+
+// B operand of one 32-entry tile: KS = DI/16 registers of 8 bf16
+template <int DI, int KF>
+__device__ __forceinline__ void load_b(const Dev& a, int b, int ent, int h, bf16x8* breg) {
+  constexpr int KS = DI / 16;
+  if constexpr (KF == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(a.k_idx + ((size_t)b * a.N + ent) * DI + 8 * h);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) breg[ks] = as_bf16x8(p[2 * ks]);
+  } else {
+    // codes: DI/4 bytes at (DI/4)*h; scales: groups of 32 dims
+    const uint8_t* cp = a.k_codes + ((size_t)b * a.N + ent) * (DI / 2) + (DI / 4) * h;
+    const uint8_t* sp = a.k_scales + ((size_t)b * a.N + ent) * (DI / 32);
+    uint32_t codes[DI / 16];
+    if constexpr (DI / 4 >= 16) {
+#pragma unroll
+      for (int q = 0; q < DI / 64; ++q) {
+        uint4 v = reinterpret_cast<const uint4*>(cp)[q];
+        codes[4 * q] = v.x; codes[4 * q + 1] = v.y; codes[4 * q + 2] = v.z; codes[4 * q + 3] = v.w;
+      }
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(cp);
+      codes[0] = v.x; codes[1] = v.y;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = dim_of<DI, KF>(ks, h);
+      const float sc = e8m0_to_f32(sp[d0 / 32]);
+      const uint32_t cw = codes[ks];
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((cw >> (4 * e)) & 15u) * sc;
+      breg[ks] = as_bf16x8(pack8(f));  // exact: E2M1 x 2^k is a bf16 number
+    }
+  }
+}
+
+// A operand (q_I of one query) and the head weights in the C layout
+template <int DI, int KF, int MT>
+__device__ __forceinline__ void load_query(const Dev& a, int row, int lane, bf16x8 (*areg)[DI / 16],
+                                           float (*wreg)[16]) {
+  const int h = lane / 32;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int head = 32 * mt + lane % 32;
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (head < a.H_I)
+        v = *reinterpret_cast<const uint4*>(a.q_idx + ((size_t)row * a.H_I + head) * DI + dim_of<DI, KF>(ks, h));
+      areg[mt][ks] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = 32 * mt + 8 * (r / 4) + 4 * h + (r % 4);  // C-layout row of register r
+      wreg[mt][r] = hr < a.H_I ? a.w[(size_t)row * a.H_I + hr] : 0.f;
+    }
+  }
+}
+
+template <int DI, int MT>
+__device__ __forceinline__ float tile_score(const bf16x8 (*areg)[DI / 16], const bf16x8* breg,
+                                            const float (*wreg)[16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(areg[mt][ks], breg[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wreg[mt][r] * fmaxf(acc[r], 0.f);
+  }
+  // lanes l and l^32 hold the two halves of the head rows of the same entry
+  s += __shfl_xor(s, 32, 64);
+  return s;
+}
+
+__device__ __forceinline__ int n_visible(const Dev& a, int row) {
+  const int t = a.q_pos[row];
+  const int nv = t >= 0 ? t / a.m : 0;
+  return nv < a.N ? nv : a.N;
+}
+
+// write scores (lanes 0..31) and, optionally, block maxima of one 32-slot tile
+template <bool kBlockMax>
+__device__ __forceinline__ void emit(const Dev& a, int row, int lane, int slot, int limit, float s) {
+  const bool ok = slot < limit;
+  if (lane < 32 && ok) a.scores[(size_t)row * a.row_stride + slot] = s;
+  if constexpr (kBlockMax) {
+    float v = ok ? s : -INFINITY;
+    for (int o = 1; o < a.block; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if (lane < 32 && ok && (slot % a.block) == 0) a.block_max[(size_t)row * a.nblk + slot / a.block] = v;
+  }
+}
+
+// ---------------------------------------------------------------- private-B scan
+template <int DI, int KF, int MT, bool kCand, bool kBlockMax>
+__global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
+  const int row = blockIdx.x;
+  const int b = row / a.T;
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int limit = kCand ? min(a.n_cand[row], a.cand_stride) : n_visible(a, row);
+  const int c0 = blockIdx.y * chunk;
+  const int c1 = min(c0 + chunk, limit);
+  if (c0 >= c1) return;
+
+  bf16x8 areg[MT][DI / 16];
+  float wreg[MT][16];
+  load_query<DI, KF, MT>(a, row, lane, areg, wreg);
+
+  const int h = lane / 32;
+  auto entry_of = [&](int slot) -> int {
+    int s = min(slot, c1 - 1);
+    if constexpr (kCand) {
+      int e = a.cand[(size_t)row * a.cand_stride + s];
+      return min(max(e, 0), a.N - 1);
+    }
+    return s;
+  };
+
+  int tb = c0 + 32 * wave;
+  if (tb >= c1) return;
+  bf16x8 bcur[DI / 16], bnext[DI / 16];
+  load_b<DI, KF>(a, b, entry_of(tb + lane % 32), h, bcur);
+  for (; tb < c1; tb += 32 * kWaves) {
+    const int tn = tb + 32 * kWaves;
+    if (tn < c1) load_b<DI, KF>(a, b, entry_of(tn + lane % 32), h, bnext);
+    float s = tile_score<DI, MT>(areg, bcur, wreg);
+    if constexpr (kCand) {
+      const int slot = tb + lane % 32;
+      if (slot < c1) {
+        const int e = a.cand[(size_t)row * a.cand_stride + slot];
+        if (e < 0 || e >= a.N) s = -INFINITY;
+      }
+    }
+    emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks) bcur[ks] = bnext[ks];
+  }
+}
+
+// ---------------------------------------------------------------- shared-B scan (prefill)
+constexpr int kShWaves = 8;
+constexpr int kShThreads = 64 * kShWaves;
+constexpr int kShTile = 64;  // entries per LDS stage
+
+template <int DI, int KF, int MT, bool kBlockMax>
+__global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total) {
+  // workgroup -> 8 consecutive query rows of one sequence; heavy (late) groups first
+  const int groups_per_seq = (a.T + kShWaves - 1) / kShWaves;
+  const int gid = blockIdx.x;
+  const int b = gid / groups_per_seq;
+  const int g = groups_per_seq - 1 - (gid % groups_per_seq);
+  const int lane = threadIdx.x % 64;
+  const int wave = threadIdx.x / 64;
+  const int t = g * kShWaves + wave;
+  const bool active = t < a.T;
+  const int row = b * a.T + (active ? t : 0);
+  const int limit = active ? n_visible(a, row) : 0;
+  // the group's scan length: the largest limit of its queries
+  __shared__ int s_lim[kShWaves];
+  if (lane == 0) s_lim[wave] = limit;
+  __syncthreads();
+  int glim = 0;
+#pragma unroll
+  for (int i = 0; i < kShWaves; ++i) glim = max(glim, s_lim[i]);
+  if (glim == 0) return;
+
+  // LDS: two stages of kShTile entries x DI bf16, [entry][16-byte chunk], the chunk index
+  // XOR-swizzled with the entry so the 32 lanes of an MFMA B read hit distinct banks
+  constexpr int kCPR = DI / 8;  // chunks per entry row
+  __shared__ uint4 tile[2][kShTile * kCPR];
+  bf16x8 areg[MT][DI / 16];
+  float wreg[MT][16];
+  load_query<DI, KF, MT>(a, row, lane, areg, wreg);
+  const int h = lane / 32;
+
+  constexpr int kChunks = kShTile * kCPR;
+  constexpr int kPerThread = (kChunks + kShThreads - 1) / kShThreads;
+  uint4 pre[kPerThread];
+  // global -> registers for the stage starting at `base`
+  auto fetch = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = threadIdx.x + i * kShThreads;
+      if (q < kChunks) {
+        const int e = q / kCPR, part = q % kCPR;
+        const int ent = min(base + e, glim - 1);
+        if constexpr (KF == 0) {
+          pre[i] = reinterpret_cast<const uint4*>(a.k_idx + ((size_t)b * a.N + ent) * DI)[part];
+        } else {
+          // dims 8*part .. 8*part+7 in natural order, dequantised (exact in bf16)
+          const uint8_t* cp = a.k_codes + ((size_t)b * a.N + ent) * (DI / 2) + 4 * part;
+          const float sc = e8m0_to_f32(a.k_scales[((size_t)b * a.N + ent) * (DI / 32) + (8 * part) / 32]);
+          const uint32_t cw = *reinterpret_cast<const uint32_t*>(cp);
+          float f[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) f[k] = e2m1_to_f32((cw >> (4 * k)) & 15u) * sc;
+          pre[i] = pack8(f);
+        }
+      }
+    }
+  };
+  auto commit = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = threadIdx.x + i * kShThreads;
+      if (q < kChunks) {
+        const int e = q / kCPR, part = q % kCPR;
+        tile[st][e * kCPR + (part ^ (e & (kCPR - 1)))] = pre[i];
+      }
+    }
+  };
+
+  fetch(0);
+  commit(0);
+  __syncthreads();
+  int st = 0;
+  for (int base = 0; base < glim; base += kShTile) {
+    const bool more = base + kShTile < glim;
+    if (more) fetch(base + kShTile);
+    if (active && base < limit) {
+#pragma unroll
+      for (int sub = 0; sub < kShTile / 32; ++sub) {
+        const int slot0 = base + 32 * sub;
+        if (slot0 < limit) {
+          bf16x8 breg[DI / 16];
+          const int e = 32 * sub + lane % 32;
+#pragma unroll
+          for (int ks = 0; ks < DI / 16; ++ks) {
+            // LDS holds natural dim order; read the dims this lane's A registers hold
+            const int part = dim_of<DI, KF>(ks, h) / 8;
+            breg[ks] = as_bf16x8(tile[st][e * kCPR + (part ^ (e & (kCPR - 1)))]);
+          }
+          const float s = tile_score<DI, MT>(areg, breg, wreg);
+          emit<kBlockMax>(a, row, lane, slot0 + lane % 32, limit, s);
+        }
+      }
+    }
+    if (more) commit(st ^ 1);
+    __syncthreads();
+    st ^= 1;
+  }
+  (void)rows_total;
+}
+
+template <int DI, int KF, int MT>
+hipError_t launch3(const ScanArgs& s, const Dev& d, hipStream_t st) {
+  const int rows = s.B * s.T;
+  const bool cand = s.cand != nullptr;
+  const bool bm = s.block_max != nullptr;
+  if (!cand && s.T >= kShWaves) {
+    const int gps = (s.T + kShWaves - 1) / kShWaves;
+    dim3 grid(gps * s.B);
+    if (bm) hipLaunchKernelGGL((scan_shared<DI, KF, MT, true>), grid, dim3(kShThreads), 0, st, d, rows);
+    else hipLaunchKernelGGL((scan_shared<DI, KF, MT, false>), grid, dim3(kShThreads), 0, st, d, rows);
+    return hipGetLastError();
+  }
+  const int len = cand ? s.cand_stride : s.N;
+  // chunk: a multiple of 128 entries; aim for >= 2048 workgroups in total
+  int chunk = 4096;
+  while (chunk > 512 && (long long)rows * ((len + chunk - 1) / chunk) < 2048) chunk /= 2;
+  dim3 grid(rows, (len + chunk - 1) / chunk);
+  if (cand) {
+    hipLaunchKernelGGL((scan_private<DI, KF, MT, true, false>), grid, dim3(kPrivThreads), 0, st, d, chunk);
+  } else if (bm) {
+    hipLaunchKernelGGL((scan_private<DI, KF, MT, false, true>), grid, dim3(kPrivThreads), 0, st, d, chunk);
+  } else {
+    hipLaunchKernelGGL((scan_private<DI, KF, MT, false, false>), grid, dim3(kPrivThreads), 0, st, d, chunk);
+  }
+  return hipGetLastError();
+}
+
+template <int DI, int KF>
+hipError_t launch2(const ScanArgs& s, const Dev& d, hipStream_t st) {
+  return s.H_I <= 32 ? launch3<DI, KF, 1>(s, d, st) : launch3<DI, KF, 2>(s, d, st);
+}
+
+template <int DI>
+hipError_t launch1(const ScanArgs& s, const Dev& d, hipStream_t st) {
+  return s.k_dtype == CSA2_MXFP4 ? launch2<DI, 1>(s, d, st) : launch2<DI, 0>(s, d, st);
+}
+
+}  // namespace
+
+hipError_t launch_index_scan(const ScanArgs& s, hipStream_t st) {
+  if (s.B * s.T == 0) return hipSuccess;
+  // every pointer a kernel dereferences must be set
+  if (!s.q_idx || !s.w || !s.q_pos || !s.scores || (s.N > 0 && s.k_dtype == CSA2_BF16 && !s.k_idx) ||
+      (s.N > 0 && s.k_dtype == CSA2_MXFP4 && (!s.k_codes || !s.k_scales)) ||
+      (s.cand && (!s.n_cand || s.cand_stride < 1)))
+    return hipErrorInvalidValue;
+  Dev d;
+  d.T = s.T; d.H_I = s.H_I; d.N = s.N; d.m = s.m; d.block = s.block > 0 ? s.block : 1;
+  d.cand_stride = s.cand_stride; d.nblk = s.nblk;
+  d.q_idx = (const uint16_t*)s.q_idx; d.w = s.w; d.q_pos = s.q_pos;
+  d.k_idx = (const uint16_t*)s.k_idx; d.k_codes = s.k_codes; d.k_scales = s.k_scales;
+  d.cand = s.cand; d.n_cand = s.n_cand; d.scores = s.scores; d.row_stride = s.row_stride;
+  d.block_max = s.block_max;
+  ScopedProf p(st, s.cand ? "index_scan_reindex" : (s.T >= kShWaves ? "index_scan_prefill" : "index_scan_decode"));
+  switch (s.d_I) {
+    case 32: return launch1<32>(s, d, st);
+    case 64: return launch1<64>(s, d, st);
+    case 128: return launch1<128>(s, d, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace csa2

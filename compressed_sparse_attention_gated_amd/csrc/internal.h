@@ -1,0 +1,77 @@
+// Internal interface between the host API (api.cpp) and the kernel launchers (*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+// kernel timing hooks (no-ops unless csa2_profile_enable(1) on this thread)
+void prof_begin(hipStream_t s, const char* name);
+void prof_end(hipStream_t s);
+
+struct ScopedProf {
+  hipStream_t s;
+  ScopedProf(hipStream_t st, const char* name) : s(st) { prof_begin(st, name); }
+  ~ScopedProf() { prof_end(s); }
+};
+
+// ---- compressor (compress.hip)
+hipError_t launch_compress(const csa2_compress_desc& d, hipStream_t s);
+
+// ---- indexer scan (index.hip)
+struct ScanArgs {
+  int B, T, H_I, d_I, N, m, block;
+  const void* q_idx;
+  const float* w;
+  const int32_t* q_pos;
+  csa2_dtype k_dtype;
+  const void* k_idx;
+  const uint8_t *k_codes, *k_scales;
+  const int32_t *cand, *n_cand;  // REINDEX: score slots of cand instead of entries 0..n_vis-1
+  int cand_stride;
+  float* scores;          // [B*T, row_stride]
+  int64_t row_stride;
+  float* block_max;       // [B*T, nblk] or null (FULL only)
+  int nblk;
+};
+hipError_t launch_index_scan(const ScanArgs& a, hipStream_t s);
+
+// ---- top-k selection (topk.hip)
+// Rows of fp32 scores; row r has length len(r) given either by the causal rule
+// (q_pos, m, N) or by counts[r]; idx_map (optional) maps a slot to the reported id.
+struct TopkArgs {
+  int rows, k;
+  const float* scores;
+  int64_t row_stride;
+  // row length: if counts != null, len = counts[r]; else len = min(N, floor(q_pos[r]/m))
+  // (with `len_div` > 1 meaning ceil(len / len_div), used for block rows)
+  const int32_t* counts;
+  const int32_t* q_pos;
+  int N, m, len_div;
+  int force_last;          // 1: the row's last slot always wins (hierarchical pool)
+  const int32_t* idx_map;  // [rows, idx_map_stride] or null
+  int64_t idx_map_stride;
+  int32_t* out_idx;        // [rows, k]
+  int max_len;             // upper bound of len over rows (sizes the launch)
+  void* ws;                // workspace for the two-level path
+  size_t ws_bytes;
+};
+size_t topk_workspace_bytes(int rows, int k, int max_len);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// expand selected blocks (ascending, -1 padded) into candidate positions
+hipError_t launch_hier_expand(int rows, int n_keep, int block, const int32_t* sel_blocks,
+                              const int32_t* q_pos, int N, int m, int32_t* out_cand,
+                              int32_t* out_count, hipStream_t s);
+
+hipError_t launch_copy_idx(const int32_t* src, int32_t* dst, size_t n, hipStream_t s);
+
+// ---- sparse attention (attn.hip)
+size_t attn_workspace_bytes(const csa2_attn_desc& d);
+hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace csa2
