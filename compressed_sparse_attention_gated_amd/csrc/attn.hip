@@ -43,8 +43,9 @@ struct AttnDev {
   const float* sink;
   void* out;
   float* out_mass;
-  float* part_o;   // [rows][n_hg][splits][64][c]
-  float* part_ml;  // [rows][n_hg][splits][2][64]
+  float* part_o;   // [rows][n_hg][splits][32][c]
+  float* part_ml;  // [rows][n_hg][splits][2][32]
+  RopeFreq rope;   // theta^(-2u/r)
 };
 
 struct WinRange {
@@ -103,10 +104,10 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 #pragma unroll
   for (int j = 0; j < kSimpleMaxPerLane; ++j) {
     const int ch = lane + 64 * j;
-    const float other = __shfl_xor(qv[j], 1, 64);
+    const float other = dpp<kDppXor1>(qv[j]);
     if (a.rope_dims > 0 && ch < c && ch >= c - a.rope_dims) {
       float cs, sn;
-      rope_cos_sin((double)t_pos, (ch - (c - a.rope_dims)) / 2, a.rope_dims, a.rope_theta, &cs, &sn);
+      rope_cs((double)t_pos, a.rope.f[(ch - (c - a.rope_dims)) / 2], &cs, &sn);
       qv[j] = (ch & 1) ? (other * sn + qv[j] * cs) : (qv[j] * cs - other * sn);
     }
   }
@@ -171,10 +172,10 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 #pragma unroll
   for (int j = 0; j < kSimpleMaxPerLane; ++j) {
     const int ch = lane + 64 * j;
-    const float other = __shfl_xor(o[j], 1, 64);
+    const float other = dpp<kDppXor1>(o[j]);
     if (a.rope_dims > 0 && ch < c && ch >= c - a.rope_dims) {
       float cs, sn;
-      rope_cos_sin(-(double)t_pos, (ch - (c - a.rope_dims)) / 2, a.rope_dims, a.rope_theta, &cs, &sn);
+      rope_cs(-(double)t_pos, a.rope.f[(ch - (c - a.rope_dims)) / 2], &cs, &sn);
       o[j] = (ch & 1) ? (other * sn + o[j] * cs) : (o[j] * cs - other * sn);
     }
   }
@@ -189,48 +190,59 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 
 // ------------------------------------------------------------------ attn_mfma
 constexpr int kC = 512;           // channels
-constexpr int kHG = 64;           // heads per workgroup
+constexpr int kHG = 32;           // heads per workgroup
 constexpr int kTile = 32;         // rows per tile
 constexpr int kRowBytes = kC * 2;
 constexpr int kThreadsM = 256;
-constexpr int kChunksPerRow = kRowBytes / 16;  // 64
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// XOR swizzle of the 16-byte chunk index within a row (low 4 bits only)
-__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-__device__ __forceinline__ int chunk_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
-}
+// LDS row pitch: 1024 B of bf16 channels + 16 B of padding, so the 16 rows read by one
+// MFMA A operand (16 B each) fall in different banks, and every offset inside a tile is
+// a compile-time immediate.
+constexpr int kPitch = kRowBytes + 16;
+constexpr int kPPitch = kTile + 8;    // P rows (bf16), padded likewise
+constexpr int kMaxSplitTiles = 32;    // row tiles per split (slots staged in LDS)
+// Softmax reference: each head fixes the max of its first valid tile as the reference m
+// and keeps it; the final normalisation divides by a sum taken with the same reference,
+// so the result is the exact softmax for any m, and the accumulators are never rescaled.
+// Terms are 2^(z - m) <= 2^kOverflow; if a later tile exceeds m by more than that, the
+// split starts again with the larger reference (never for normalised inputs, where
+// |z| <= sqrt(c) * log2(e)).
+constexpr float kOverflow = 60.0f;
 
 struct MfmaSmem {
-  // two row tiles; the first 64 KiB also stage q_hat ([64 heads][512] bf16) and, at the
-  // end, the bf16 output tile
-  alignas(16) uint8_t tile[2][kTile * kRowBytes];
-  alignas(16) uint16_t pbuf[kHG][kTile];  // P in PV A-operand order (bf16)
-  float alpha[kHG];
-  float mfin[kHG], lfin[kHG];
-  uint32_t vmask[2];
-  int src_row[2][kTile];  // per tile row: >= 0 kv entry id, -2-w window row w, -1 empty
+  // two row tiles; the same bytes also stage q_hat ([32 heads][kPitch]) before the loop
+  // and the bf16 output tile ([32][512]) after it
+  alignas(16) uint8_t tile[2][kTile * kPitch];
+  alignas(16) uint16_t pbuf[kHG][kPPitch];  // P in PV A-operand order (bf16)
+  float wmax[2][kHG];                       // per row half: tile max per head
+  float lpart[2][kHG];                      // per row half: sum of p per head
+  float mfin[kHG];
+  float rope_c[64], rope_s[64];             // cos/sin of the query position, per frequency
+  int ovf[4];                               // per wave: a head overflowed its reference
+  int src[kMaxSplitTiles * kTile];          // per slot: >= 0 kv entry id, -2-w window row w, -1 empty
 };
+static_assert(sizeof(MfmaSmem) <= 80 * 1024, "two workgroups per CU");
 
-// fetch registers for one tile: each thread holds up to 8 chunks (bf16 rows) or 2 FP4
-// code chunks + their 2 scale bytes
+// registers for one tile in flight.  bf16 rows: wave w owns rows w, w+4, .., w+28 and
+// lane l carries their 16-byte chunk l.  FP4 rows: thread q = tid + 256*i carries code
+// chunk q%16 of row q/16 and the two E4M3 scales of its 32 channels.
+template <bool kFP4>
 struct Prefetch {
   uint4 v[8];
-  uint4 fc[2];
-  uint32_t fs[2];
+  uint4 fc[kFP4 ? 2 : 1];
+  uint32_t fs[kFP4 ? 2 : 1];
 };
 
-__device__ __forceinline__ void resolve_rows(const AttnDev& a, int row, int b, int slot0, int slot_end,
-                                             const WinRange& wr, int* src) {
-  // one thread per tile row
-  const int r = threadIdx.x;
-  if (r < kTile) {
-    const int s = slot0 + r;
+// slot -> row source, for the slots [slot0, slot0 + n) of this split
+__device__ __forceinline__ void stage_slots(const AttnDev& a, int row, int slot0, int n, int R,
+                                            const WinRange& wr, int* src) {
+  for (int i = threadIdx.x; i < n; i += kThreadsM) {
+    const int s = slot0 + i;
     int v = -1;
-    if (s < slot_end) {
+    if (s < R) {
       if (s < a.k) {
         const int e = a.idx[(size_t)row * a.k + s];
         v = (e >= 0 && e < a.N) ? e : -1;
@@ -238,33 +250,30 @@ __device__ __forceinline__ void resolve_rows(const AttnDev& a, int row, int b, i
         v = -2 - (wr.lo_row + (s - a.k));
       }
     }
-    src[r] = v;
+    src[i] = v;
   }
 }
 
-__device__ __forceinline__ void fetch_tile(const AttnDev& a, int b, const int* src, Prefetch& pf) {
-  const int tid = threadIdx.x;
-  // bf16 rows (kv rows when bf16, window rows always): chunk q = tid + 256*i -> row q/64
+template <bool kFP4>
+__device__ __forceinline__ void fetch_tile(const AttnDev& a, int b, const int* src, Prefetch<kFP4>& pf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 6) + 4 * i, ch = tid & 63;
-    const int sr = src[r];
+    const int sr = __builtin_amdgcn_readfirstlane(src[wave + 4 * i]);  // uniform per wave
     const uint16_t* base = nullptr;
     if (sr <= -2) base = (const uint16_t*)a.win + ((size_t)b * a.Lw + (-2 - sr)) * kC;
-    else if (sr >= 0 && a.kv_kind == 0) base = (const uint16_t*)a.kv + ((size_t)b * a.N + sr) * kC;
-    pf.v[i] = base ? reinterpret_cast<const uint4*>(base)[ch] : make_uint4(0, 0, 0, 0);
+    else if (!kFP4 && sr >= 0) base = (const uint16_t*)a.kv + ((size_t)b * a.N + sr) * kC;
+    pf.v[i] = base ? reinterpret_cast<const uint4*>(base)[lane] : make_uint4(0, 0, 0, 0);
   }
-  if (a.kv_kind == 1) {
-    // FP4 rows: 16 code chunks of 16 B per row -> q = tid + 256*i, row q/16, part q%16
+  if constexpr (kFP4) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i;
+      const int q = threadIdx.x + 256 * i;
       const int r = q >> 4, part = q & 15;
       const int sr = src[r];
       if (sr >= 0) {
         pf.fc[i] = reinterpret_cast<const uint4*>(a.kv_codes + ((size_t)b * a.N + sr) * (kC / 2))[part];
-        const uint8_t* sp = a.kv_scales + ((size_t)b * a.N + sr) * (kC / 16) + 2 * part;
-        pf.fs[i] = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+        pf.fs[i] = *reinterpret_cast<const uint16_t*>(a.kv_scales + ((size_t)b * a.N + sr) * (kC / 16) + 2 * part);
       } else {
         pf.fc[i] = make_uint4(0, 0, 0, 0);
         pf.fs[i] = 0;
@@ -273,22 +282,22 @@ __device__ __forceinline__ void fetch_tile(const AttnDev& a, int b, const int* s
   }
 }
 
-__device__ __forceinline__ void commit_tile(const AttnDev& a, const int* src, const Prefetch& pf, uint8_t* tile) {
-  const int tid = threadIdx.x;
+template <bool kFP4>
+__device__ __forceinline__ void commit_tile(const int* src, const Prefetch<kFP4>& pf, uint8_t* tile) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 6) + 4 * i, ch = tid & 63;
-    const int sr = src[r];
-    if (sr <= -2 || sr == -1 || a.kv_kind == 0)
-      *reinterpret_cast<uint4*>(tile + chunk_off(r, ch)) = pf.v[i];
+    const int r = wave + 4 * i;
+    const int sr = __builtin_amdgcn_readfirstlane(src[r]);
+    if (!kFP4 || sr < 0) *reinterpret_cast<uint4*>(tile + r * kPitch + 16 * lane) = pf.v[i];
   }
-  if (a.kv_kind == 1) {
+  if constexpr (kFP4) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i;
+      const int q = threadIdx.x + 256 * i;
       const int r = q >> 4, part = q & 15;
       if (src[r] >= 0) {
-        // 32 codes -> channels 32*part .. 32*part+31, scales for groups 2*part, 2*part+1
+        // 32 codes -> channels 32*part .. 32*part+31; scales of groups 2*part, 2*part+1
         const float s0 = e4m3_to_f32(pf.fs[i] & 0xffu), s1 = e4m3_to_f32(pf.fs[i] >> 8);
         const uint32_t words[4] = {pf.fc[i].x, pf.fc[i].y, pf.fc[i].z, pf.fc[i].w};
 #pragma unroll
@@ -297,14 +306,24 @@ __device__ __forceinline__ void commit_tile(const AttnDev& a, const int* src, co
           const float sc = qq < 2 ? s0 : s1;
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((words[qq] >> (4 * e)) & 15u) * sc;
-          *reinterpret_cast<uint4*>(tile + chunk_off(r, 4 * part + qq)) = pack8(f);
+          *reinterpret_cast<uint4*>(tile + r * kPitch + 64 * part + 16 * qq) = pack8(f);
         }
       }
     }
   }
 }
 
-__global__ void __launch_bounds__(kThreadsM) attn_mfma(AttnDev a) {
+// cos/sin of t_pos * theta^(-2u/r) for u < r/2, one thread per frequency
+__device__ __forceinline__ void stage_rope(const AttnDev& a, int t_pos, float* rc, float* rs) {
+  const int u = threadIdx.x;
+  if (a.rope_dims > 0 && u < a.rope_dims / 2) rope_cs((double)t_pos, a.rope.f[u], &rc[u], &rs[u]);
+}
+
+// Workgroup = one query x 32 heads x one split of its row slots.  Wave w = (hq, mr):
+// S^T tile rows 16*mr.. x heads 16*hq.. of each 32-row tile; for PV, wave w owns output
+// channels 128*w .. 128*w+127 of all 32 heads.
+template <bool kFP4>
+__global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   MfmaSmem& sm = *reinterpret_cast<MfmaSmem*>(smem_raw);
   const int split = blockIdx.y;
@@ -313,167 +332,173 @@ __global__ void __launch_bounds__(kThreadsM) attn_mfma(AttnDev a) {
   const int b = row / a.T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
+  const int hq = wave & 1, mr = wave >> 1;
   const int t_pos = a.q_pos[row];
   const WinRange wr = window_of(a, b, t_pos);
   const int R = a.k + wr.cnt;
   const int n_tiles = (R + kTile - 1) / kTile;
   const int tile0 = split * a.tiles_per_split;
   const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
+  const int rope_lo = kC - a.rope_dims;
+  const int head0 = hg * kHG;
 
-  // ---- q_hat for this wave's 16 heads -> LDS (bf16) -> B-operand registers
-  uint16_t* qs = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [64][512]
-  for (int hh = 0; hh < 16; ++hh) {
-    const int hl = 16 * wave + hh;
-    const int head = hg * kHG + hl;
-    const uint16_t* qp = (const uint16_t*)a.q + ((size_t)row * a.H + head) * kC + 8 * lane;
-    float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(qp), f);
-    if (a.q_norm) {
-      float ss = 0.f;
+  // ---- every global load of the prologue at once: this split's slot ids, and the q rows
+  // ---- of this wave's 8 heads
+  if (tile0 < tile1) stage_slots(a, row, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, sm.src);
+  uint4 qraw[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-      ss = wave_sum(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)kC + a.eps);
+  for (int hh = 0; hh < 8; ++hh)
+    qraw[hh] = *reinterpret_cast<const uint4*>((const uint16_t*)a.q + ((size_t)row * a.H + head0 + 8 * wave + hh) * kC + 8 * lane);
+  stage_rope(a, t_pos, sm.rope_c, sm.rope_s);
+  __syncthreads();
+  // rows of the first tile start travelling while q_hat is formed
+  Prefetch<kFP4> pf;
+  if (tile0 < tile1) fetch_tile<kFP4>(a, b, sm.src, pf);
+
+  // ---- q_hat = RoPE_t(RMSNorm(q)) * scale * log2(e) -> LDS (bf16) -> B-operand registers
+  uint8_t* qs = sm.tile[0];  // [32 heads][kPitch]
+  float qf[8][8];
+  float ssq[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] *= inv;
-    }
-    if (a.rope_dims > 0 && 8 * lane + 8 > kC - a.rope_dims) {
+  for (int hh = 0; hh < 8; ++hh) {
+    unpack8(qraw[hh], qf[hh]);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += qf[hh][e] * qf[hh][e];
+    ssq[hh] = ss;
+  }
+  if (a.q_norm) {
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) ssq[hh] = wave_sum(ssq[hh]);
+  }
+  const bool rope_lane = a.rope_dims > 0 && 8 * lane + 8 > rope_lo;
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) {
+    float* f = qf[hh];
+    const float mul = a.q_norm ? a.scale_log2 * fast_rsqrt(ssq[hh] / (float)kC + a.eps) : a.scale_log2;
+    if (rope_lane) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const int ch = 8 * lane + e;
-        if (ch >= kC - a.rope_dims) {
-          float cs, sn;
-          rope_cos_sin((double)t_pos, (ch - (kC - a.rope_dims)) / 2, a.rope_dims, a.rope_theta, &cs, &sn);
-          const float x0 = f[e], x1 = f[e + 1];
-          f[e] = x0 * cs - x1 * sn;
-          f[e + 1] = x0 * sn + x1 * cs;
-        }
+        const int u = max(ch - rope_lo, 0) >> 1;
+        const float cs = ch >= rope_lo ? sm.rope_c[u] : 1.f, sn = ch >= rope_lo ? sm.rope_s[u] : 0.f;
+        const float x0 = f[e], x1 = f[e + 1];
+        f[e] = x0 * cs - x1 * sn;
+        f[e + 1] = x0 * sn + x1 * cs;
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] *= a.scale_log2;
-    *reinterpret_cast<uint4*>(qs + hl * kC + 8 * lane) = pack8(f);
+    for (int e = 0; e < 8; ++e) f[e] *= mul;
+    *reinterpret_cast<uint4*>(qs + (8 * wave + hh) * kPitch + 16 * lane) = pack8(f);
   }
   __syncthreads();
   bf16x8 qreg[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks)
-    qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qs + (16 * wave + li) * kC + 32 * ks + 8 * g));
+    qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qs + (16 * hq + li) * kPitch + 64 * ks + 16 * g));
   __syncthreads();
 
-  // ---- state
-  float m_run = -INFINITY, l_run = 0.f;  // head 16*wave + li (replicated over g)
-  f32x4 oacc[4][8];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // per-lane LDS byte offsets (tile-relative): A operand row 16*mr + li at chunk g;
+  // transpose-read source rows 4g + li/4 (and +16) at channel 128*wave + 4*(li%4)
+  const int a_off = (16 * mr + li) * kPitch + 16 * g;
+  const int t_off0 = (4 * g + (li >> 2)) * kPitch + 8 * (li & 3) + 256 * wave;
+  const int t_off1 = t_off0 + 16 * kPitch;
+  const int my_head = 16 * hq + li;  // WG-local head of this lane's S^T column
 
-  Prefetch pf;
-  if (tile0 < tile1) {
-    resolve_rows(a, row, b, tile0 * kTile, R, wr, sm.src_row[0]);
-    __syncthreads();
-    fetch_tile(a, b, sm.src_row[0], pf);
-  }
-  int buf = 0;
-  for (int ti = tile0; ti < tile1; ++ti) {
-    commit_tile(a, sm.src_row[buf], pf, sm.tile[buf]);
-    if (threadIdx.x == 0) {
-      uint32_t vm = 0;
-      for (int r = 0; r < kTile; ++r) vm |= (sm.src_row[buf][r] != -1 ? 1u : 0u) << r;
-      sm.vmask[buf] = vm;
+  float m_use = -INFINITY, l_part = 0.f;  // head my_head, rows of half mr (replicated over g)
+  f32x4 oacc[2][8];
+  for (int pass = 0;; ++pass) {
+    if (pass > 0) {  // restart with a larger reference: every wave left the loop together
+      __syncthreads();
+      fetch_tile<kFP4>(a, b, sm.src, pf);
     }
-    const bool more = ti + 1 < tile1;
-    if (more) resolve_rows(a, row, b, (ti + 1) * kTile, R, wr, sm.src_row[buf ^ 1]);
-    __syncthreads();
-    if (more) fetch_tile(a, b, sm.src_row[buf ^ 1], pf);
+    l_part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool overflow = false;
+    int buf = 0;
+    for (int ti = tile0; ti < tile1; ++ti) {
+      const int* src = sm.src + (ti - tile0) * kTile;
+      commit_tile<kFP4>(src, pf, sm.tile[buf]);
+      __syncthreads();
+      if (ti + 1 < tile1) fetch_tile<kFP4>(a, b, src + kTile, pf);
+      // valid rows of this wave's half: row 16*mr + r <-> bit r
+      const uint32_t vm = (uint32_t)__ballot(lane < 16 && src[16 * mr + (lane & 15)] != -1);
 
-    const uint8_t* tl = sm.tile[buf];
-    const lds_u8* tl3 = (const lds_u8*)tl;  // LDS view for the transpose reads
-    const uint32_t vm = sm.vmask[buf];
-    // ---- S^T = rows x heads for this wave's 16 heads (two 16-row M tiles)
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      const uint8_t* tl = sm.tile[buf];
+      const lds_u8* tl3 = (const lds_u8*)tl;
+      // ---- S^T tile: rows 16*mr.. x heads 16*hq..; A reads issued ahead of the MFMAs
+      bf16x8 av[16];
 #pragma unroll
-    for (int mr = 0; mr < 2; ++mr) {
-      const int r = 16 * mr + li;
+      for (int ks = 0; ks < 16; ++ks) av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tl + a_off + 64 * ks));
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(tl + chunk_off(r, 4 * ks + g)));
-        sacc[mr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[ks], sacc[mr], 0, 0, 0);
-      }
-    }
-    // lane holds head 16*wave+li, rows 16*mr + 4*g + j
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mr = 0; mr < 2; ++mr)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if ((vm >> (16 * mr + 4 * g + j)) & 1u) tmax = fmaxf(tmax, sacc[mr][j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == m_run) ? 1.0f : exp2f(m_run - m_new);
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int mr = 0; mr < 2; ++mr)
+      for (int ks = 0; ks < 16; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], qreg[ks], sacc, 0, 0, 0);
+      // lane holds head my_head, rows 16*mr + 4*g + j
+      bool valid[4];
+      float tmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool v = (vm >> (16 * mr + 4 * g + j)) & 1u;
-        const float pv = v ? exp2f(sacc[mr][j] - m_new) : 0.f;
-        p[4 * mr + j] = pv;
-        psum += pv;
+        valid[j] = (vm >> (4 * g + j)) & 1u;
+        if (valid[j]) tmax = fmaxf(tmax, sacc[j]);
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // P for head 16*wave+li, k-slots 8g..8g+7 = rows {4g..4g+3, 16+4g..16+4g+3}
-    *reinterpret_cast<uint4*>(&sm.pbuf[16 * wave + li][8 * g]) = pack8(p);
-    if (g == 0) sm.alpha[16 * wave + li] = alpha;
-    __syncthreads();
+      tmax = rows_max(tmax);
+      if (g == 0) sm.wmax[mr][my_head] = tmax;
+      __syncthreads();
+      tmax = fmaxf(sm.wmax[0][my_head], sm.wmax[1][my_head]);  // whole 32-row tile
+      if (m_use == -INFINITY) m_use = tmax;  // first valid tile of this head: O is still 0
+      const bool ovf = tmax > m_use + kOverflow;
+      float p[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = valid[j] ? exp2f(sacc[j] - m_use) : 0.f;
+        psum += p[j];
+      }
+      l_part += rows_sum(psum);
+      // P for head my_head, k-slots 8g + 4*mr + j = row 16*mr + 4g + j
+      *reinterpret_cast<uint2*>(&sm.pbuf[my_head][8 * g + 4 * mr]) =
+          make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+      if (lane == 0) sm.ovf[wave] = __ballot(ovf) != 0;
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(sm.ovf[0] | sm.ovf[1] | sm.ovf[2] | sm.ovf[3])) {
+        overflow = true;
+        m_use = fmaxf(m_use, tmax);
+        break;
+      }
 
-    // ---- O[:, 128*wave .. +128] = O * alpha + P x V
+      // ---- O[:, 128*wave .. +128] += P x V
+      bf16x8 pa[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      float al[4];
+      for (int mt = 0; mt < 2; ++mt) pa[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.pbuf[16 * mt + li][8 * g]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = sm.alpha[16 * mt + 4 * g + j];
+      for (int nt = 0; nt < 8; ++nt) {
+        // channels 128*wave + 16*nt + (0..15); rows 4g..4g+3 and 16+4g..16+4g+3
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off0 + 32 * nt));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off1 + 32 * nt));
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) oacc[mt][nt][j] *= al[j];
+        for (int mt = 0; mt < 2; ++mt)
+          oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], bv, oacc[mt][nt], 0, 0, 0);
+      }
+      buf ^= 1;
     }
-    bf16x8 pa[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) pa[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.pbuf[16 * mt + li][8 * g]));
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int ch_base = 128 * wave + 16 * nt;
-      // source lane (g, s=li): row base + li/4, channels ch_base + 4*(li%4) .. +3
-      const int chunk = (ch_base >> 3) + ((li & 3) >> 1);
-      const int within = 8 * (li & 1);
-      const int r0 = 4 * g + (li >> 2);
-      const int r1 = 16 + 4 * g + (li >> 2);
-      const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + chunk_off(r0, chunk) + within));
-      const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + chunk_off(r1, chunk) + within));
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], bv, oacc[mt][nt], 0, 0, 0);
-    }
-    buf ^= 1;
+    if (!overflow) break;
   }
 
   // ---- finish: publish (m, l) per head
-  if (g == 0) { sm.mfin[16 * wave + li] = m_run; sm.lfin[16 * wave + li] = l_run; }
+  if (g == 0) {
+    sm.lpart[mr][my_head] = l_part;
+    if (mr == 0) sm.mfin[my_head] = m_use;
+  }
   __syncthreads();
-  const int head0 = hg * kHG;
   if (a.splits > 1) {
     const size_t pidx = ((size_t)row * a.n_hg + hg) * a.splits + split;
     float* po = a.part_o + pidx * kHG * kC;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -482,33 +507,33 @@ __global__ void __launch_bounds__(kThreadsM) attn_mfma(AttnDev a) {
     if (threadIdx.x < kHG) {
       float* pml = a.part_ml + pidx * 2 * kHG;
       pml[threadIdx.x] = sm.mfin[threadIdx.x];
-      pml[kHG + threadIdx.x] = sm.lfin[threadIdx.x];
+      pml[kHG + threadIdx.x] = sm.lpart[0][threadIdx.x] + sm.lpart[1][threadIdx.x];
     }
     return;
   }
   // single split: normalise, inverse-rotate, stage bf16 output in LDS, coalesced store
-  uint16_t* os = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [64][512]
+  uint16_t* os = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [32][512], contiguous
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < 2; ++mt) {
     float inv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int hl = 16 * mt + 4 * g + j;
-      const float l = sm.lfin[hl], m = sm.mfin[hl];
+      const float l = sm.lpart[0][hl] + sm.lpart[1][hl], m = sm.mfin[hl];
       float den = l;
       if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + hl] * kLog2e - m);
-      inv[j] = l > 0.f ? 1.0f / den : 0.f;
+      inv[j] = l > 0.f ? fast_rcp(den) : 0.f;
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const int ch = 128 * wave + 16 * nt + li;
       float cs = 1.f, sn = 0.f;
-      const bool rot = a.rope_dims > 0 && ch >= kC - a.rope_dims;
-      if (rot) rope_cos_sin(-(double)t_pos, (ch - (kC - a.rope_dims)) / 2, a.rope_dims, a.rope_theta, &cs, &sn);
+      const bool rot = a.rope_dims > 0 && ch >= rope_lo;
+      if (rot) { cs = sm.rope_c[(ch - rope_lo) >> 1]; sn = -sm.rope_s[(ch - rope_lo) >> 1]; }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float v = oacc[mt][nt][j] * inv[j];
-        const float other = __shfl_xor(v, 1, 64);
+        const float other = dpp<kDppXor1>(v);
         float o = v;
         if (rot) o = (ch & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
         os[(16 * mt + 4 * g + j) * kC + ch] = f32_to_bf16_bits(o);
@@ -516,7 +541,7 @@ __global__ void __launch_bounds__(kThreadsM) attn_mfma(AttnDev a) {
     }
   }
   if (a.out_mass && threadIdx.x < kHG) {
-    const float l = sm.lfin[threadIdx.x], m = sm.mfin[threadIdx.x];
+    const float l = sm.lpart[0][threadIdx.x] + sm.lpart[1][threadIdx.x], m = sm.mfin[threadIdx.x];
     float den = l;
     if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + threadIdx.x] * kLog2e - m);
     a.out_mass[(size_t)row * a.H + head0 + threadIdx.x] = l > 0.f ? l / den : 0.f;
@@ -527,50 +552,55 @@ __global__ void __launch_bounds__(kThreadsM) attn_mfma(AttnDev a) {
   for (int q = threadIdx.x; q < kHG * kC / 8; q += kThreadsM) op[q] = src[q];
 }
 
-// merge the splits of one (query, 64-head group) in split order
+// merge the splits of one query for 4 heads (one head per wave, 8 channels per lane), in
+// split order
+constexpr int kCombHeads = 4;
 __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
-  const int row = blockIdx.x, hg = blockIdx.y;
+  __shared__ float rc[64], rs[64];
+  const int row = blockIdx.x;
+  const int hg = blockIdx.y / (kHG / kCombHeads);
+  const int hl = (blockIdx.y % (kHG / kCombHeads)) * kCombHeads + threadIdx.x / 64;
+  const int c8 = (threadIdx.x % 64) * 8;
   const int t_pos = a.q_pos[row];
+  const int rope_lo = kC - a.rope_dims;
+  stage_rope(a, t_pos, rc, rs);
   const size_t pbase = ((size_t)row * a.n_hg + hg) * a.splits;
   const int head0 = hg * kHG;
-  for (int q = threadIdx.x; q < kHG * kC / 8; q += 256) {
-    const int hl = q / (kC / 8), c8 = (q % (kC / 8)) * 8;
-    float mx = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_ml[(pbase + s) * 2 * kHG + hl]);
-    float l = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (mx != -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float ms = a.part_ml[(pbase + s) * 2 * kHG + hl];
-        if (ms == -INFINITY) continue;
-        const float wgt = exp2f(ms - mx);
-        l += wgt * a.part_ml[(pbase + s) * 2 * kHG + kHG + hl];
-        const float4* po = reinterpret_cast<const float4*>(a.part_o + ((pbase + s) * kHG + hl) * kC + c8);
-        const float4 x0 = po[0], x1 = po[1];
-        o[0] += wgt * x0.x; o[1] += wgt * x0.y; o[2] += wgt * x0.z; o[3] += wgt * x0.w;
-        o[4] += wgt * x1.x; o[5] += wgt * x1.y; o[6] += wgt * x1.z; o[7] += wgt * x1.w;
-      }
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_ml[(pbase + s) * 2 * kHG + hl]);
+  float l = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (mx != -INFINITY) {
+    for (int s = 0; s < a.splits; ++s) {
+      const float ms = a.part_ml[(pbase + s) * 2 * kHG + hl];
+      if (ms == -INFINITY) continue;
+      const float wgt = exp2f(ms - mx);
+      l += wgt * a.part_ml[(pbase + s) * 2 * kHG + kHG + hl];
+      const float4* po = reinterpret_cast<const float4*>(a.part_o + ((pbase + s) * kHG + hl) * kC + c8);
+      const float4 x0 = po[0], x1 = po[1];
+      o[0] += wgt * x0.x; o[1] += wgt * x0.y; o[2] += wgt * x0.z; o[3] += wgt * x0.w;
+      o[4] += wgt * x1.x; o[5] += wgt * x1.y; o[6] += wgt * x1.z; o[7] += wgt * x1.w;
     }
-    float den = l;
-    if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + hl] * kLog2e - mx);
-    const float inv = l > 0.f ? 1.0f / den : 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= inv;
-    if (a.rope_dims > 0 && c8 + 8 > kC - a.rope_dims) {
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const int ch = c8 + e;
-        if (ch >= kC - a.rope_dims) {
-          float cs, sn;
-          rope_cos_sin(-(double)t_pos, (ch - (kC - a.rope_dims)) / 2, a.rope_dims, a.rope_theta, &cs, &sn);
-          const float x0 = o[e], x1 = o[e + 1];
-          o[e] = x0 * cs - x1 * sn;
-          o[e + 1] = x0 * sn + x1 * cs;
-        }
-      }
-    }
-    *reinterpret_cast<uint4*>((uint16_t*)a.out + ((size_t)row * a.H + head0 + hl) * kC + c8) = pack8(o);
-    if (a.out_mass && c8 == 0) a.out_mass[(size_t)row * a.H + head0 + hl] = l > 0.f ? l * inv : 0.f;
   }
+  float den = l;
+  if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + hl] * kLog2e - mx);
+  const float inv = l > 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] *= inv;
+  __syncthreads();
+  if (a.rope_dims > 0 && c8 + 8 > rope_lo) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int ch = c8 + e;
+      if (ch >= rope_lo) {
+        const float cs = rc[(ch - rope_lo) >> 1], sn = -rs[(ch - rope_lo) >> 1];
+        const float x0 = o[e], x1 = o[e + 1];
+        o[e] = x0 * cs - x1 * sn;
+        o[e + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+  *reinterpret_cast<uint4*>((uint16_t*)a.out + ((size_t)row * a.H + head0 + hl) * kC + c8) = pack8(o);
+  if (a.out_mass && c8 == 0) a.out_mass[(size_t)row * a.H + head0 + hl] = l > 0.f ? l * inv : 0.f;
 }
 
 bool mfma_ok(const csa2_attn_desc& d) {
@@ -587,6 +617,8 @@ void pick_splits(const csa2_attn_desc& d, int* splits, int* tps) {
   int s = d.num_splits > 0 ? d.num_splits : (512 + rows * n_hg - 1) / (rows * n_hg);
   if (s < 1) s = 1;
   if (s > n_tiles) s = n_tiles;
+  const int min_s = (n_tiles + kMaxSplitTiles - 1) / kMaxSplitTiles;
+  if (s < min_s) s = min_s;
   const int per = (n_tiles + s - 1) / s;
   *tps = per < 1 ? 1 : per;
   *splits = (n_tiles + *tps - 1) / *tps;
@@ -606,6 +638,7 @@ AttnDev make_dev(const csa2_attn_desc& d) {
   a.idx = d.idx; a.win = d.win; a.win_pos0 = d.win_pos0; a.sink = d.sink; a.out = d.out;
   a.out_mass = d.out_mass;
   a.n_hg = d.H / kHG;
+  rope_freq_host(&a.rope, d.rope_dims, d.rope_theta);
   return a;
 }
 
@@ -652,18 +685,23 @@ hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipSt
   const size_t lds = sizeof(MfmaSmem);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)attn_mfma<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  {
-    ScopedProf p(s, d.kv_dtype == CSA2_FP4_E4M3 ? "attn_mfma_fp4" : "attn_mfma");
-    hipLaunchKernelGGL(attn_mfma, dim3(rows, splits, a.n_hg), dim3(kThreadsM), lds, s, a);
+  if (d.kv_dtype == CSA2_FP4_E4M3) {
+    ScopedProf p(s, "attn_mfma_fp4");
+    hipLaunchKernelGGL(attn_mfma<true>, dim3(rows, splits, a.n_hg), dim3(kThreadsM), lds, s, a);
+  } else {
+    ScopedProf p(s, "attn_mfma");
+    hipLaunchKernelGGL(attn_mfma<false>, dim3(rows, splits, a.n_hg), dim3(kThreadsM), lds, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
   ScopedProf p(s, "attn_combine");
-  hipLaunchKernelGGL(attn_combine, dim3(rows, a.n_hg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine, dim3(rows, a.n_hg * (kHG / kCombHeads)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "../../include/csa2.h"
@@ -20,15 +21,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
-// round to nearest even; NaN stays NaN
+// round to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // 16 bytes holding 8 bf16 -> 8 floats
@@ -77,34 +77,104 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 // ----------------------------------------------------------------- wave helpers
+// Lane exchanges without address arithmetic: DPP within 16-lane rows, ds_swizzle across
+// the two 16-lane rows of a 32-lane half, ds_bpermute (precomputed address) across halves.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
+__device__ __forceinline__ float swz_xor16(float v) {  // lane l <- lane l^16 (within 32)
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (0x10 << 10) | 0x1F));
+}
+__device__ __forceinline__ float xor32(float v) {  // lane l <- lane l^32
+  const int addr = ((__lane_id() ^ 32) << 2);
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+}
+// sum over all 64 lanes, returned in every lane
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  v += swz_xor16(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  v = fmaxf(v, swz_xor16(v));
+  return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
+}
+// sum / max over the 4 lanes l, l^16, l^32, l^48 (the four 16-lane rows)
+__device__ __forceinline__ float rows_sum(float v) {
+  v += swz_xor16(v);
+  return v + xor32(v);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  v = fmaxf(v, swz_xor16(v));
+  return fmaxf(v, xor32(v));
 }
 // sum over aligned groups of G lanes (G a power of two <= 64)
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if constexpr (G >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (G >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (G >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (G >= 32) v += swz_xor16(v);
+  if constexpr (G >= 64) v += xor32(v);
   return v;
 }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ----------------------------------------------------------------- RoPE angle
-// cos/sin of pos * theta^(-2u/r): the angle is formed and reduced modulo 2*pi in fp64
-// (positions reach 2^20, where an fp32 product loses ~0.06 rad), then evaluated in fp32.
-__device__ __forceinline__ void rope_cos_sin(double pos, int u, int r, float theta, float* c, float* s) {
-  double freq = exp2(-2.0 * (double)u / (double)r * log2((double)theta));
-  double a = pos * freq;
-  const double two_pi = 6.283185307179586476925286766559;
-  a = a - two_pi * floor(a / two_pi);
-  float af = (float)a;
-  sincosf(af, s, c);
+// Frequencies theta^(-2u/r), u < r/2, computed on the host in double precision and passed
+// by value with the kernel arguments.
+constexpr int kMaxRopePairs = 64;
+struct RopeFreq {
+  double f[kMaxRopePairs];
+};
+inline void rope_freq_host(RopeFreq* rf, int r, float theta) {
+  for (int u = 0; u < kMaxRopePairs; ++u)
+    rf->f[u] = (r > 0 && u < r / 2) ? pow((double)theta, -2.0 * (double)u / (double)r) : 0.0;
+}
+
+// cos/sin of pos * freq.  The angle (|pos| <= 2^31, freq <= 1) is formed and reduced by
+// pi/2 in fp64 - a single fp32 product would lose ~0.06 rad at positions near 2^20 - and
+// the reduced argument |x| <= pi/4 goes through the Taylor series of sin and cos in fp32
+// (truncation below 2e-9), with the quadrant applied afterwards.
+__device__ __forceinline__ void rope_cs(double pos, double freq, float* c, float* s) {
+  const double a = pos * freq;
+  const double q = rint(a * 0.63661977236758134308);          // 2/pi
+  const double r = fma(-q, 1.5707963267948966192, a);         // pi/2
+  const float x = (float)r, x2 = x * x;
+  // sin x = x - x^3/3! + x^5/5! - x^7/7! + x^9/9!
+  float sn = fmaf(x2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+  sn = fmaf(x2, sn, 1.0f / 120.0f);
+  sn = fmaf(x2, sn, -1.0f / 6.0f);
+  sn = fmaf(x2 * x, sn, x);
+  // cos x = 1 - x^2/2! + x^4/4! - x^6/6! + x^8/8! - x^10/10!
+  float cs = fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+  cs = fmaf(x2, cs, -1.0f / 720.0f);
+  cs = fmaf(x2, cs, 1.0f / 24.0f);
+  cs = fmaf(x2, cs, -0.5f);
+  cs = fmaf(x2, cs, 1.0f);
+  const long long qi = (long long)q;
+  switch (qi & 3) {
+    case 0: *c = cs; *s = sn; break;
+    case 1: *c = -sn; *s = cs; break;
+    case 2: *c = -cs; *s = -sn; break;
+    default: *c = sn; *s = -cs; break;
+  }
 }
 
 }  // namespace csa2

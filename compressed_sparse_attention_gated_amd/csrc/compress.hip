@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
     int n, int c, int m, int overlap, const T* __restrict__ ca, const T* __restrict__ za,
     const T* __restrict__ cb, const T* __restrict__ zb, const float* __restrict__ ba,
     const float* __restrict__ bb, const int32_t* __restrict__ pos0, int norm, float eps,
-    int rope_dims, float rope_theta, T* __restrict__ out, int64_t out_bstride,
+    int rope_dims, RopeFreq rope, T* __restrict__ out, int64_t out_bstride,
     const T* __restrict__ w_ik, int d_index, T* __restrict__ out_ik, int64_t out_ik_bstride) {
   constexpr bool kProj = kDI > 0;
   extern __shared__ float xs[];  // [kRowsPerWG][c] pre-RoPE normalised entries (kProj only)
@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
       ss = group_sum<G>(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)c + eps);
+      const float inv = fast_rsqrt(ss / (float)c + eps);
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] *= inv;
     }
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
         const int cc = ch + e;
         if (cc >= c - rope_dims) {
           float cs, sn;
-          rope_cos_sin(pos, (cc - (c - rope_dims)) / 2, rope_dims, rope_theta, &cs, &sn);
+          rope_cs(pos, rope.f[(cc - (c - rope_dims)) / 2], &cs, &sn);
           const float x0 = y[e], x1 = y[e + 1];
           y[e] = x0 * cs - x1 * sn;
           y[e + 1] = x0 * sn + x1 * cs;
@@ -171,9 +171,11 @@ hipError_t launch_t(const csa2_compress_desc& d, hipStream_t s) {
   const int64_t ob = d.out_batch_stride ? d.out_batch_stride : (int64_t)n_ent * d.c;
   const int64_t oib = d.out_ik_batch_stride ? d.out_ik_batch_stride : (int64_t)n_ent * d.d_index;
   const size_t lds = kDI > 0 ? (size_t)kRowsPerWG * d.c * sizeof(float) : 0;
+  RopeFreq rope;
+  rope_freq_host(&rope, d.rope_dims, d.rope_theta);
   hipLaunchKernelGGL((compress_kernel<T, G, kDI>), grid, dim3(kThreads), lds, s, d.n, d.c, d.m,
                      d.overlap, (const T*)d.ca, (const T*)d.za, (const T*)d.cb, (const T*)d.zb, d.ba,
-                     d.bb, d.pos0, d.norm, d.eps, d.rope_dims, d.rope_theta, (T*)d.out, ob,
+                     d.bb, d.pos0, d.norm, d.eps, d.rope_dims, rope, (T*)d.out, ob,
                      (const T*)d.w_ik, d.d_index, (T*)d.out_ik, oib);
   return hipGetLastError();
 }

@@ -126,7 +126,7 @@ __device__ __forceinline__ float tile_score(const bf16x8 (*areg)[DI / 16], const
     for (int r = 0; r < 16; ++r) s += wreg[mt][r] * fmaxf(acc[r], 0.f);
   }
   // lanes l and l^32 hold the two halves of the head rows of the same entry
-  s += __shfl_xor(s, 32, 64);
+  s += xor32(s);
   return s;
 }
 
@@ -143,7 +143,12 @@ __device__ __forceinline__ void emit(const Dev& a, int row, int lane, int slot, 
   if (lane < 32 && ok) a.scores[(size_t)row * a.row_stride + slot] = s;
   if constexpr (kBlockMax) {
     float v = ok ? s : -INFINITY;
-    for (int o = 1; o < a.block; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    // max over aligned groups of `block` lanes: quad swaps, then mirrors pair the halves
+    if (a.block >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+    if (a.block >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+    if (a.block >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    if (a.block >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+    if (a.block >= 32) v = fmaxf(v, swz_xor16(v));
     if (lane < 32 && ok && (slot % a.block) == 0) a.block_max[(size_t)row * a.nblk + slot / a.block] = v;
   }
 }

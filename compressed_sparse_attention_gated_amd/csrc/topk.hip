@@ -36,7 +36,7 @@ struct RowSrc {
   }
 };
 
-struct Smem {
+struct alignas(16) Smem {
   uint32_t hist[kBins];
   uint32_t wsum[kWavesTk];
   uint32_t wgt[kWavesTk], weq[kWavesTk];
@@ -201,9 +201,29 @@ __device__ __forceinline__ int32_t map_id(const Params& p, int r, int slot) {
   return p.idx_map ? p.idx_map[(size_t)r * p.idx_map_stride + slot] : slot;
 }
 
+// Keys of a row or chunk staged once into LDS (vector loads); all passes then run from
+// LDS.  Up to kStageMax keys are staged; longer rows are read from global memory.
+constexpr int kStageMax = 32768;
+
+__device__ __forceinline__ void stage_keys(const float* scores, int n, int force, uint32_t* keys) {
+  const bool vec = (((uintptr_t)scores) & 15u) == 0;
+  const int n4 = vec ? n / 4 : 0;
+  for (int i = threadIdx.x; i < n4; i += kThreads) {
+    const float4 v = reinterpret_cast<const float4*>(scores)[i];
+    keys[4 * i] = float_key(v.x); keys[4 * i + 1] = float_key(v.y);
+    keys[4 * i + 2] = float_key(v.z); keys[4 * i + 3] = float_key(v.w);
+  }
+  for (int i = 4 * n4 + threadIdx.x; i < n; i += kThreads) keys[i] = float_key(scores[i]);
+  __syncthreads();
+  if (force >= 0 && threadIdx.x == 0) keys[force] = 0xffffffffu;
+  __syncthreads();
+}
+
 // single level: one workgroup per row
-__global__ void __launch_bounds__(kThreads) topk_single(Params p) {
-  __shared__ Smem sm;
+__global__ void __launch_bounds__(kThreads) topk_single(Params p, int stage_cap) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + sizeof(Smem));
   const int r = blockIdx.x;
   const int n = row_len(p, r);
   int32_t* out = p.out_idx + (size_t)r * p.k;
@@ -211,15 +231,23 @@ __global__ void __launch_bounds__(kThreads) topk_single(Params p) {
     for (int i = threadIdx.x; i < p.k; i += kThreads) out[i] = i < n ? map_id(p, r, i) : -1;
     return;
   }
-  RowSrc src{p.scores + (size_t)r * p.row_stride, nullptr, p.force_last ? n - 1 : -1};
+  const float* row = p.scores + (size_t)r * p.row_stride;
+  const int force = p.force_last ? n - 1 : -1;
+  RowSrc src{row, nullptr, force};
+  if (n <= stage_cap) {
+    stage_keys(row, n, force, skeys);
+    src = RowSrc{nullptr, skeys, -1};
+  }
   uint32_t T, take;
   radix_threshold(src, n, p.k, sm, &T, &take);
   ordered_compact(src, n, p.k, T, take, sm, [&](uint32_t pos, int i, uint32_t) { out[pos] = map_id(p, r, i); });
 }
 
 // two-level, first level: grid (rows, nchunks); chunk c of row r -> ws[r][c*k .. c*k+k)
-__global__ void __launch_bounds__(kThreads) topk_chunk(Params p) {
-  __shared__ Smem sm;
+__global__ void __launch_bounds__(kThreads) topk_chunk(Params p, int stage_cap) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + sizeof(Smem));
   const int r = blockIdx.x, c = blockIdx.y;
   const int n = row_len(p, r);
   const int c0 = c * p.chunk;
@@ -227,13 +255,18 @@ __global__ void __launch_bounds__(kThreads) topk_chunk(Params p) {
   uint32_t* ok = p.ws_keys + ((size_t)r * p.nchunks + c) * p.k;
   int32_t* os = p.ws_slot + ((size_t)r * p.nchunks + c) * p.k;
   const int force = (p.force_last && n > 0 && n - 1 >= c0 && n - 1 < c0 + p.chunk) ? (n - 1 - c0) : -1;
-  RowSrc src{p.scores + (size_t)r * p.row_stride + c0, nullptr, force};
+  const float* row = p.scores + (size_t)r * p.row_stride + c0;
+  RowSrc src{row, nullptr, force};
   if (len <= p.k) {
     for (int i = threadIdx.x; i < p.k; i += kThreads) {
       ok[i] = i < len ? src.key(i) : 0u;
       os[i] = i < len ? c0 + i : -1;
     }
     return;
+  }
+  if (len <= stage_cap) {
+    stage_keys(row, len, force, skeys);
+    src = RowSrc{nullptr, skeys, -1};
   }
   uint32_t T, take;
   radix_threshold(src, len, p.k, sm, &T, &take);
@@ -244,8 +277,10 @@ __global__ void __launch_bounds__(kThreads) topk_chunk(Params p) {
 }
 
 // two-level, second level: one workgroup per row over nchunks*k pairs; key 0 marks padding
-__global__ void __launch_bounds__(kThreads) topk_merge(Params p) {
-  __shared__ Smem sm;
+__global__ void __launch_bounds__(kThreads) topk_merge(Params p, int stage_cap) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + sizeof(Smem));
   const int r = blockIdx.x;
   const int n = row_len(p, r);
   int32_t* out = p.out_idx + (size_t)r * p.k;
@@ -255,7 +290,18 @@ __global__ void __launch_bounds__(kThreads) topk_merge(Params p) {
     return;
   }
   const int m = p.nchunks * p.k;
-  RowSrc src{nullptr, p.ws_keys + (size_t)r * m, -1};
+  const uint32_t* gkeys = p.ws_keys + (size_t)r * m;
+  RowSrc src{nullptr, gkeys, -1};
+  if (m <= stage_cap) {
+    const uint4* g4 = reinterpret_cast<const uint4*>(gkeys);  // k is a multiple of 4 here or not:
+    if ((m & 3) == 0 && (((uintptr_t)gkeys) & 15u) == 0) {
+      for (int i = threadIdx.x; i < m / 4; i += kThreads) reinterpret_cast<uint4*>(skeys)[i] = g4[i];
+    } else {
+      for (int i = threadIdx.x; i < m; i += kThreads) skeys[i] = gkeys[i];
+    }
+    __syncthreads();
+    src = RowSrc{nullptr, skeys, -1};
+  }
   uint32_t T, take;
   radix_threshold(src, m, p.k, sm, &T, &take);
   ordered_compact(src, m, p.k, T, take, sm, [&](uint32_t pos, int i, uint32_t) {
@@ -313,6 +359,11 @@ size_t topk_workspace_bytes(int rows, int k, int max_len) {
   return (size_t)rows * nchunks * k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
+static hipError_t set_lds(const void* fn, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   // every pointer a kernel dereferences must be set
@@ -325,9 +376,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   p.force_last = a.force_last; p.idx_map = a.idx_map; p.idx_map_stride = a.idx_map_stride;
   p.out_idx = a.out_idx;
   p.max_len = a.max_len;
+  hipError_t e;
   if (a.max_len <= kSingleMax) {
+    const int cap = a.max_len < kStageMax ? a.max_len : kStageMax;
+    const size_t lds = sizeof(Smem) + (size_t)cap * 4;
+    if ((e = set_lds((const void*)topk_single, lds)) != hipSuccess) return e;
     ScopedProf pr(s, "topk_single");
-    hipLaunchKernelGGL(topk_single, dim3(a.rows), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(topk_single, dim3(a.rows), dim3(kThreads), lds, s, p, cap);
     return hipGetLastError();
   }
   p.chunk = pick_chunk(a.max_len, a.k);
@@ -335,14 +390,21 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   p.ws_keys = (uint32_t*)a.ws;
   p.ws_slot = (int32_t*)((char*)a.ws + (size_t)a.rows * p.nchunks * a.k * sizeof(uint32_t));
   {
+    const int cap = p.chunk < kStageMax ? p.chunk : kStageMax;
+    const size_t lds = sizeof(Smem) + (size_t)cap * 4;
+    if ((e = set_lds((const void*)topk_chunk, lds)) != hipSuccess) return e;
     ScopedProf pr(s, "topk_chunk");
-    hipLaunchKernelGGL(topk_chunk, dim3(a.rows, p.nchunks), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(topk_chunk, dim3(a.rows, p.nchunks), dim3(kThreads), lds, s, p, cap);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
+    const int m = p.nchunks * a.k;
+    const int cap = m < kStageMax ? m : kStageMax;
+    const size_t lds = sizeof(Smem) + (size_t)cap * 4;
+    if ((e = set_lds((const void*)topk_merge, lds)) != hipSuccess) return e;
     ScopedProf pr(s, "topk_merge");
-    hipLaunchKernelGGL(topk_merge, dim3(a.rows), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(topk_merge, dim3(a.rows), dim3(kThreads), lds, s, p, cap);
   }
   return hipGetLastError();
 }
