@@ -224,7 +224,7 @@ def main():
     ms = time_steps(torch, step, args.steps, args.warmup)
     kern = per_kernel(C, torch, step, args.steps)
 
-    scan_name = "index_scan_decode"
+    scan_name = next((n for n in kern if n.startswith("index_scan")), "index_scan_decode")
     attn_name = "attn_mfma_fp4" if fp4 else "attn_mfma"
     k_bytes = wl.d_I // 2 + wl.d_I // 32 if fp4 else wl.d_I * 2
     row_bytes = 288 if fp4 else wl.c * 2
@@ -236,7 +236,7 @@ def main():
     workload_tag = "decode_full_b32_l65536" if not fp4 else "decode_fp4_b64_l262144"
     traffic = load_traffic(scan_name, workload_tag)
     stages = {k: {**v} for k, v in kern.items()}
-    stages[scan_name]["algorithmic_bytes"] = scan_bytes
+    stages.setdefault(scan_name, {})["algorithmic_bytes"] = scan_bytes
     stages[scan_name]["GB_per_s"] = achieved
     stages[scan_name]["frac_hbm"] = achieved / HBM_PEAK_GBS
     if attn_name in stages:

@@ -184,9 +184,20 @@ static int check_index(const csa2_index_desc* d, csa2_mode mode) {
   return CSA2_OK;
 }
 
+// decode-style FULL calls (few queries per sequence, long rows) fuse the chunk-local
+// top-k into the scan; the workspace then holds (key, slot) pairs instead of scores
+static bool use_fused(const csa2_index_desc* d, csa2_mode mode) {
+  return mode == CSA2_MODE_FULL && d->T < 8 && d->N > 8192;
+}
+
 static size_t index_ws(const csa2_index_desc* d, csa2_mode mode) {
   const size_t rows = (size_t)d->B * d->T;
   if (mode == CSA2_MODE_REUSE || rows == 0) return 0;
+  if (use_fused(d, mode)) {
+    const int chunk = scan_select_chunk(d->N, d->k);
+    const size_t nchunks = (size_t)(d->N + chunk - 1) / chunk;
+    return align256(rows * nchunks * d->k * sizeof(uint32_t)) + align256(rows * nchunks * d->k * sizeof(int32_t));
+  }
   const int len = mode == CSA2_MODE_FULL ? d->N : d->cand_stride;
   size_t bytes = 0;
   if (!d->out_scores) bytes += align256(rows * (size_t)len * sizeof(float));
@@ -212,6 +223,26 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
   const size_t need = index_ws(d, mode);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(CSA2_ERR_WORKSPACE, "index: workspace of %zu bytes required, %zu given", need, ws_bytes);
+  if (use_fused(d, mode)) {
+    const int chunk = scan_select_chunk(d->N, d->k);
+    const int nchunks = (d->N + chunk - 1) / chunk;
+    uint32_t* keys = (uint32_t*)ws;
+    int32_t* slots = (int32_t*)((char*)ws + align256((size_t)rows * nchunks * d->k * sizeof(uint32_t)));
+    ScanArgs a{};
+    a.B = d->B; a.T = d->T; a.H_I = d->H_I; a.d_I = d->d_I; a.N = d->N; a.m = d->m;
+    a.block = d->block > 0 ? d->block : 1;
+    a.q_idx = d->q_idx; a.w = d->w; a.q_pos = d->q_pos; a.k_dtype = d->k_dtype; a.k_idx = d->k_idx;
+    a.k_codes = d->k_codes; a.k_scales = d->k_scales;
+    a.scores = d->out_scores; a.row_stride = d->N;
+    a.block_max = d->out_block_max;
+    a.nblk = (d->N + a.block - 1) / a.block;
+    hipError_t e = launch_index_scan_select(a, d->k, chunk, nchunks, keys, slots, s);
+    if (e != hipSuccess) return hip_status(e, "index/scan_select");
+    TopkArgs t{};
+    t.rows = (int)rows; t.k = d->k; t.q_pos = d->q_pos; t.N = d->N; t.m = d->m; t.len_div = 1;
+    t.out_idx = d->out_idx; t.max_len = d->N;
+    return hip_status(launch_topk_merge(t, nchunks, keys, slots, s), "index/topk_merge");
+  }
   const int len = mode == CSA2_MODE_FULL ? d->N : d->cand_stride;
   char* wp = (char*)ws;
   float* scores = d->out_scores;

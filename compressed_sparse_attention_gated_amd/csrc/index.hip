@@ -22,6 +22,9 @@
 
 #include "common.h"
 #include "internal.h"
+#include "topk_core.h"
+
+#include <type_traits>
 
 namespace csa2 {
 namespace {
@@ -136,21 +139,24 @@ __device__ __forceinline__ int n_visible(const Dev& a, int row) {
   return nv < a.N ? nv : a.N;
 }
 
+// block maxima of one 32-slot tile: max over aligned groups of `block` lanes (quad swaps,
+// then mirrors pair the halves), visible slots only
+__device__ __forceinline__ void emit_block_max(const Dev& a, int row, int lane, int slot, int limit, float s) {
+  const bool ok = slot < limit;
+  float v = ok ? s : -INFINITY;
+  if (a.block >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+  if (a.block >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+  if (a.block >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if (a.block >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  if (a.block >= 32) v = fmaxf(v, swz_xor16(v));
+  if (lane < 32 && ok && (slot % a.block) == 0) a.block_max[(size_t)row * a.nblk + slot / a.block] = v;
+}
+
 // write scores (lanes 0..31) and, optionally, block maxima of one 32-slot tile
 template <bool kBlockMax>
 __device__ __forceinline__ void emit(const Dev& a, int row, int lane, int slot, int limit, float s) {
-  const bool ok = slot < limit;
-  if (lane < 32 && ok) a.scores[(size_t)row * a.row_stride + slot] = s;
-  if constexpr (kBlockMax) {
-    float v = ok ? s : -INFINITY;
-    // max over aligned groups of `block` lanes: quad swaps, then mirrors pair the halves
-    if (a.block >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
-    if (a.block >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-    if (a.block >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-    if (a.block >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-    if (a.block >= 32) v = fmaxf(v, swz_xor16(v));
-    if (lane < 32 && ok && (slot % a.block) == 0) a.block_max[(size_t)row * a.nblk + slot / a.block] = v;
-  }
+  if (lane < 32 && slot < limit) a.scores[(size_t)row * a.row_stride + slot] = s;
+  if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, limit, s);
 }
 
 // ---------------------------------------------------------------- private-B scan
@@ -179,14 +185,15 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
     return s;
   };
 
-  int tb = c0 + 32 * wave;
-  if (tb >= c1) return;
-  bf16x8 bcur[DI / 16], bnext[DI / 16];
-  load_b<DI, KF>(a, b, entry_of(tb + lane % 32), h, bcur);
-  for (; tb < c1; tb += 32 * kWaves) {
-    const int tn = tb + 32 * kWaves;
-    if (tn < c1) load_b<DI, KF>(a, b, entry_of(tn + lane % 32), h, bnext);
-    float s = tile_score<DI, MT>(areg, bcur, wreg);
+  // three tiles in flight per wave: tile t is consumed while t+1 and t+2 load
+  constexpr int kStride = 32 * kWaves;
+  const int t0 = c0 + 32 * wave;
+  if (t0 >= c1) return;
+  bf16x8 b0[DI / 16], b1[DI / 16], b2[DI / 16];
+  load_b<DI, KF>(a, b, entry_of(t0 + lane % 32), h, b0);
+  load_b<DI, KF>(a, b, entry_of(t0 + kStride + lane % 32), h, b1);
+  auto consume = [&](const bf16x8* bb, int tb) {
+    float s = tile_score<DI, MT>(areg, bb, wreg);
     if constexpr (kCand) {
       const int slot = tb + lane % 32;
       if (slot < c1) {
@@ -195,9 +202,91 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
       }
     }
     emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
-#pragma unroll
-    for (int ks = 0; ks < DI / 16; ++ks) bcur[ks] = bnext[ks];
+  };
+  for (int tb = t0; tb < c1; tb += 3 * kStride) {
+    load_b<DI, KF>(a, b, entry_of(tb + 2 * kStride + lane % 32), h, b2);
+    consume(b0, tb);
+    if (tb + kStride >= c1) break;
+    load_b<DI, KF>(a, b, entry_of(tb + 3 * kStride + lane % 32), h, b0);
+    consume(b1, tb + kStride);
+    if (tb + 2 * kStride >= c1) break;
+    load_b<DI, KF>(a, b, entry_of(tb + 4 * kStride + lane % 32), h, b1);
+    consume(b2, tb + 2 * kStride);
   }
+}
+
+// ---------------------------------------------------------------- fused scan + chunk top-k
+// Decode: workgroup (query, chunk) scans its chunk like scan_private but keeps the keys of
+// its scores in LDS, then selects the chunk's top-k there and writes (key, slot) pairs;
+// the chunk union contains the row's top-k, which topk_merge extracts.
+constexpr int kSelThreads = 256;
+
+template <int DI, int KF, int MT, bool kBlockMax, bool kScores>
+__global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int k, int nchunks,
+                                                           uint32_t* wkeys, int32_t* wslot) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  TopkSmem<kSelThreads>& sm = *reinterpret_cast<TopkSmem<kSelThreads>*>(smem_raw);
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15));
+  const int row = blockIdx.x, c = blockIdx.y;
+  const int b = row / a.T;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int limit = n_visible(a, row);
+  const int c0 = c * chunk;
+  const int c1 = min(c0 + chunk, limit);
+  const int len = c1 - c0;
+  uint32_t* ok = wkeys + ((size_t)row * nchunks + c) * k;
+  int32_t* os = wslot + ((size_t)row * nchunks + c) * k;
+  if (len <= 0) {  // uniform: nothing visible in this chunk
+    for (int i = threadIdx.x; i < k; i += kSelThreads) { ok[i] = 0u; os[i] = -1; }
+    return;
+  }
+  bf16x8 areg[MT][DI / 16];
+  float wreg[MT][16];
+  load_query<DI, KF, MT>(a, row, lane, areg, wreg);
+  const int h = lane / 32;
+  // three tiles in flight per wave: tile t is consumed while t+1 and t+2 load
+  constexpr int kStride = 32 * kWaves;
+  const int t0 = c0 + 32 * wave;
+  if (t0 < c1) {
+    auto ent = [&](int slot) { return min(slot, c1 - 1); };
+    bf16x8 b0[DI / 16], b1[DI / 16], b2[DI / 16];
+    load_b<DI, KF>(a, b, ent(t0 + lane % 32), h, b0);
+    load_b<DI, KF>(a, b, ent(t0 + kStride + lane % 32), h, b1);
+    auto consume = [&](const bf16x8* bb, int tb) {
+      const float s = tile_score<DI, MT>(areg, bb, wreg);
+      const int slot = tb + lane % 32;
+      if (lane < 32 && slot < c1) skeys[slot - c0] = float_key(s);
+      if constexpr (kScores) {
+        if (lane < 32 && slot < c1) a.scores[(size_t)row * a.row_stride + slot] = s;
+      }
+      if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, c1, s);
+    };
+    for (int tb = t0; tb < c1; tb += 3 * kStride) {
+      load_b<DI, KF>(a, b, ent(tb + 2 * kStride + lane % 32), h, b2);
+      consume(b0, tb);
+      if (tb + kStride >= c1) break;
+      load_b<DI, KF>(a, b, ent(tb + 3 * kStride + lane % 32), h, b0);
+      consume(b1, tb + kStride);
+      if (tb + 2 * kStride >= c1) break;
+      load_b<DI, KF>(a, b, ent(tb + 4 * kStride + lane % 32), h, b1);
+      consume(b2, tb + 2 * kStride);
+    }
+  }
+  __syncthreads();
+  if (len <= k) {
+    for (int i = threadIdx.x; i < k; i += kSelThreads) {
+      ok[i] = i < len ? skeys[i] : 0u;
+      os[i] = i < len ? c0 + i : -1;
+    }
+    return;
+  }
+  const KeysLds src{skeys};
+  uint32_t T, take;
+  radix_threshold<kSelThreads>(src, len, k, sm, &T, &take);
+  ordered_compact<kSelThreads>(src, len, k, T, take, sm, [&](uint32_t pos, int i, uint32_t key) {
+    ok[pos] = key;
+    os[pos] = c0 + i;
+  });
 }
 
 // ---------------------------------------------------------------- shared-B scan (prefill)
@@ -342,7 +431,66 @@ hipError_t launch1(const ScanArgs& s, const Dev& d, hipStream_t st) {
   return s.k_dtype == CSA2_MXFP4 ? launch2<DI, 1>(s, d, st) : launch2<DI, 0>(s, d, st);
 }
 
+template <int DI, int KF, int MT>
+hipError_t launch_sel3(const ScanArgs& s, const Dev& d, int k, int chunk, int nchunks, uint32_t* keys,
+                       int32_t* slots, hipStream_t st) {
+  const size_t lds = ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15) + (size_t)chunk * 4;
+  dim3 grid(s.B * s.T, nchunks);
+  const bool bm = s.block_max != nullptr, sc = s.scores != nullptr;
+  const void* fn = bm ? (sc ? (const void*)scan_select<DI, KF, MT, true, true> : (const void*)scan_select<DI, KF, MT, true, false>)
+                      : (sc ? (const void*)scan_select<DI, KF, MT, false, true> : (const void*)scan_select<DI, KF, MT, false, false>);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (bm && sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
+  else if (bm) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
+  else if (sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, false, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
+  else hipLaunchKernelGGL((scan_select<DI, KF, MT, false, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
+  return hipGetLastError();
+}
+
+Dev make_dev(const ScanArgs& s) {
+  Dev d;
+  d.T = s.T; d.H_I = s.H_I; d.N = s.N; d.m = s.m; d.block = s.block > 0 ? s.block : 1;
+  d.cand_stride = s.cand_stride; d.nblk = s.nblk;
+  d.q_idx = (const uint16_t*)s.q_idx; d.w = s.w; d.q_pos = s.q_pos;
+  d.k_idx = (const uint16_t*)s.k_idx; d.k_codes = s.k_codes; d.k_scales = s.k_scales;
+  d.cand = s.cand; d.n_cand = s.n_cand; d.scores = s.scores; d.row_stride = s.row_stride;
+  d.block_max = s.block_max;
+  return d;
+}
+
 }  // namespace
+
+int scan_select_chunk(int N, int k) {
+  // a power of two >= 2048 such that the merge row (nchunks * k) stays <= 16384 keys
+  int chunk = 2048;
+  while ((long long)((N + chunk - 1) / chunk) * k > 16384 && chunk < (1 << 30)) chunk *= 2;
+  return chunk;
+}
+
+hipError_t launch_index_scan_select(const ScanArgs& s, int k, int chunk, int nchunks, uint32_t* keys,
+                                    int32_t* slots, hipStream_t st) {
+  if (s.B * s.T == 0) return hipSuccess;
+  if (!s.q_idx || !s.w || !s.q_pos || !keys || !slots || s.cand || (s.N > 0 && s.k_dtype == CSA2_BF16 && !s.k_idx) ||
+      (s.N > 0 && s.k_dtype == CSA2_MXFP4 && (!s.k_codes || !s.k_scales)) || chunk % 128 != 0 || k < 1)
+    return hipErrorInvalidValue;
+  const Dev d = make_dev(s);
+  ScopedProf p(st, "index_scan_select");
+  auto go = [&](auto di, auto kf) -> hipError_t {
+    constexpr int DI = decltype(di)::value, KF = decltype(kf)::value;
+    return s.H_I <= 32 ? launch_sel3<DI, KF, 1>(s, d, k, chunk, nchunks, keys, slots, st)
+                       : launch_sel3<DI, KF, 2>(s, d, k, chunk, nchunks, keys, slots, st);
+  };
+  const bool mx = s.k_dtype == CSA2_MXFP4;
+  switch (s.d_I) {
+    case 32: return mx ? go(std::integral_constant<int, 32>{}, std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 32>{}, std::integral_constant<int, 0>{});
+    case 64: return mx ? go(std::integral_constant<int, 64>{}, std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 64>{}, std::integral_constant<int, 0>{});
+    case 128: return mx ? go(std::integral_constant<int, 128>{}, std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 128>{}, std::integral_constant<int, 0>{});
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_index_scan(const ScanArgs& s, hipStream_t st) {
   if (s.B * s.T == 0) return hipSuccess;
@@ -351,13 +499,7 @@ hipError_t launch_index_scan(const ScanArgs& s, hipStream_t st) {
       (s.N > 0 && s.k_dtype == CSA2_MXFP4 && (!s.k_codes || !s.k_scales)) ||
       (s.cand && (!s.n_cand || s.cand_stride < 1)))
     return hipErrorInvalidValue;
-  Dev d;
-  d.T = s.T; d.H_I = s.H_I; d.N = s.N; d.m = s.m; d.block = s.block > 0 ? s.block : 1;
-  d.cand_stride = s.cand_stride; d.nblk = s.nblk;
-  d.q_idx = (const uint16_t*)s.q_idx; d.w = s.w; d.q_pos = s.q_pos;
-  d.k_idx = (const uint16_t*)s.k_idx; d.k_codes = s.k_codes; d.k_scales = s.k_scales;
-  d.cand = s.cand; d.n_cand = s.n_cand; d.scores = s.scores; d.row_stride = s.row_stride;
-  d.block_max = s.block_max;
+  const Dev d = make_dev(s);
   ScopedProf p(st, s.cand ? "index_scan_reindex" : (s.T >= kShWaves ? "index_scan_prefill" : "index_scan_decode"));
   switch (s.d_I) {
     case 32: return launch1<32>(s, d, st);

@@ -137,10 +137,15 @@ def test_index_validation(L):
     # REUSE needs no workspace; B*T == 0 is a no-op
     assert L.csa2_index_workspace_bytes(C.byref(_index(src_idx=FAKE)), U) == 0
     assert L.csa2_index_topk(C.byref(_index(B=0)), F, None, 0, None) == csa2.CSA2_OK
-    # long decode rows take the two-level selection, which needs extra workspace
-    short = L.csa2_index_workspace_bytes(C.byref(_index(N=30000)), F)
-    long_ = L.csa2_index_workspace_bytes(C.byref(_index(N=70000)), F)
-    assert short == (2 * 30000 * 4 + 255) // 256 * 256 and long_ > (2 * 70000 * 4 + 255) // 256 * 256
+    # decode rows (one query per sequence) fuse the chunk top-k into the scan: the
+    # workspace holds chunk candidates, far less than a score row
+    dec = L.csa2_index_workspace_bytes(C.byref(_index(N=70000)), F)
+    assert 0 < dec < 2 * 70000 * 4
+    # many queries per sequence keep a score row per query, plus the two-level buffers
+    # for rows longer than the single-workgroup limit
+    pre = L.csa2_index_workspace_bytes(C.byref(_index(B=1, T=16, N=30000)), F)
+    pre_long = L.csa2_index_workspace_bytes(C.byref(_index(B=1, T=16, N=70000)), F)
+    assert pre == (16 * 30000 * 4 + 255) // 256 * 256 and pre_long > (16 * 70000 * 4 + 255) // 256 * 256
 
 
 def test_hier_validation(L):
