@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound of the oracle sample")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
     return p.parse_args()
 
 
@@ -124,11 +126,13 @@ def load_traffic(kernel, workload):
             vals[k] = v
     import hashlib
 
-    src = os.path.join(ROOT, "compressed_sparse_attention_gated_amd", "csrc", vals.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if h != vals.get("source_sha256_16"):
+    h = hashlib.sha256()
+    for name in vals.get("source", "").split(","):
+        src = os.path.join(ROOT, "compressed_sparse_attention_gated_amd", "csrc", name.strip())
+        if not name.strip() or not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest()[:16] != vals.get("source_sha256_16"):
         return None
     try:
         return float(vals["bytes_per_launch"])
@@ -184,6 +188,19 @@ def cpu_baseline_decode(torch, wl, d, budget_s, fp4=False):
                       f"attention) by the fp64 numpy oracle, {spent:.1f} s"}
 
 
+def copy_probe(torch, mib):
+    """A plain device-to-device copy of known size: the scale for FETCH_SIZE / WRITE_SIZE."""
+    torch.cuda.set_device(0)
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 4}), flush=True)
+
+
 # ---------------------------------------------------------------------------- main
 def main():
     args = parse()
@@ -193,6 +210,9 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+        return
     sys.path.insert(0, ROOT)
     from compressed_sparse_attention_gated_amd import csa2 as C
     from compressed_sparse_attention_gated_amd import workloads as W
