@@ -17,6 +17,10 @@ from HIP events recorded around every kernel on its stream (a second timed pass;
 first pass, without per-kernel events, gives `value`).
 
     python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu-baseline]
+
+  --config 3  the 32,768-token prefill (value in tokens/s; the scan's roofline is bf16 MFMA)
+  --config 4  the hierarchical decoder group at 1M context (Full + pool + Reindex + 3 Reuse)
+  --config 5  the FP4 / MXFP4 cache decode
 """
 from __future__ import annotations
 
@@ -46,44 +50,6 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
     return p.parse_args()
-
-
-# ---------------------------------------------------------------------------- workloads
-def make_decode(torch, W, wl, seed, fp4=False):
-    """One instance of a decode workload on the device (seeded generator)."""
-    g = W.rng(seed, device="cuda")
-    B, L, c, H = wl.B, wl.L, wl.c, wl.H
-    d = {}
-    if fp4:
-        d.update(W.indexer_inputs(g, B, 1, L, wl.H_I, wl.d_I, wl.w_values, k_format="mxfp4"))
-        a = W.attn_inputs(g, B, 1, L, H, c, Lw=wl.window, kv_format="fp4")
-    else:
-        d.update(W.indexer_inputs(g, B, 1, L, wl.H_I, wl.d_I, wl.w_values))
-        a = W.attn_inputs(g, B, 1, L, H, c, Lw=wl.window)
-    d.update(a)
-    d["q_pos"] = torch.full((B, 1), L, dtype=torch.int32, device="cuda")
-    d["win_pos0"] = torch.full((B,), L - wl.window + 1, dtype=torch.int32, device="cuda")
-    # the new token's projected KV and gate logits (m = 1 compress input)
-    d["c_new"] = g.normal((B, 1, c), dtype="bf16")
-    d["z_new"] = g.normal((B, 1, c), dtype="bf16")
-    return d
-
-
-def decode_step(C, torch, wl, d, ws, out_idx, out, fp4=False):
-    B, c = wl.B, wl.c
-    # 1. compress: the new token's row (m = 1: RMSNorm + RoPE at position L) into the
-    #    last slot of the window buffer
-    win = d["win"]
-    C.csa2_compress(d["c_new"], d["z_new"], 1, pos0=d["q_pos"][:, 0], rope_dims=wl.rope_dims,
-                    out=win[:, wl.window - 1:, :])
-    # 2. indexer scan + top-k over all L visible entries
-    kw = (dict(k_codes=d["k_codes"], k_scales=d["k_scales"]) if fp4 else dict(k_idx=d["k_idx"]))
-    C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"], w=d["w"], m=1,
-                      out_idx=out_idx, workspace=ws["index"], **kw)
-    # 3. sparse attention over the selected entries + the window
-    kvkw = (dict(kv_codes=d["kv_codes"], kv_scales=d["kv_scales"]) if fp4 else dict(kv=d["kv"]))
-    C.csa2_sparse_attn(d["q"], d["q_pos"], out_idx, win=win, win_pos0=d["win_pos0"], n_win=wl.window,
-                       sink=d["sink"], rope_dims=wl.rope_dims, out=out, workspace=ws["attn"], **kvkw)
 
 
 # ---------------------------------------------------------------------------- timing
@@ -141,51 +107,92 @@ def load_traffic(kernel, workload):
 
 
 # ---------------------------------------------------------------------------- CPU baseline
-def cpu_baseline_decode(torch, wl, d, budget_s, fp4=False):
-    """The oracle, as it stands, on a bounded sample of the same decode workload: whole
-    queries (scan + top-k + attention) until about `budget_s` seconds of oracle work."""
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _h(t):
+    return t.float().cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
+
+
+def cpu_baseline(wl, d, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload: whole queries
+    (scan + top-k + attention; the whole layer group for the hierarchical workload) until
+    about `budget_s` seconds of oracle work.  Host copies of the inputs are not timed."""
     sys.path.insert(0, ROOT)
     import oracle as O
     from oracle import formats as F
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
     done, spent = 0, 0.0
-    b = 0
-    while spent < budget_s and b < wl.B:
-        # host copies of one sequence (not timed)
-        qi = d["q_idx"][b:b + 1].float().cpu().numpy().astype(np.float64)
-        w = d["w"][b:b + 1].cpu().numpy().astype(np.float64)
-        if fp4:
-            ki = F.mxfp4_decode(d["k_codes"][b:b + 1].cpu().numpy(), d["k_scales"][b:b + 1].cpu().numpy())
+    kind = wl.kind
+    n_units = wl.n_tokens if kind == "prefill" else wl.B
+    rs = np.random.default_rng(0)
+    while spent < budget_s and done < n_units:
+        if kind == "prefill":
+            # one query token at a random position over the compressed entries (the
+            # compressor's share, one entry per m tokens, is timed with it)
+            t = int(rs.integers(wl.n_tokens // 2, wl.n_tokens))
+            qi, w, q = _h(d["q_idx"][0, t]), _h(d["w"][0, t]), _h(d["q"][0, t])
+            blk = slice(wl.m * (t // wl.m), wl.m * (t // wl.m) + wl.m)
+            ca, za, w_ik = _h(d["ca"][0, blk]), _h(d["za"][0, blk]), _h(d["w_ik"])
+            kidx = _h(d["k_oracle"]) if "k_oracle" in d else None
+            win_src = _h(d["win_src"][0, max(0, t - wl.window + 1):t + 1])
+            sink = _h(d["sink"])
+            entries = d.get("e_oracle")
+            t0 = time.perf_counter()
+            O.compress(ca, za, wl.m, rope_dims=wl.rope_dims, pos0=blk.start, w_ik=w_ik)
+            wr, _ = O.compress(win_src, win_src, 1, rope_dims=wl.rope_dims, pos0=max(0, t - wl.window + 1))
+            nv = O.n_visible(t, wl.n_tokens // wl.m, wl.m)
+            idx = O.topk_indices(O.indexer_scores(qi, w, kidx, nv), wl.k)
+            sel = idx[idx >= 0]
+            O.sparse_attn(q[None, None], np.array([[t]]), entries[sel][None], np.arange(len(sel))[None, None],
+                          wr[None], [max(0, t - wl.window + 1)], wl.window, sink, rope_dims=wl.rope_dims)
         else:
-            ki = d["k_idx"][b:b + 1].float().cpu().numpy().astype(np.float64)
-        q = d["q"][b:b + 1].float().cpu().numpy().astype(np.float64)
-        win = d["win"][b:b + 1].float().cpu().numpy().astype(np.float64)
-        qp = d["q_pos"][b:b + 1].cpu().numpy()
-        wp0 = d["win_pos0"][b:b + 1].cpu().numpy()
-        sink = d["sink"].cpu().numpy().astype(np.float64)
-        if fp4:
-            kv_all = (d["kv_codes"][b:b + 1].cpu().numpy(), d["kv_scales"][b:b + 1].cpu().numpy())
-        else:
-            kv_all = d["kv"][b:b + 1].float().cpu().numpy()
-        t0 = time.perf_counter()
-        idx = O.index_topk_full(qi, w, ki, qp, 1, wl.k)
-        sel = idx[0, 0][idx[0, 0] >= 0]
-        kv_rows = (F.fp4_main_decode(kv_all[0][0, sel], kv_all[1][0, sel]) if fp4
-                   else kv_all[0, sel].astype(np.float64))
-        O.sparse_attn(q, qp, kv_rows[None], np.arange(len(sel))[None, None], win, wp0, wl.window, sink,
-                      rope_dims=wl.rope_dims)
+            b = done
+            hier = kind == "hier"
+            layers = d["layers"] if hier else [d]
+            fp4 = kind == "decode_fp4"
+            if fp4:
+                ki = F.mxfp4_decode(_h(d["k_codes"][b]), _h(d["k_scales"][b]))
+            else:
+                ki = _h(d["k_idx"][b])
+            qs = [(_h(e["q_idx"][b, 0]) if "q_idx" in e else None, _h(e["w"][b, 0]) if "w" in e else None,
+                   _h(e["q"][b, 0]), _h(e["win"][b]), _h(e["sink"])) for e in layers]
+            kv_b = ((d["kv_codes"][b], d["kv_scales"][b]) if fp4 else d["kv"][b])
+            L = wl.L
+            t0 = time.perf_counter()
+            s = O.indexer_scores(qs[0][0], qs[0][1], ki, L)
+            sels = [O.topk_indices(s, wl.k)]
+            if hier:
+                pool = O.hier_candidates(O.block_max(s, wl.block), L, n_keep=wl.n_keep_blocks, block=wl.block)
+                sels.append(O.reindex_topk(qs[1][0], qs[1][1], ki, pool, wl.k))
+                sels += [sels[1]] * (len(layers) - 2)
+            for (qi, w, q, win, sink), idx in zip(qs, sels):
+                sel = idx[idx >= 0]
+                st = torch.as_tensor(sel, device=kv_b[0].device if fp4 else kv_b.device)
+                if fp4:
+                    rows = F.fp4_main_decode(kv_b[0].index_select(0, st).cpu().numpy(),
+                                             kv_b[1].index_select(0, st).cpu().numpy())
+                else:
+                    rows = _h(kv_b.index_select(0, st))
+                O.sparse_attn(q[None, None], np.array([[L]]), rows[None], np.arange(len(sel))[None, None],
+                              win[None], [L - wl.window + 1], wl.window, sink, rope_dims=wl.rope_dims)
         spent += time.perf_counter() - t0
         done += 1
-        b += 1
-    return {"value": done / spent, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of the {wl.B} decode queries (full scan of {wl.L} entries, top-{wl.k}, "
-                      f"attention) by the fp64 numpy oracle, {spent:.1f} s"}
+    unit = "tokens/s" if kind == "prefill" else "queries/s"
+    what = {"prefill": f"{done} query tokens of the {wl.n_tokens}-token prefill (their compressor block and "
+                       f"window rows, causal scan, top-{wl.k}, attention)",
+            "hier": f"{done} of the {wl.B} queries, each through the whole 5-layer group (full scan of {wl.L}, "
+                    f"pool, Reindex, 5 attentions)",
+            }.get(kind, f"{done} of the {wl.B} decode queries (full scan of {wl.L} entries, top-{wl.k}, attention)")
+    return {"value": done / spent, "unit": unit, "cores": int(_cores()), "kind": "oracle",
+            "sample": f"{what} by the fp64 numpy oracle, {spent:.1f} s; the gathered rows are copied to the "
+                      "host inside the timed region"}
 
 
 def copy_probe(torch, mib):
@@ -202,6 +209,28 @@ def copy_probe(torch, mib):
 
 
 # ---------------------------------------------------------------------------- main
+TAGS = {2: "decode_full_b32_l65536", 3: "prefill_n32768", 4: "hier_b8_l1048576", 5: "decode_fp4_b64_l262144"}
+
+
+def scan_work(wl):
+    """Algorithmic bytes and flops of one indexer-scan launch (the Full layer's)."""
+    fp4 = wl.kind == "decode_fp4"
+    k_bytes = wl.d_I // 2 + wl.d_I // 32 if fp4 else wl.d_I * 2
+    q_bytes = wl.H_I * wl.d_I * 2 + wl.H_I * 4
+    if wl.kind == "prefill":
+        ne = wl.n_tokens // wl.m
+        pairs = sum(min(ne, t // wl.m) for t in range(wl.n_tokens))
+        return ne * k_bytes + wl.n_tokens * (q_bytes + wl.k * 4), 2.0 * wl.H_I * wl.d_I * pairs, pairs
+    pairs = wl.B * wl.L
+    return pairs * k_bytes + wl.B * q_bytes, 2.0 * wl.H_I * wl.d_I * pairs, pairs
+
+
+def attn_bytes(wl):
+    row_bytes = 288 if wl.kind == "decode_fp4" else wl.c * 2
+    queries = wl.n_tokens if wl.kind == "prefill" else wl.B
+    return queries * (wl.k * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2 + wl.k * 4)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,60 +244,66 @@ def main():
         return
     sys.path.insert(0, ROOT)
     from compressed_sparse_attention_gated_amd import csa2 as C
+    from compressed_sparse_attention_gated_amd import steps as S
     from compressed_sparse_attention_gated_amd import workloads as W
 
     C.lib()
     torch.cuda.set_device(0)
     wl = W.WORKLOADS[args.config]
-    if args.config not in (2, 5):
-        print("bench.py: only the decode workloads (--config 2, 5) are wired into the step yet",
-              file=sys.stderr)
-        sys.exit(2)
-    fp4 = args.config == 5
-    insts = [make_decode(torch, W, wl, 2000 + 17 * i, fp4=fp4) for i in range(2)]
-    out_idx = torch.empty((wl.B, 1, wl.k), dtype=torch.int32, device="cuda")
-    out = torch.empty((wl.B, 1, wl.H, wl.c), dtype=torch.bfloat16, device="cuda")
-    d0 = insts[0]
-    kw = (dict(k_codes=d0["k_codes"], k_scales=d0["k_scales"]) if fp4 else dict(k_idx=d0["k_idx"]))
-    ws_idx = C.csa2_index_workspace_bytes(C.CSA2_MODE_FULL, d0["q_pos"], wl.k, q_idx=d0["q_idx"], w=d0["w"],
-                                          m=1, out_idx=out_idx, **kw)
-    kvkw = (dict(kv_codes=d0["kv_codes"], kv_scales=d0["kv_scales"]) if fp4 else dict(kv=d0["kv"]))
-    ws_attn = C.csa2_attn_workspace_bytes(d0["q"], d0["q_pos"], out_idx, win=d0["win"], win_pos0=d0["win_pos0"],
-                                          n_win=wl.window, sink=d0["sink"], rope_dims=wl.rope_dims, out=out, **kvkw)
-    ws = {"index": torch.empty(max(ws_idx, 1), dtype=torch.uint8, device="cuda"),
-          "attn": torch.empty(max(ws_attn, 1), dtype=torch.uint8, device="cuda")}
+    make, Step = {"decode": (W.decode_inputs, S.DecodeStep), "decode_fp4": (W.decode_inputs, S.DecodeStep),
+                  "hier": (W.hier_inputs, S.HierStep), "prefill": (W.prefill_inputs, S.PrefillStep)}[wl.kind]
+    # two independent input instances alternate, so no step finds its rows cache-resident
+    n_inst = 2
+    insts = [make(wl, 2000 + 17 * i) for i in range(n_inst)]
+    runner = Step(wl, insts[0])
 
     def step(i):
-        decode_step(C, torch, wl, insts[i % 2], ws, out_idx, out, fp4=fp4)
+        runner.run(insts[i % n_inst])
 
     ms = time_steps(torch, step, args.steps, args.warmup)
     kern = per_kernel(C, torch, step, args.steps)
+    launches_per_step = {k: v["launches"] / args.steps for k, v in kern.items()}
 
-    scan_name = next((n for n in kern if n.startswith("index_scan")), "index_scan_decode")
-    attn_name = "attn_mfma_fp4" if fp4 else "attn_mfma"
-    k_bytes = wl.d_I // 2 + wl.d_I // 32 if fp4 else wl.d_I * 2
-    row_bytes = 288 if fp4 else wl.c * 2
-    scan_bytes = wl.B * wl.L * k_bytes + wl.B * (wl.H_I * wl.d_I * 2 + wl.H_I * 4)
-    attn_bytes = wl.B * (wl.k * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2 + wl.k * 4)
-    scan_ms = kern.get(scan_name, {}).get("avg_ms", float("nan"))
-    attn_ms = sum(v["avg_ms"] for k, v in kern.items() if k.startswith("attn_"))
-    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    workload_tag = "decode_full_b32_l65536" if not fp4 else "decode_fp4_b64_l262144"
-    traffic = load_traffic(scan_name, workload_tag)
-    stages = {k: {**v} for k, v in kern.items()}
-    stages.setdefault(scan_name, {})["algorithmic_bytes"] = scan_bytes
-    stages[scan_name]["GB_per_s"] = achieved
-    stages[scan_name]["frac_hbm"] = achieved / HBM_PEAK_GBS
-    if attn_name in stages:
-        a_gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
-        stages[attn_name]["algorithmic_bytes"] = attn_bytes
-        stages[attn_name]["GB_per_s_incl_combine"] = a_gbs
-        stages[attn_name]["frac_hbm_incl_combine"] = a_gbs / HBM_PEAK_GBS
-    value = wl.B / (ms * 1e-3)
+    # the Full layer's scan: the fused scan + chunk top-k at decode, the shared-tile scan at prefill
+    scan_name = "index_scan_prefill" if wl.kind == "prefill" else "index_scan_select"
+    if scan_name not in kern:
+        scan_name = next(n for n in kern if n.startswith("index_scan"))
+    sb, sf, pairs = scan_work(wl)
+    scan_ms = kern[scan_name]["avg_ms"]
+    stages = {k: dict(v) for k, v in kern.items()}
+    if wl.kind == "prefill":
+        achieved = sf / (scan_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": scan_name, "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                "flops_per_launch": sf}
+    else:
+        achieved = sb / (scan_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": scan_name, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(scan_name, TAGS[args.config]),
+                "bytes_per_launch": sb}
+    attn_ms = sum(v["avg_ms"] * launches_per_step[k] for k, v in kern.items() if k.startswith("attn_"))
+    n_attn = 5 if wl.kind == "hier" else 1
+    ab = attn_bytes(wl) * n_attn
+    stages["attention_total"] = {"ms_per_step": attn_ms, "algorithmic_bytes": ab,
+                                 "GB_per_s": ab / (attn_ms * 1e-3) / 1e9,
+                                 "frac_hbm": ab / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    prefill = wl.kind == "prefill"
+    units = wl.n_tokens if prefill else wl.B
+    value = units / (ms * 1e-3)
+    cfg = {"workload": wl.name}
+    if prefill:
+        cfg.update({"tokens": wl.n_tokens, "m": wl.m, "entries": wl.n_tokens // wl.m})
+    else:
+        cfg.update({"batch_queries": wl.B, "context_entries": wl.L, "m": wl.m})
+    cfg.update({"indexer": f"{wl.H_I}x{wl.d_I}", "top_k": wl.k, "window": wl.window, "heads": wl.H,
+                "head_dim": wl.c, "kv_cache": "fp4+e4m3" if wl.kind == "decode_fp4" else "bf16",
+                "indexer_k": "mxfp4" if wl.kind == "decode_fp4" else "bf16"})
+    if wl.kind == "hier":
+        cfg["layers"] = "Full (scan, top-512, block max) + pool (2048 blocks) + Reindex + 3 Reuse"
     res = {
         "metric": METRIC,
         "value": value,
-        "unit": "queries/s",
+        "unit": "tokens/s" if prefill else "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -278,17 +313,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded on-device generator; random-init, no trained weights)",
-        "config": {"workload": wl.name, "batch_queries": wl.B, "context_entries": wl.L, "m": wl.m,
-                   "indexer": f"{wl.H_I}x{wl.d_I}", "top_k": wl.k, "window": wl.window,
-                   "heads": wl.H, "head_dim": wl.c, "kv_cache": "fp4+e4m3" if fp4 else "bf16",
-                   "indexer_k": "mxfp4" if fp4 else "bf16"},
-        "scores_per_s": wl.B * wl.L / (scan_ms * 1e-3),
-        "roofline": {"bound": "hbm", "kernel": scan_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "config": cfg,
+        "scores_per_s": pairs / (scan_ms * 1e-3),
+        "roofline": roof,
         "stages": stages,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(torch, wl, insts[0], args.cpu_seconds, fp4=fp4)
+        d0 = insts[0]
+        if prefill:  # the oracle's own write path for the sampled tokens' entries and K_I
+            sys.path.insert(0, ROOT)
+            import oracle as O
+
+            e, k = O.compress(_h(d0["ca"][0]), _h(d0["za"][0]), wl.m, rope_dims=wl.rope_dims, w_ik=_h(d0["w_ik"]))
+            d0 = dict(d0, e_oracle=e, k_oracle=torch.from_numpy(np.clip(np.rint(2 * k), -3, 3)))
+        res["cpu_baseline"] = cpu_baseline(wl, d0, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

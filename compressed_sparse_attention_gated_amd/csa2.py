@@ -213,6 +213,13 @@ def csa2_hier_candidates(block_max, q_pos, N, *, m=1, block=8, n_keep=2048, out_
     return out_cand, out_count
 
 
+def csa2_hier_workspace_bytes(block_max, q_pos, N, *, m=1, block=8, n_keep=2048):
+    B, T = q_pos.shape
+    d = HierDesc(B=B, T=T, N=N, m=m, block=block, n_keep=n_keep, q_pos=_p(q_pos), block_max=_p(block_max),
+                 out_cand=None, out_count=None)
+    return lib().csa2_hier_workspace_bytes(C.byref(d))
+
+
 # ---------------------------------------------------------------------------- attention
 def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
                win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0, eps=1e-6,

@@ -1,0 +1,151 @@
+"""The libcsa2 call chains that make up one step of each workload.
+
+Nothing here computes: each class allocates its outputs and workspaces once, then
+`run(inputs)` enqueues the library calls of one step on the current stream.
+
+  DecodeStep   compress the new token into the window -> index FULL + top-k over every
+               cached entry -> sparse attention (bf16 or FP4 main KV, bf16 or MXFP4 K_I).
+  HierStep     the decoder group: Full layer (scan, top-k, block max, attention) ->
+               candidate pool -> Reindex layer (rescore candidates, top-k, attention) ->
+               three Reuse layers (same indices, own query / window / sink).
+  PrefillStep  compress a sequence (m = 2, with the indexer-K projection) and its window
+               rows (m = 1) -> causal index FULL + top-k per token -> sparse attention.
+
+The layer structure follows [CSA2 column] (modes table, hierarchical indexer) and
+[Evolution blog] §4.2-§4.4.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import csa2 as C
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+class DecodeStep:
+    def __init__(self, wl, d):
+        self.wl = wl
+        self.fp4 = wl.kind == "decode_fp4"
+        dev = d["q"].device
+        B = wl.B
+        self.idx = torch.empty((B, 1, wl.k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, 1, wl.H, wl.c), dtype=torch.bfloat16, device=dev)
+        self.ws_index = _ws(C.csa2_index_workspace_bytes(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"],
+                                                         w=d["w"], m=wl.m, out_idx=self.idx, **self._kidx(d)), dev)
+        self.ws_attn = _ws(C.csa2_attn_workspace_bytes(d["q"], d["q_pos"], self.idx, win=d["win"],
+                                                       win_pos0=d["win_pos0"], n_win=wl.window, sink=d["sink"],
+                                                       rope_dims=wl.rope_dims, out=self.out, **self._kv(d)), dev)
+
+    def _kidx(self, d):
+        return dict(k_codes=d["k_codes"], k_scales=d["k_scales"]) if self.fp4 else dict(k_idx=d["k_idx"])
+
+    def _kv(self, d):
+        return dict(kv_codes=d["kv_codes"], kv_scales=d["kv_scales"]) if self.fp4 else dict(kv=d["kv"])
+
+    def run(self, d):
+        wl = self.wl
+        win = d["win"]
+        # the new token's row (m = 1: RMSNorm + RoPE at position L) into the window's last slot
+        C.csa2_compress(d["c_new"], d["z_new"], 1, pos0=d["q_pos"][:, 0], rope_dims=wl.rope_dims,
+                        out=win[:, wl.window - 1:, :])
+        C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"], w=d["w"], m=wl.m,
+                          out_idx=self.idx, workspace=self.ws_index, **self._kidx(d))
+        C.csa2_sparse_attn(d["q"], d["q_pos"], self.idx, win=win, win_pos0=d["win_pos0"], n_win=wl.window,
+                           sink=d["sink"], rope_dims=wl.rope_dims, out=self.out, workspace=self.ws_attn,
+                           **self._kv(d))
+        return self.idx, self.out
+
+
+class HierStep:
+    def __init__(self, wl, d):
+        self.wl = wl
+        dev = d["kv"].device
+        B, L = wl.B, wl.L
+        nblk = -(-L // wl.block)
+        self.bmax = torch.empty((B, 1, nblk), dtype=torch.float32, device=dev)
+        self.idx_full = torch.empty((B, 1, wl.k), dtype=torch.int32, device=dev)
+        self.idx_re = torch.empty((B, 1, wl.k), dtype=torch.int32, device=dev)
+        self.cand = torch.empty((B, 1, wl.n_keep_blocks * wl.block), dtype=torch.int32, device=dev)
+        self.count = torch.empty((B, 1), dtype=torch.int32, device=dev)
+        self.outs = [torch.empty((B, 1, wl.H, wl.c), dtype=torch.bfloat16, device=dev) for _ in d["layers"]]
+        l0, l1 = d["layers"][0], d["layers"][1]
+        self.ws_full = _ws(C.csa2_index_workspace_bytes(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=l0["q_idx"],
+                                                        w=l0["w"], k_idx=d["k_idx"], out_idx=self.idx_full,
+                                                        out_block_max=self.bmax), dev)
+        self.ws_re = _ws(C.csa2_index_workspace_bytes(C.CSA2_MODE_REINDEX, d["q_pos"], wl.k, q_idx=l1["q_idx"],
+                                                      w=l1["w"], k_idx=d["k_idx"], cand=self.cand,
+                                                      n_cand=self.count, out_idx=self.idx_re), dev)
+        self.ws_attn = _ws(C.csa2_attn_workspace_bytes(l0["q"], d["q_pos"], self.idx_full, kv=d["kv"], win=l0["win"],
+                                                       win_pos0=d["win_pos0"], n_win=wl.window, sink=l0["sink"],
+                                                       rope_dims=wl.rope_dims, out=self.outs[0]), dev)
+        self.ws_hier = _ws(C.csa2_hier_workspace_bytes(self.bmax, d["q_pos"], L, block=wl.block,
+                                                       n_keep=wl.n_keep_blocks), dev)
+
+    def _attn(self, d, layer, idx):
+        e = d["layers"][layer]
+        wl = self.wl
+        C.csa2_sparse_attn(e["q"], d["q_pos"], idx, kv=d["kv"], win=e["win"], win_pos0=d["win_pos0"],
+                           n_win=wl.window, sink=e["sink"], rope_dims=wl.rope_dims, out=self.outs[layer],
+                           workspace=self.ws_attn)
+
+    def run(self, d):
+        wl = self.wl
+        l0, l1 = d["layers"][0], d["layers"][1]
+        # Full layer: scan every entry, its own top-k, block maxima for the pool
+        C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=l0["q_idx"], w=l0["w"], k_idx=d["k_idx"],
+                          out_idx=self.idx_full, out_block_max=self.bmax, block=wl.block, workspace=self.ws_full)
+        self._attn(d, 0, self.idx_full)
+        # candidate pool from the block maxima
+        C.csa2_hier_candidates(self.bmax, d["q_pos"], wl.L, block=wl.block, n_keep=wl.n_keep_blocks,
+                               out_cand=self.cand, out_count=self.count, workspace=self.ws_hier)
+        # Reindex layer: this layer's indexer over the candidates only
+        C.csa2_index_topk(C.CSA2_MODE_REINDEX, d["q_pos"], wl.k, q_idx=l1["q_idx"], w=l1["w"], k_idx=d["k_idx"],
+                          cand=self.cand, n_cand=self.count, out_idx=self.idx_re, workspace=self.ws_re)
+        self._attn(d, 1, self.idx_re)
+        # Reuse layers: the Reindex layer's indices, in place (no indexer work)
+        for layer in range(2, len(d["layers"])):
+            C.csa2_index_topk(C.CSA2_MODE_REUSE, d["q_pos"], wl.k, src_idx=self.idx_re, out_idx=self.idx_re)
+            self._attn(d, layer, self.idx_re)
+        return self.idx_full, self.cand, self.count, self.idx_re, self.outs
+
+
+class PrefillStep:
+    def __init__(self, wl, d):
+        self.wl = wl
+        dev = d["q"].device
+        n, c = wl.n_tokens, wl.c
+        ne = n // wl.m
+        self.entries = torch.empty((1, ne, c), dtype=torch.bfloat16, device=dev)
+        self.k_index = torch.empty((1, ne, wl.d_I), dtype=torch.bfloat16, device=dev)
+        self.win = torch.empty((1, n, c), dtype=torch.bfloat16, device=dev)
+        self.idx = torch.empty((1, n, wl.k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((1, n, wl.H, c), dtype=torch.bfloat16, device=dev)
+        self.ws_index = _ws(C.csa2_index_workspace_bytes(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"],
+                                                         w=d["w"], m=wl.m, k_idx=self.k_index,
+                                                         out_idx=self.idx), dev)
+        self.ws_attn = _ws(C.csa2_attn_workspace_bytes(d["q"], d["q_pos"], self.idx, kv=self.entries, win=self.win,
+                                                       win_pos0=self._wp0(dev), n_win=wl.window, sink=d["sink"],
+                                                       rope_dims=wl.rope_dims, out=self.out), dev)
+        self.wp0 = self._wp0(dev)
+
+    @staticmethod
+    def _wp0(dev):
+        return torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def run(self, d, k_idx=None):
+        """k_idx: the indexer K the index stage reads; default the compressor's projection."""
+        wl = self.wl
+        C.csa2_compress(d["ca"], d["za"], wl.m, rope_dims=wl.rope_dims, out=self.entries, w_ik=d["w_ik"],
+                        out_ik=self.k_index)
+        # window rows: every token's own row (m = 1 keeps the row; RMSNorm + RoPE at its position)
+        C.csa2_compress(d["win_src"], d["win_src"], 1, rope_dims=wl.rope_dims, out=self.win)
+        C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"], w=d["w"], m=wl.m,
+                          k_idx=self.k_index if k_idx is None else k_idx, out_idx=self.idx,
+                          workspace=self.ws_index)
+        C.csa2_sparse_attn(d["q"], d["q_pos"], self.idx, kv=self.entries, win=self.win, win_pos0=self.wp0,
+                           n_win=wl.window, sink=d["sink"], rope_dims=wl.rope_dims, out=self.out,
+                           workspace=self.ws_attn)
+        return self.entries, self.k_index, self.win, self.idx, self.out

@@ -223,3 +223,65 @@ def random_topk_lists(g, B, T, n_vis, k):
                 s = g.sorted_sample(int(nv[b, t]), kk)
                 out[b, t, :kk] = np.asarray(s.cpu() if hasattr(s, "cpu") else s)
     return out
+
+
+# ----------------------------------------------------------------- whole-step inputs
+def decode_inputs(wl, seed, device="cuda"):
+    """One instance of a decode workload (indexer + attention inputs, the new token's
+    compressor input, positions) for a step of `wl` (kind "decode" or "decode_fp4").
+    Every query sits at position t = L, so all L cached entries are visible."""
+    import torch
+
+    g = rng(seed, device=device)
+    B, L, c, H = wl.B, wl.L, wl.c, wl.H
+    fp4 = wl.kind == "decode_fp4"
+    d = dict(indexer_inputs(g, B, 1, L, wl.H_I, wl.d_I, wl.w_values, k_format="mxfp4" if fp4 else "bf16"))
+    d.update(attn_inputs(g, B, 1, L, H, c, Lw=wl.window, kv_format="fp4" if fp4 else "bf16"))
+    d["q_pos"] = torch.full((B, 1), L, dtype=torch.int32, device=device)
+    d["win_pos0"] = torch.full((B,), L - wl.window + 1, dtype=torch.int32, device=device)
+    d["c_new"] = g.normal((B, 1, c), dtype="bf16")
+    d["z_new"] = g.normal((B, 1, c), dtype="bf16")
+    return d
+
+
+def hier_inputs(wl, seed, device="cuda", n_layers=5):
+    """The hierarchical decoder group: one shared main KV and indexer K, then per layer
+    (Full, Reindex, Reuse x3) its own indexer query and weights (the first two layers),
+    attention query, 128-token window and sink.  Queries sit at t = L."""
+    import torch
+
+    g = rng(seed, device=device)
+    B, L, c, H = wl.B, wl.L, wl.c, wl.H
+    d = {"kv": g.normal((B, L, c), dtype="bf16"),
+         "k_idx": g.ints((B, L, wl.d_I), -3, 3, dtype="bf16")}
+    d["layers"] = []
+    for layer in range(n_layers):
+        e = {}
+        if layer < 2:
+            e["q_idx"] = g.ints((B, 1, wl.H_I, wl.d_I), -3, 3, dtype="bf16")
+            e["w"] = g.choice((B, 1, wl.H_I), wl.w_values, dtype="f32")
+        e["q"] = g.normal((B, 1, H, c), dtype="bf16")
+        e["win"] = g.normal((B, wl.window, c), dtype="bf16")
+        e["sink"] = g.normal((H,), dtype="f32")
+        d["layers"].append(e)
+    d["q_pos"] = torch.full((B, 1), L, dtype=torch.int32, device=device)
+    d["win_pos0"] = torch.full((B,), L - wl.window + 1, dtype=torch.int32, device=device)
+    return d
+
+
+def prefill_inputs(wl, seed, device="cuda"):
+    """One prefill sequence: compressor input C, Z [1, n, c] ~ N(0,1), W_IK ~ N(0, 1/c),
+    the per-token window source [1, n, c] ~ N(0,1), indexer queries (integers) and head
+    weights, attention queries ~ N(0,1) and sink ~ N(0,1); query t sits at position t."""
+    import torch
+
+    g = rng(seed, device=device)
+    n, c, H = wl.n_tokens, wl.c, wl.H
+    d = compress_inputs(g, n, c, wl.m, dtype="bf16", d_I=wl.d_I)
+    d["win_src"] = g.normal((1, n, c), dtype="bf16")
+    d["q_idx"] = g.ints((1, n, wl.H_I, wl.d_I), -3, 3, dtype="bf16")
+    d["w"] = g.choice((1, n, wl.H_I), wl.w_values, dtype="f32")
+    d["q"] = g.normal((1, n, H, c), dtype="bf16")
+    d["sink"] = g.normal((H,), dtype="f32")
+    d["q_pos"] = torch.arange(n, dtype=torch.int32, device=device)[None]
+    return d
