@@ -11,7 +11,7 @@
 // entry column, so the ReLU, the signed head weight and the head sum are an in-lane
 // epilogue plus one swap between the two half-waves.  No LDS: every K_I byte is read
 // exactly once per query.  MXFP4 rows (E2M1 codes + E8M0 scale per 32) are dequantised
-// into the B registers (exact in bf16).
+// into the B registers by the hardware's scaled FP4 convert (exact in bf16).
 //
 // Two variants:
 //  * scan_private: one query per workgroup slice; the 4 waves split the entry range.
@@ -56,38 +56,68 @@ __device__ __forceinline__ int dim_of(int ks, int h) {
   return KF == 0 ? 16 * ks + 8 * h : (DI / 2) * h + 8 * ks;
 }
 
-// B operand of one 32-entry tile: KS = DI/16 registers of 8 bf16
+// B operand of one 32-entry tile, as loaded from HBM.  The loads of a tile are issued
+// well before the tile is used; conversion to the MFMA operand (to_b) happens at use, so
+// nothing waits on a load early.
 template <int DI, int KF>
-__device__ __forceinline__ void load_b(const Dev& a, int b, int ent, int h, bf16x8* breg) {
-  constexpr int KS = DI / 16;
+struct RawB;
+template <int DI>
+struct RawB<DI, 0> {
+  bf16x8 v[DI / 16];
+};
+template <int DI>
+struct RawB<DI, 1> {
+  uint32_t c[DI / 16];  // this lane's DI/4 code bytes: 8 E2M1 codes per word, low nibble first
+  uint32_t s;           // the entry's DI/32 E8M0 scale bytes
+};
+
+template <int DI, int KF>
+__device__ __forceinline__ void load_raw(const Dev& a, int b, int ent, int h, RawB<DI, KF>& r) {
   if constexpr (KF == 0) {
     const uint4* p = reinterpret_cast<const uint4*>(a.k_idx + ((size_t)b * a.N + ent) * DI + 8 * h);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) breg[ks] = as_bf16x8(p[2 * ks]);
+    for (int ks = 0; ks < DI / 16; ++ks) r.v[ks] = as_bf16x8(p[2 * ks]);
   } else {
-    // codes: DI/4 bytes at (DI/4)*h; scales: groups of 32 dims
+    // codes: DI/4 bytes at (DI/4)*h of the entry's DI/2 code bytes
     const uint8_t* cp = a.k_codes + ((size_t)b * a.N + ent) * (DI / 2) + (DI / 4) * h;
     const uint8_t* sp = a.k_scales + ((size_t)b * a.N + ent) * (DI / 32);
-    uint32_t codes[DI / 16];
     if constexpr (DI / 4 >= 16) {
 #pragma unroll
       for (int q = 0; q < DI / 64; ++q) {
-        uint4 v = reinterpret_cast<const uint4*>(cp)[q];
-        codes[4 * q] = v.x; codes[4 * q + 1] = v.y; codes[4 * q + 2] = v.z; codes[4 * q + 3] = v.w;
+        const uint4 v = reinterpret_cast<const uint4*>(cp)[q];
+        r.c[4 * q] = v.x; r.c[4 * q + 1] = v.y; r.c[4 * q + 2] = v.z; r.c[4 * q + 3] = v.w;
       }
     } else {
       const uint2 v = *reinterpret_cast<const uint2*>(cp);
-      codes[0] = v.x; codes[1] = v.y;
+      r.c[0] = v.x; r.c[1] = v.y;
     }
+    if constexpr (DI == 128) r.s = *reinterpret_cast<const uint32_t*>(sp);
+    else if constexpr (DI == 64) r.s = *reinterpret_cast<const uint16_t*>(sp);
+    else r.s = *sp;
+  }
+}
+
+// MFMA B registers of a loaded tile.  MXFP4: the hardware's scaled FP4 -> bf16 convert
+// takes the power of two 2^(e-127) as an fp32 whose exponent field is e (an E8M0 byte is
+// exactly that exponent field), two codes per instruction; E2M1 x 2^k is exact in bf16.
+template <int DI, int KF>
+__device__ __forceinline__ void to_b(const RawB<DI, KF>& r, int h, bf16x8* breg) {
+  if constexpr (KF == 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = dim_of<DI, KF>(ks, h);
-      const float sc = e8m0_to_f32(sp[d0 / 32]);
-      const uint32_t cw = codes[ks];
-      float f[8];
+    for (int ks = 0; ks < DI / 16; ++ks) breg[ks] = r.v[ks];
+  } else {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((cw >> (4 * e)) & 15u) * sc;
-      breg[ks] = as_bf16x8(pack8(f));  // exact: E2M1 x 2^k is a bf16 number
+    for (int ks = 0; ks < DI / 16; ++ks) {
+      const int g = dim_of<DI, KF>(ks, h) / 32;
+      const float sc = __builtin_bit_cast(float, ((r.s >> (8 * g)) & 0xffu) << 23);
+      const uint32_t cw = r.c[ks];
+      uint4 v;
+      v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0));
+      v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1));
+      v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2));
+      v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
+      breg[ks] = as_bf16x8(v);
     }
   }
 }
@@ -189,11 +219,13 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
   constexpr int kStride = 32 * kWaves;
   const int t0 = c0 + 32 * wave;
   if (t0 >= c1) return;
-  bf16x8 b0[DI / 16], b1[DI / 16], b2[DI / 16];
-  load_b<DI, KF>(a, b, entry_of(t0 + lane % 32), h, b0);
-  load_b<DI, KF>(a, b, entry_of(t0 + kStride + lane % 32), h, b1);
-  auto consume = [&](const bf16x8* bb, int tb) {
-    float s = tile_score<DI, MT>(areg, bb, wreg);
+  RawB<DI, KF> b0, b1, b2;
+  load_raw<DI, KF>(a, b, entry_of(t0 + lane % 32), h, b0);
+  load_raw<DI, KF>(a, b, entry_of(t0 + kStride + lane % 32), h, b1);
+  auto consume = [&](const RawB<DI, KF>& raw, int tb) {
+    bf16x8 breg[DI / 16];
+    to_b<DI, KF>(raw, h, breg);
+    float s = tile_score<DI, MT>(areg, breg, wreg);
     if constexpr (kCand) {
       const int slot = tb + lane % 32;
       if (slot < c1) {
@@ -204,13 +236,13 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
     emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
   };
   for (int tb = t0; tb < c1; tb += 3 * kStride) {
-    load_b<DI, KF>(a, b, entry_of(tb + 2 * kStride + lane % 32), h, b2);
+    load_raw<DI, KF>(a, b, entry_of(tb + 2 * kStride + lane % 32), h, b2);
     consume(b0, tb);
     if (tb + kStride >= c1) break;
-    load_b<DI, KF>(a, b, entry_of(tb + 3 * kStride + lane % 32), h, b0);
+    load_raw<DI, KF>(a, b, entry_of(tb + 3 * kStride + lane % 32), h, b0);
     consume(b1, tb + kStride);
     if (tb + 2 * kStride >= c1) break;
-    load_b<DI, KF>(a, b, entry_of(tb + 4 * kStride + lane % 32), h, b1);
+    load_raw<DI, KF>(a, b, entry_of(tb + 4 * kStride + lane % 32), h, b1);
     consume(b2, tb + 2 * kStride);
   }
 }
@@ -249,11 +281,13 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
   const int t0 = c0 + 32 * wave;
   if (t0 < c1) {
     auto ent = [&](int slot) { return min(slot, c1 - 1); };
-    bf16x8 b0[DI / 16], b1[DI / 16], b2[DI / 16];
-    load_b<DI, KF>(a, b, ent(t0 + lane % 32), h, b0);
-    load_b<DI, KF>(a, b, ent(t0 + kStride + lane % 32), h, b1);
-    auto consume = [&](const bf16x8* bb, int tb) {
-      const float s = tile_score<DI, MT>(areg, bb, wreg);
+    RawB<DI, KF> b0, b1, b2;
+    load_raw<DI, KF>(a, b, ent(t0 + lane % 32), h, b0);
+    load_raw<DI, KF>(a, b, ent(t0 + kStride + lane % 32), h, b1);
+    auto consume = [&](const RawB<DI, KF>& raw, int tb) {
+      bf16x8 breg[DI / 16];
+      to_b<DI, KF>(raw, h, breg);
+      const float s = tile_score<DI, MT>(areg, breg, wreg);
       const int slot = tb + lane % 32;
       if (lane < 32 && slot < c1) skeys[slot - c0] = float_key(s);
       if constexpr (kScores) {
@@ -262,13 +296,13 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
       if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, c1, s);
     };
     for (int tb = t0; tb < c1; tb += 3 * kStride) {
-      load_b<DI, KF>(a, b, ent(tb + 2 * kStride + lane % 32), h, b2);
+      load_raw<DI, KF>(a, b, ent(tb + 2 * kStride + lane % 32), h, b2);
       consume(b0, tb);
       if (tb + kStride >= c1) break;
-      load_b<DI, KF>(a, b, ent(tb + 3 * kStride + lane % 32), h, b0);
+      load_raw<DI, KF>(a, b, ent(tb + 3 * kStride + lane % 32), h, b0);
       consume(b1, tb + kStride);
       if (tb + 2 * kStride >= c1) break;
-      load_b<DI, KF>(a, b, ent(tb + 4 * kStride + lane % 32), h, b1);
+      load_raw<DI, KF>(a, b, ent(tb + 4 * kStride + lane % 32), h, b1);
       consume(b2, tb + 2 * kStride);
     }
   }
@@ -327,8 +361,10 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
 
   constexpr int kChunks = kShTile * kCPR;
   constexpr int kPerThread = (kChunks + kShThreads - 1) / kShThreads;
-  uint4 pre[kPerThread];
-  // global -> registers for the stage starting at `base`
+  // global -> registers for the stage starting at `base` (MXFP4: raw codes and scale,
+  // converted when committed to LDS, so the loads stay in flight meanwhile)
+  uint4 pre[KF == 0 ? kPerThread : 1];
+  uint32_t pre_c[KF == 1 ? kPerThread : 1], pre_s[KF == 1 ? kPerThread : 1];
   auto fetch = [&](int base) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
@@ -339,14 +375,9 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
         if constexpr (KF == 0) {
           pre[i] = reinterpret_cast<const uint4*>(a.k_idx + ((size_t)b * a.N + ent) * DI)[part];
         } else {
-          // dims 8*part .. 8*part+7 in natural order, dequantised (exact in bf16)
-          const uint8_t* cp = a.k_codes + ((size_t)b * a.N + ent) * (DI / 2) + 4 * part;
-          const float sc = e8m0_to_f32(a.k_scales[((size_t)b * a.N + ent) * (DI / 32) + (8 * part) / 32]);
-          const uint32_t cw = *reinterpret_cast<const uint32_t*>(cp);
-          float f[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) f[k] = e2m1_to_f32((cw >> (4 * k)) & 15u) * sc;
-          pre[i] = pack8(f);
+          // dims 8*part .. 8*part+7 in natural order
+          pre_c[i] = *reinterpret_cast<const uint32_t*>(a.k_codes + ((size_t)b * a.N + ent) * (DI / 2) + 4 * part);
+          pre_s[i] = a.k_scales[((size_t)b * a.N + ent) * (DI / 32) + (8 * part) / 32];
         }
       }
     }
@@ -357,7 +388,18 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
       const int q = threadIdx.x + i * kShThreads;
       if (q < kChunks) {
         const int e = q / kCPR, part = q % kCPR;
-        tile[st][e * kCPR + (part ^ (e & (kCPR - 1)))] = pre[i];
+        uint4 v;
+        if constexpr (KF == 0) {
+          v = pre[i];
+        } else {
+          // E2M1 x 2^(e-127) by the hardware's scaled convert (exact in bf16)
+          const float sc = __builtin_bit_cast(float, pre_s[i] << 23);
+          v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pre_c[i], sc, 0));
+          v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pre_c[i], sc, 1));
+          v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pre_c[i], sc, 2));
+          v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pre_c[i], sc, 3));
+        }
+        tile[st][e * kCPR + (part ^ (e & (kCPR - 1)))] = v;
       }
     }
   };
