@@ -196,7 +196,8 @@ static size_t index_ws(const csa2_index_desc* d, csa2_mode mode) {
   if (use_fused(d, mode)) {
     const int chunk = scan_select_chunk(d->N, d->k);
     const size_t nchunks = (size_t)(d->N + chunk - 1) / chunk;
-    return align256(rows * nchunks * d->k * sizeof(uint32_t)) + align256(rows * nchunks * d->k * sizeof(int32_t));
+    return align256(rows * nchunks * d->k * sizeof(uint32_t)) + align256(rows * nchunks * d->k * sizeof(int32_t)) +
+           align256(rows * nchunks * sizeof(uint2));
   }
   const int len = mode == CSA2_MODE_FULL ? d->N : d->cand_stride;
   size_t bytes = 0;
@@ -228,6 +229,7 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
     const int nchunks = (d->N + chunk - 1) / chunk;
     uint32_t* keys = (uint32_t*)ws;
     int32_t* slots = (int32_t*)((char*)ws + align256((size_t)rows * nchunks * d->k * sizeof(uint32_t)));
+    uint2* bounds = (uint2*)((char*)slots + align256((size_t)rows * nchunks * d->k * sizeof(int32_t)));
     ScanArgs a{};
     a.B = d->B; a.T = d->T; a.H_I = d->H_I; a.d_I = d->d_I; a.N = d->N; a.m = d->m;
     a.block = d->block > 0 ? d->block : 1;
@@ -236,12 +238,12 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
     a.scores = d->out_scores; a.row_stride = d->N;
     a.block_max = d->out_block_max;
     a.nblk = (d->N + a.block - 1) / a.block;
-    hipError_t e = launch_index_scan_select(a, d->k, chunk, nchunks, keys, slots, s);
+    hipError_t e = launch_index_scan_select(a, d->k, chunk, nchunks, keys, slots, bounds, s);
     if (e != hipSuccess) return hip_status(e, "index/scan_select");
     TopkArgs t{};
     t.rows = (int)rows; t.k = d->k; t.q_pos = d->q_pos; t.N = d->N; t.m = d->m; t.len_div = 1;
     t.out_idx = d->out_idx; t.max_len = d->N;
-    return hip_status(launch_topk_merge(t, nchunks, keys, slots, s), "index/topk_merge");
+    return hip_status(launch_topk_merge(t, nchunks, keys, slots, bounds, s), "index/topk_merge");
   }
   const int len = mode == CSA2_MODE_FULL ? d->N : d->cand_stride;
   char* wp = (char*)ws;

@@ -255,7 +255,7 @@ constexpr int kSelThreads = 256;
 
 template <int DI, int KF, int MT, bool kBlockMax, bool kScores>
 __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int k, int nchunks,
-                                                           uint32_t* wkeys, int32_t* wslot) {
+                                                           uint32_t* wkeys, int32_t* wslot, uint2* wbound) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TopkSmem<kSelThreads>& sm = *reinterpret_cast<TopkSmem<kSelThreads>*>(smem_raw);
   uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15));
@@ -268,8 +268,10 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
   const int len = c1 - c0;
   uint32_t* ok = wkeys + ((size_t)row * nchunks + c) * k;
   int32_t* os = wslot + ((size_t)row * nchunks + c) * k;
+  uint2* ob = wbound + (size_t)row * nchunks + c;
   if (len <= 0) {  // uniform: nothing visible in this chunk
     for (int i = threadIdx.x; i < k; i += kSelThreads) { ok[i] = 0u; os[i] = -1; }
+    if (threadIdx.x == 0) *ob = make_uint2(0u, 0u);
     return;
   }
   bf16x8 areg[MT][DI / 16];
@@ -312,11 +314,15 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
       ok[i] = i < len ? skeys[i] : 0u;
       os[i] = i < len ? c0 + i : -1;
     }
+    if (threadIdx.x == 0) *ob = make_uint2(0u, (uint32_t)len);  // every key >= 0
     return;
   }
   const KeysLds src{skeys};
-  uint32_t T, take;
-  radix_threshold<kSelThreads>(src, len, k, sm, &T, &take);
+  uint32_t T, take, L2, g2;
+  // pruning bound for the merge, from the first radix pass
+  const int k2 = bound_rank(k, nchunks);
+  radix_threshold<kSelThreads>(src, len, k, sm, &T, &take, k2, &L2, &g2);
+  if (threadIdx.x == 0) *ob = make_uint2(L2, g2);
   ordered_compact<kSelThreads>(src, len, k, T, take, sm, [&](uint32_t pos, int i, uint32_t key) {
     ok[pos] = key;
     os[pos] = c0 + i;
@@ -475,7 +481,7 @@ hipError_t launch1(const ScanArgs& s, const Dev& d, hipStream_t st) {
 
 template <int DI, int KF, int MT>
 hipError_t launch_sel3(const ScanArgs& s, const Dev& d, int k, int chunk, int nchunks, uint32_t* keys,
-                       int32_t* slots, hipStream_t st) {
+                       int32_t* slots, uint2* bounds, hipStream_t st) {
   const size_t lds = ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15) + (size_t)chunk * 4;
   dim3 grid(s.B * s.T, nchunks);
   const bool bm = s.block_max != nullptr, sc = s.scores != nullptr;
@@ -485,10 +491,10 @@ hipError_t launch_sel3(const ScanArgs& s, const Dev& d, int k, int chunk, int nc
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (bm && sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
-  else if (bm) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
-  else if (sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, false, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
-  else hipLaunchKernelGGL((scan_select<DI, KF, MT, false, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots);
+  if (bm && sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  else if (bm) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  else if (sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, false, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  else hipLaunchKernelGGL((scan_select<DI, KF, MT, false, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
   return hipGetLastError();
 }
 
@@ -513,17 +519,17 @@ int scan_select_chunk(int N, int k) {
 }
 
 hipError_t launch_index_scan_select(const ScanArgs& s, int k, int chunk, int nchunks, uint32_t* keys,
-                                    int32_t* slots, hipStream_t st) {
+                                    int32_t* slots, uint2* bounds, hipStream_t st) {
   if (s.B * s.T == 0) return hipSuccess;
-  if (!s.q_idx || !s.w || !s.q_pos || !keys || !slots || s.cand || (s.N > 0 && s.k_dtype == CSA2_BF16 && !s.k_idx) ||
+  if (!s.q_idx || !s.w || !s.q_pos || !keys || !slots || !bounds || s.cand || (s.N > 0 && s.k_dtype == CSA2_BF16 && !s.k_idx) ||
       (s.N > 0 && s.k_dtype == CSA2_MXFP4 && (!s.k_codes || !s.k_scales)) || chunk % 128 != 0 || k < 1)
     return hipErrorInvalidValue;
   const Dev d = make_dev(s);
   ScopedProf p(st, "index_scan_select");
   auto go = [&](auto di, auto kf) -> hipError_t {
     constexpr int DI = decltype(di)::value, KF = decltype(kf)::value;
-    return s.H_I <= 32 ? launch_sel3<DI, KF, 1>(s, d, k, chunk, nchunks, keys, slots, st)
-                       : launch_sel3<DI, KF, 2>(s, d, k, chunk, nchunks, keys, slots, st);
+    return s.H_I <= 32 ? launch_sel3<DI, KF, 1>(s, d, k, chunk, nchunks, keys, slots, bounds, st)
+                       : launch_sel3<DI, KF, 2>(s, d, k, chunk, nchunks, keys, slots, bounds, st);
   };
   const bool mx = s.k_dtype == CSA2_MXFP4;
   switch (s.d_I) {

@@ -63,15 +63,17 @@ struct TopkArgs {
 size_t topk_workspace_bytes(int rows, int k, int max_len);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
-// second level only: rows of nchunks*k (key, slot) pairs already written by a first level
-hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int32_t* slots, hipStream_t s);
+// second level only: rows of nchunks*k (key, slot) pairs already written by a first level,
+// with one (bound, count) pair per chunk: `count` keys of the chunk are >= `bound`
+hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int32_t* slots, uint2* bounds,
+                             hipStream_t s);
 
 // fused decode scan + chunk-local top-k (FULL mode, one query per sequence): the scan
 // writes (key, slot) pairs of each chunk's top-k; topk_merge finishes.  Returns the chunk
 // size used through *chunk_out and the number of chunks through *nchunks_out.
 int scan_select_chunk(int N, int k);
 hipError_t launch_index_scan_select(const ScanArgs& a, int k, int chunk, int nchunks, uint32_t* keys,
-                                    int32_t* slots, hipStream_t s);
+                                    int32_t* slots, uint2* bounds, hipStream_t s);
 
 // expand selected blocks (ascending, -1 padded) into candidate positions
 hipError_t launch_hier_expand(int rows, int n_keep, int block, const int32_t* sel_blocks,

@@ -24,6 +24,8 @@ namespace {
 constexpr int kThreads = 256;       // single rows and chunks
 constexpr int kMergeThreads = 1024; // merge rows (few workgroups, long rows)
 constexpr int kSingleMax = 32768;
+constexpr size_t kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kWideBelow = 256;          // fewer workgroups than this: 1024 threads each
 
 struct Params {
   int rows, k;
@@ -41,7 +43,10 @@ struct Params {
   int chunk, nchunks;
   uint32_t* ws_keys;  // [rows, nchunks*k]
   int32_t* ws_slot;   // [rows, nchunks*k]
+  uint2* ws_bound;    // [rows, nchunks]: (bound, count) - count keys of the chunk are >= bound
 };
+
+
 
 __device__ __forceinline__ int row_len(const Params& p, int r) {
   int len;
@@ -80,79 +85,112 @@ __device__ __forceinline__ void stage_keys(const float* scores, int n, int force
   __syncthreads();
 }
 
+// Selected positions are first collected in LDS (sel[pos] = i) and mapped / written after
+// one barrier, so the id map (Reindex) is read with all loads in flight at once.  Used
+// when k <= kDeferMax and the LDS has room; otherwise each selection is written directly.
+constexpr int kDeferMax = 4096;
+
+__host__ __device__ __forceinline__ size_t smem_keys_off(size_t smem_bytes) { return (smem_bytes + 15) & ~(size_t)15; }
+
 // single level: one workgroup per row
-__global__ void __launch_bounds__(kThreads) topk_single(Params p, int stage_cap) {
+template <int kT>
+__global__ void __launch_bounds__(kT) topk_single(Params p, int stage_cap, int defer) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  TopkSmem<kThreads>& sm = *reinterpret_cast<TopkSmem<kThreads>*>(smem_raw);
-  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + ((sizeof(TopkSmem<kThreads>) + 15) & ~(size_t)15));
+  TopkSmem<kT>& sm = *reinterpret_cast<TopkSmem<kT>*>(smem_raw);
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + smem_keys_off(sizeof(TopkSmem<kT>)));
+  int32_t* sel = reinterpret_cast<int32_t*>(skeys + ((stage_cap + 3) & ~3));
   const int r = blockIdx.x;
   const int n = row_len(p, r);
   int32_t* out = p.out_idx + (size_t)r * p.k;
   if (n <= p.k) {
-    for (int i = threadIdx.x; i < p.k; i += kThreads) out[i] = i < n ? map_id(p, r, i) : -1;
+    for (int i = threadIdx.x; i < p.k; i += kT) out[i] = i < n ? map_id(p, r, i) : -1;
     return;
   }
   const float* row = p.scores + (size_t)r * p.row_stride;
   const int force = p.force_last ? n - 1 : -1;
   uint32_t T, take;
-  auto emit = [&](uint32_t pos, int i, uint32_t) { out[pos] = map_id(p, r, i); };
+  auto direct = [&](uint32_t pos, int i, uint32_t) { out[pos] = map_id(p, r, i); };
+  auto deferred = [&](uint32_t pos, int i, uint32_t) { sel[pos] = i; };
   if (n <= stage_cap) {
-    stage_keys<kThreads>(row, n, force, skeys);
+    stage_keys<kT>(row, n, force, skeys);
     const KeysLds src{skeys};
-    radix_threshold<kThreads>(src, n, p.k, sm, &T, &take);
-    ordered_compact<kThreads>(src, n, p.k, T, take, sm, emit);
+    radix_threshold<kT>(src, n, p.k, sm, &T, &take);
+    if (defer) ordered_compact<kT>(src, n, p.k, T, take, sm, deferred);
+    else ordered_compact<kT>(src, n, p.k, T, take, sm, direct);
   } else {
     const KeysScores src{row, force};
-    radix_threshold<kThreads>(src, n, p.k, sm, &T, &take);
-    ordered_compact<kThreads>(src, n, p.k, T, take, sm, emit);
+    radix_threshold<kT>(src, n, p.k, sm, &T, &take);
+    if (defer) ordered_compact<kT>(src, n, p.k, T, take, sm, deferred);
+    else ordered_compact<kT>(src, n, p.k, T, take, sm, direct);
+  }
+  if (defer) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < p.k; q += kT) out[q] = map_id(p, r, sel[q]);
   }
 }
 
 // two-level, first level: grid (rows, nchunks); chunk c of row r -> ws[r][c*k .. c*k+k)
-__global__ void __launch_bounds__(kThreads) topk_chunk(Params p, int stage_cap) {
+template <int kT>
+__global__ void __launch_bounds__(kT) topk_chunk(Params p, int stage_cap) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  TopkSmem<kThreads>& sm = *reinterpret_cast<TopkSmem<kThreads>*>(smem_raw);
-  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + ((sizeof(TopkSmem<kThreads>) + 15) & ~(size_t)15));
+  TopkSmem<kT>& sm = *reinterpret_cast<TopkSmem<kT>*>(smem_raw);
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + smem_keys_off(sizeof(TopkSmem<kT>)));
   const int r = blockIdx.x, c = blockIdx.y;
   const int n = row_len(p, r);
   const int c0 = c * p.chunk;
   const int len = max(0, min(p.chunk, n - c0));
   uint32_t* ok = p.ws_keys + ((size_t)r * p.nchunks + c) * p.k;
   int32_t* os = p.ws_slot + ((size_t)r * p.nchunks + c) * p.k;
+  uint2* ob = p.ws_bound + (size_t)r * p.nchunks + c;
   const int force = (p.force_last && n > 0 && n - 1 >= c0 && n - 1 < c0 + p.chunk) ? (n - 1 - c0) : -1;
   const float* row = p.scores + (size_t)r * p.row_stride + c0;
   if (len <= p.k) {
     const KeysScores src{row, force};
-    for (int i = threadIdx.x; i < p.k; i += kThreads) {
+    for (int i = threadIdx.x; i < p.k; i += kT) {
       ok[i] = i < len ? src.key(i) : 0u;
       os[i] = i < len ? c0 + i : -1;
     }
+    if (threadIdx.x == 0) *ob = make_uint2(0u, (uint32_t)len);  // every key >= 0
     return;
   }
-  uint32_t T, take;
+  uint32_t T, take, L2, g2;
+  const int k2 = bound_rank(p.k, p.nchunks);
   auto emit = [&](uint32_t pos, int i, uint32_t key) {
     ok[pos] = key;
     os[pos] = c0 + i;
   };
   if (len <= stage_cap) {
-    stage_keys<kThreads>(row, len, force, skeys);
+    stage_keys<kT>(row, len, force, skeys);
     const KeysLds src{skeys};
-    radix_threshold<kThreads>(src, len, p.k, sm, &T, &take);
-    ordered_compact<kThreads>(src, len, p.k, T, take, sm, emit);
+    radix_threshold<kT>(src, len, p.k, sm, &T, &take, k2, &L2, &g2);
+    if (threadIdx.x == 0) *ob = make_uint2(L2, g2);
+    ordered_compact<kT>(src, len, p.k, T, take, sm, emit);
   } else {
     const KeysScores src{row, force};
-    radix_threshold<kThreads>(src, len, p.k, sm, &T, &take);
-    ordered_compact<kThreads>(src, len, p.k, T, take, sm, emit);
+    radix_threshold<kT>(src, len, p.k, sm, &T, &take, k2, &L2, &g2);
+    if (threadIdx.x == 0) *ob = make_uint2(L2, g2);
+    ordered_compact<kT>(src, len, p.k, T, take, sm, emit);
   }
 }
 
 // two-level, second level: one workgroup per row over nchunks*k (key, slot) pairs; key 0
-// marks padding (below every real key)
-__global__ void __launch_bounds__(kMergeThreads) topk_merge(Params p, int stage_cap) {
+// marks padding (below every real key).
+//
+// Pruned form (rows of at most kPruneMax pairs, chunk bounds present): the chunk bounds
+// give a key L with at least k candidates >= L, so L <= the row's k-th largest key and
+// every key below L can be dropped.  The survivors are gathered in index order into LDS,
+// and the selection runs over them alone.
+constexpr int kPruneMax = 16384;
+
+__global__ void __launch_bounds__(kMergeThreads) topk_merge(Params p, int stage_cap, int defer, int prune) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TopkSmem<kMergeThreads>& sm = *reinterpret_cast<TopkSmem<kMergeThreads>*>(smem_raw);
-  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + ((sizeof(TopkSmem<kMergeThreads>) + 15) & ~(size_t)15));
+  uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + smem_keys_off(sizeof(TopkSmem<kMergeThreads>)));
+  const int cap4 = (stage_cap + 3) & ~3;
+  int32_t* sidx = reinterpret_cast<int32_t*>(skeys + cap4);  // pruned form: survivor -> its slot
+  int32_t* sel = prune ? sidx + cap4 : reinterpret_cast<int32_t*>(skeys + cap4);
   const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = row_len(p, r);
   int32_t* out = p.out_idx + (size_t)r * p.k;
   const int32_t* slots = p.ws_slot + (size_t)r * p.nchunks * p.k;
@@ -163,12 +201,86 @@ __global__ void __launch_bounds__(kMergeThreads) topk_merge(Params p, int stage_
   const int m = p.nchunks * p.k;
   const uint32_t* gkeys = p.ws_keys + (size_t)r * m;
   uint32_t T, take;
-  auto emit = [&](uint32_t pos, int i, uint32_t) {
+  if (prune) {
+    // this thread's pairs [16t, 16t + 16): loads issued first, in flight during the bound
+    constexpr int kPer = kPruneMax / kMergeThreads;
+    const int i0 = kPer * threadIdx.x;
+    uint32_t kk[kPer];
+    int32_t ks[kPer];  // their slots
+    if ((m & 3) == 0) {
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        int4 w = make_int4(-1, -1, -1, -1);
+        if (i0 + 4 * q < m) {
+          v = reinterpret_cast<const uint4*>(gkeys + i0)[q];
+          w = reinterpret_cast<const int4*>(slots + i0)[q];
+        }
+        kk[4 * q] = v.x; kk[4 * q + 1] = v.y; kk[4 * q + 2] = v.z; kk[4 * q + 3] = v.w;
+        ks[4 * q] = w.x; ks[4 * q + 1] = w.y; ks[4 * q + 2] = w.z; ks[4 * q + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        kk[j] = i0 + j < m ? gkeys[i0 + j] : 0u;
+        ks[j] = i0 + j < m ? slots[i0 + j] : -1;
+      }
+    }
+    // L: the largest chunk bound such that the chunks with bounds >= it hold >= k keys at
+    // or above it.  The bounds are staged in LDS (the survivor arrays are free until the
+    // survivors are written, after a barrier below).
+    uint2* sb = reinterpret_cast<uint2*>(skeys);  // nchunks <= m <= the two arrays' 2*cap4 words / 2
+    const uint2* bd = p.ws_bound + (size_t)r * p.nchunks;
+    for (int c = threadIdx.x; c < p.nchunks; c += kMergeThreads) sb[c] = bd[c];
+    __syncthreads();
+    uint32_t best = 0;
+    for (int c = threadIdx.x; c < p.nchunks; c += kMergeThreads) {
+      const uint32_t lc = sb[c].x;
+      uint32_t held = 0;
+      for (int j = 0; j < p.nchunks; ++j) {
+        const uint2 b = sb[j];
+        if (b.x >= lc) held += b.y;
+      }
+      if (held >= (uint32_t)p.k) best = max(best, lc);
+    }
+    best = wave_umax(best);
+    if (lane == 0) sm.whi[wave] = best;
+    __syncthreads();
+    uint32_t L = 0;
+#pragma unroll
+    for (int w = 0; w < TopkSmem<kMergeThreads>::kW; ++w) L = max(L, sm.whi[w]);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cnt += (i0 + j < m && kk[j] >= L) ? 1u : 0u;
+    uint32_t ns;
+    uint32_t pos = block_excl_scan<kMergeThreads>(cnt, &ns, sm);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (i0 + j < m && kk[j] >= L) {
+        skeys[pos] = kk[j];
+        sidx[pos] = ks[j];
+        ++pos;
+      }
+    }
+    __syncthreads();
+    const KeysLds src{skeys};
+    radix_threshold<kMergeThreads>(src, (int)ns, p.k, sm, &T, &take);
+    ordered_compact<kMergeThreads>(src, (int)ns, p.k, T, take, sm,
+                                   [&](uint32_t q, int j, uint32_t) { sel[q] = sidx[j]; });
+    __syncthreads();
+    for (int q = threadIdx.x; q < p.k; q += kMergeThreads) {
+      const int sl = sel[q];
+      out[q] = sl >= 0 ? map_id(p, r, sl) : -1;
+    }
+    return;
+  }
+  auto direct = [&](uint32_t pos, int i, uint32_t) {
     const int sl = slots[i];
     out[pos] = sl >= 0 ? map_id(p, r, sl) : -1;
   };
+  auto deferred = [&](uint32_t pos, int i, uint32_t) { sel[pos] = i; };
   if (m <= stage_cap) {
-    if ((m & 3) == 0 && (((uintptr_t)gkeys) & 15u) == 0) {
+    if ((m & 3) == 0) {
       for (int i = threadIdx.x; i < m / 4; i += kMergeThreads)
         reinterpret_cast<uint4*>(skeys)[i] = reinterpret_cast<const uint4*>(gkeys)[i];
     } else {
@@ -177,35 +289,63 @@ __global__ void __launch_bounds__(kMergeThreads) topk_merge(Params p, int stage_
     __syncthreads();
     const KeysLds src{skeys};
     radix_threshold<kMergeThreads>(src, m, p.k, sm, &T, &take);
-    ordered_compact<kMergeThreads>(src, m, p.k, T, take, sm, emit);
+    if (defer) ordered_compact<kMergeThreads>(src, m, p.k, T, take, sm, deferred);
+    else ordered_compact<kMergeThreads>(src, m, p.k, T, take, sm, direct);
   } else {
-    const KeysLds src{gkeys};
+    const KeysGlobal src{gkeys};
     radix_threshold<kMergeThreads>(src, m, p.k, sm, &T, &take);
-    ordered_compact<kMergeThreads>(src, m, p.k, T, take, sm, emit);
+    if (defer) ordered_compact<kMergeThreads>(src, m, p.k, T, take, sm, deferred);
+    else ordered_compact<kMergeThreads>(src, m, p.k, T, take, sm, direct);
+  }
+  if (defer) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < p.k; q += kMergeThreads) {
+      const int sl = slots[sel[q]];
+      out[q] = sl >= 0 ? map_id(p, r, sl) : -1;
+    }
   }
 }
 
+// LDS of a merge launch and whether it takes the pruned form
+static size_t merge_lds(int m, int k, bool have_bounds, int* cap_out, int* defer_out, int* prune_out) {
+  const size_t base = smem_keys_off(sizeof(TopkSmem<kMergeThreads>));
+  const int cap = m < kStageMax ? m : kStageMax;
+  const size_t cap4 = (size_t)((cap + 3) & ~3);
+  const bool prune = have_bounds && m <= kPruneMax && base + 2 * cap4 * 4 + (size_t)k * 4 <= kLdsMax;
+  size_t lds;
+  int defer = 0;
+  if (prune) {
+    lds = base + 2 * cap4 * 4 + (size_t)k * 4;
+  } else {
+    lds = base + cap4 * 4;
+    defer = k <= kDeferMax && lds + (size_t)k * 4 <= kLdsMax;
+    if (defer) lds += (size_t)k * 4;
+  }
+  *cap_out = cap;
+  *defer_out = defer;
+  *prune_out = prune;
+  return lds;
+}
+
 // expand selected blocks (ascending, -1 padded, the latest visible block included) into
-// positions; one workgroup per row
-__global__ void __launch_bounds__(kThreads) hier_expand(int n_keep, int block, const int32_t* sel,
-                                                         const int32_t* q_pos, int N, int m,
-                                                         int32_t* cand, int32_t* count) {
+// positions; grid (rows, ceil(n_keep*block / 256)), one position per thread
+__global__ void __launch_bounds__(kThreads) hier_expand(int n_keep, int block, const int32_t* __restrict__ sel,
+                                                         const int32_t* __restrict__ q_pos, int N, int m,
+                                                         int32_t* __restrict__ cand, int32_t* __restrict__ count) {
   const int r = blockIdx.x;
   const int t = q_pos[r];
   int nv = t >= 0 ? t / m : 0;
   if (nv > N) nv = N;
-  const int32_t* s = sel + (size_t)r * n_keep;
-  int32_t* o = cand + (size_t)r * n_keep * block;
   const int total = n_keep * block;
-  for (int q = threadIdx.x; q < total; q += kThreads) {
-    const int bi = q / block, u = q % block;
-    const int blk = s[bi];
-    const int pos = blk >= 0 ? blk * block + u : -1;
+  const int q = blockIdx.y * kThreads + threadIdx.x;
+  if (q < total) {
+    const int blk = sel[(size_t)r * n_keep + q / block];
+    const int pos = blk >= 0 ? blk * block + q % block : -1;
     // only the latest (highest, last-listed) block can be partial; its tail maps to -1 and
     // sits at the end of the list, so the valid positions stay contiguous and ascending
-    o[q] = (pos >= 0 && pos < nv) ? pos : -1;
+    cand[(size_t)r * total + q] = (pos >= 0 && pos < nv) ? pos : -1;
   }
-  if (threadIdx.x == 0) {
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
     const int nb = (nv + block - 1) / block;
     const int kept = nb < n_keep ? nb : n_keep;
     count[r] = kept == 0 ? 0 : (kept - 1) * block + (nv - (nb - 1) * block);
@@ -231,7 +371,7 @@ size_t topk_workspace_bytes(int rows, int k, int max_len) {
   if (max_len <= kSingleMax) return 0;
   const int chunk = pick_chunk(max_len, k);
   const size_t nchunks = (size_t)(max_len + chunk - 1) / chunk;
-  return (size_t)rows * nchunks * k * (sizeof(uint32_t) + sizeof(int32_t));
+  return (size_t)rows * nchunks * k * (sizeof(uint32_t) + sizeof(int32_t)) + (size_t)rows * nchunks * sizeof(uint2);
 }
 
 static hipError_t set_lds(const void* fn, size_t bytes) {
@@ -254,51 +394,66 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   hipError_t e;
   if (a.max_len <= kSingleMax) {
     const int cap = a.max_len < kStageMax ? a.max_len : kStageMax;
-    const size_t lds = ((sizeof(TopkSmem<kThreads>) + 15) & ~(size_t)15) + (size_t)cap * 4;
-    if ((e = set_lds((const void*)topk_single, lds)) != hipSuccess) return e;
+    const bool wide = a.rows < kWideBelow;
+    size_t lds = smem_keys_off(wide ? sizeof(TopkSmem<kMergeThreads>) : sizeof(TopkSmem<kThreads>)) + (size_t)((cap + 3) & ~3) * 4;
+    const int defer = a.k <= kDeferMax && lds + (size_t)a.k * 4 <= kLdsMax;
+    if (defer) lds += (size_t)a.k * 4;
     ScopedProf pr(s, "topk_single");
-    hipLaunchKernelGGL(topk_single, dim3(a.rows), dim3(kThreads), lds, s, p, cap);
+    if (wide) {
+      if ((e = set_lds((const void*)topk_single<kMergeThreads>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(topk_single<kMergeThreads>, dim3(a.rows), dim3(kMergeThreads), lds, s, p, cap, defer);
+    } else {
+      if ((e = set_lds((const void*)topk_single<kThreads>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(topk_single<kThreads>, dim3(a.rows), dim3(kThreads), lds, s, p, cap, defer);
+    }
     return hipGetLastError();
   }
   p.chunk = pick_chunk(a.max_len, a.k);
   p.nchunks = (a.max_len + p.chunk - 1) / p.chunk;
   p.ws_keys = (uint32_t*)a.ws;
   p.ws_slot = (int32_t*)((char*)a.ws + (size_t)a.rows * p.nchunks * a.k * sizeof(uint32_t));
+  p.ws_bound = (uint2*)((char*)p.ws_slot + (size_t)a.rows * p.nchunks * a.k * sizeof(int32_t));
   {
     const int cap = p.chunk < kStageMax ? p.chunk : kStageMax;
-    const size_t lds = ((sizeof(TopkSmem<kThreads>) + 15) & ~(size_t)15) + (size_t)cap * 4;
-    if ((e = set_lds((const void*)topk_chunk, lds)) != hipSuccess) return e;
+    const bool wide = (long long)a.rows * p.nchunks < kWideBelow;
+    const size_t lds =
+        smem_keys_off(wide ? sizeof(TopkSmem<kMergeThreads>) : sizeof(TopkSmem<kThreads>)) + (size_t)((cap + 3) & ~3) * 4;
     ScopedProf pr(s, "topk_chunk");
-    hipLaunchKernelGGL(topk_chunk, dim3(a.rows, p.nchunks), dim3(kThreads), lds, s, p, cap);
+    if (wide) {
+      if ((e = set_lds((const void*)topk_chunk<kMergeThreads>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(topk_chunk<kMergeThreads>, dim3(a.rows, p.nchunks), dim3(kMergeThreads), lds, s, p, cap);
+    } else {
+      if ((e = set_lds((const void*)topk_chunk<kThreads>, lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(topk_chunk<kThreads>, dim3(a.rows, p.nchunks), dim3(kThreads), lds, s, p, cap);
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    const int m = p.nchunks * a.k;
-    const int cap = m < kStageMax ? m : kStageMax;
-    const size_t lds = ((sizeof(TopkSmem<kMergeThreads>) + 15) & ~(size_t)15) + (size_t)cap * 4;
+    int cap, defer, prune;
+    const size_t lds = merge_lds(p.nchunks * a.k, a.k, true, &cap, &defer, &prune);
     if ((e = set_lds((const void*)topk_merge, lds)) != hipSuccess) return e;
     ScopedProf pr(s, "topk_merge");
-    hipLaunchKernelGGL(topk_merge, dim3(a.rows), dim3(kMergeThreads), lds, s, p, cap);
+    hipLaunchKernelGGL(topk_merge, dim3(a.rows), dim3(kMergeThreads), lds, s, p, cap, defer, prune);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int32_t* slots, hipStream_t s) {
+hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int32_t* slots, uint2* bounds,
+                             hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (!a.out_idx || !keys || !slots || (!a.counts && !a.q_pos)) return hipErrorInvalidValue;
   Params p{};
   p.rows = a.rows; p.k = a.k; p.counts = a.counts; p.q_pos = a.q_pos; p.N = a.N; p.m = a.m;
   p.len_div = a.len_div; p.force_last = a.force_last; p.idx_map = a.idx_map;
   p.idx_map_stride = a.idx_map_stride; p.out_idx = a.out_idx; p.max_len = a.max_len;
-  p.nchunks = nchunks; p.ws_keys = keys; p.ws_slot = slots;
-  const int m = nchunks * a.k;
-  const int cap = m < kStageMax ? m : kStageMax;
-  const size_t lds = ((sizeof(TopkSmem<kMergeThreads>) + 15) & ~(size_t)15) + (size_t)cap * 4;
+  p.nchunks = nchunks; p.ws_keys = keys; p.ws_slot = slots; p.ws_bound = bounds;
+  int cap, defer, prune;
+  const size_t lds = merge_lds(nchunks * a.k, a.k, bounds != nullptr, &cap, &defer, &prune);
   hipError_t e = set_lds((const void*)topk_merge, lds);
   if (e != hipSuccess) return e;
   ScopedProf pr(s, "topk_merge");
-  hipLaunchKernelGGL(topk_merge, dim3(a.rows), dim3(kMergeThreads), lds, s, p, cap);
+  hipLaunchKernelGGL(topk_merge, dim3(a.rows), dim3(kMergeThreads), lds, s, p, cap, defer, prune);
   return hipGetLastError();
 }
 
@@ -308,8 +463,9 @@ hipError_t launch_hier_expand(int rows, int n_keep, int block, const int32_t* se
   if (rows == 0) return hipSuccess;
   if (!sel_blocks || !q_pos || !out_cand || !out_count) return hipErrorInvalidValue;
   ScopedProf pr(s, "hier_expand");
-  hipLaunchKernelGGL(hier_expand, dim3(rows), dim3(kThreads), 0, s, n_keep, block, sel_blocks, q_pos,
-                     N, m, out_cand, out_count);
+  const int total = n_keep * block;
+  hipLaunchKernelGGL(hier_expand, dim3(rows, (total + kThreads - 1) / kThreads), dim3(kThreads), 0, s, n_keep,
+                     block, sel_blocks, q_pos, N, m, out_cand, out_count);
   return hipGetLastError();
 }
 

@@ -7,9 +7,10 @@
 // 2048 LDS bins (shift chosen from the span), keeps the bin holding the k-th largest key
 // and narrows the range to it, until the range is a single key.  Clustered scores (the
 // usual case once rows hold only candidates) therefore still spread over many bins, so
-// LDS atomics rarely collide.  A final pass walks the row in index order; one ballot per
-// wave plus a cross-wave prefix gives every selected key its output slot, so the output
-// is ascending and ties resolve to the lower index.
+// LDS atomics rarely collide.  A pass costs three barriers (the histograms are double
+// buffered).  The compaction counts the selected keys of every 256-key segment, scans the
+// segment counts once across the block and then places each key at its rank in index
+// order: the output is ascending and ties resolve to the lower index.
 #pragma once
 
 #include "common.h"
@@ -17,21 +18,19 @@
 namespace csa2 {
 
 constexpr int kTopkBins = 2048;
+constexpr int kSegKeys = 256;  // keys per compaction segment: 4 per lane of one wave
+constexpr int kSegMax = 128;   // segments per compaction sweep (32768 keys)
 
 template <int kT>
 struct TopkSmem {
   static constexpr int kW = kT / 64;
-  uint32_t hist[kTopkBins];
-  uint32_t wsum[kW];
-  uint32_t wgt[kW], weq[kW];
+  uint32_t hist[2][kTopkBins];  // double-buffered: one pass fills one while the other is cleared
+  uint32_t seg[kSegMax];        // per segment: (#keys > T) | (#keys == T) << 16, then their prefix
+  uint32_t wsum[2][kW];
   uint32_t wlo[kW], whi[kW];
-  uint32_t sel_bin, krem;
+  uint32_t sel_bin[2], krem[2];
+  uint32_t bound_lo, bound_cnt;
 };
-
-__device__ __forceinline__ uint64_t lane_lt_mask() {
-  const int l = threadIdx.x & 63;
-  return l == 0 ? 0ull : (~0ull >> (64 - l));
-}
 
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
@@ -57,42 +56,92 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
 }
 
-// exclusive prefix over the block of one value per thread; the total through *total
+// inclusive prefix sum over the 64 lanes of a wave, by DPP: shifts of 1, 2, 4, 8 lanes
+// inside each 16-lane row, then the row totals carried by the row broadcasts of lanes 15
+// and 31 (lanes without a source add 0)
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_or0<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_or0<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_or0<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_or0<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_or0<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or0<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+}
+
+// exclusive prefix over the block of one value per thread, with the total
 template <int kT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, TopkSmem<kT>& sm) {
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t a, uint32_t* total, TopkSmem<kT>& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sm.wsum[wave] = x;
+  const uint32_t x = wave_incl_scan(a);
+  if (lane == 63) sm.wsum[1][wave] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < TopkSmem<kT>::kW; ++w) {
-    if (w < wave) before += sm.wsum[w];
-    tot += sm.wsum[w];
+    const uint32_t u = sm.wsum[1][w];
+    if (w < wave) before += u;
+    tot += u;
   }
-  __syncthreads();
   *total = tot;
-  return before + x - v;
+  return before + x - a;
+}
+
+// every key of src[0:n): thread-strided; with vector sources 4 consecutive keys per step
+template <int kT, class Src, class F>
+__device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
+  if constexpr (Src::kVec) {
+    for (int i = 4 * threadIdx.x; i < n; i += 4 * kT) {
+      const uint4 v = src.key4(i);
+      f(v.x);
+      if (i + 1 < n) f(v.y);
+      if (i + 2 < n) f(v.z);
+      if (i + 3 < n) f(v.w);
+    }
+  } else {
+    for (int i = threadIdx.x; i < n; i += kT) f(src.key(i));
+  }
+}
+
+// the 4 keys [i, i+4) of a segment lane (keys at or past n are reported invalid)
+template <class Src>
+__device__ __forceinline__ void keys4(const Src& src, int i, int n, uint32_t (&k)[4]) {
+  if constexpr (Src::kVec) {
+    if (i < n) {
+      const uint4 v = src.key4(i);
+      k[0] = v.x; k[1] = v.y; k[2] = v.z; k[3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = i + j < n ? src.key(i + j) : 0u;
+  }
 }
 
 // Threshold T (the k-th largest key of src.key(0..n-1)) and how many keys equal to T are
 // taken.  Requires 1 <= k <= n.  Every thread of the block must call it.
+//
+// With k2 (1 <= k2 <= k) it also reports a cheap lower bound of the k2-th largest key: the
+// lower edge L2 of the first pass's bin that holds it, with g2 = the number of keys >= L2
+// (at least k2).  Chunked selection uses it to prune candidates before the merge.
 template <int kT, class Src>
 __device__ void radix_threshold(const Src& src, int n, int k, TopkSmem<kT>& sm, uint32_t* T_out,
-                                uint32_t* take_out) {
+                                uint32_t* take_out, int k2 = 0, uint32_t* L2_out = nullptr,
+                                uint32_t* g2_out = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kTopkBins; i += kT) sm.hist[0][i] = 0;
   // live range [lo, lo + span]
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = threadIdx.x; i < n; i += kT) {
-    const uint32_t kk = src.key(i);
+  for_keys<kT>(src, n, [&](uint32_t kk) {
     lo = min(lo, kk);
     hi = max(hi, kk);
-  }
+  });
   lo = wave_umin(lo);
   hi = wave_umax(hi);
   if (lane == 0) { sm.wlo[wave] = lo; sm.whi[wave] = hi; }
@@ -102,98 +151,168 @@ __device__ void radix_threshold(const Src& src, int n, int k, TopkSmem<kT>& sm, 
   uint32_t span = hi - lo;
   uint32_t krem = (uint32_t)k;
   constexpr int kPer = kTopkBins / kT;
+  int cur = 0;
+  if (k2 > 0) {  // all keys equal: the bound is that key, held by every key
+    *L2_out = lo;
+    *g2_out = (uint32_t)n;
+  }
+  bool first = true;
   while (span != 0) {
     const int bits = 32 - __builtin_clz(span);
     const int shift = bits > 11 ? bits - 11 : 0;
     const uint32_t top = lo + span;
-    for (int i = threadIdx.x; i < kTopkBins; i += kT) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kT) {
-      const uint32_t kk = src.key(i);
-      if (kk >= lo && kk <= top) atomicAdd(&sm.hist[(kk - lo) >> shift], 1u);
-    }
+    // fill hist[cur] (cleared before the last barrier); clear the other for the next pass
+    for (int i = threadIdx.x; i < kTopkBins; i += kT) sm.hist[cur ^ 1][i] = 0;
+    for_keys<kT>(src, n, [&](uint32_t kk) {
+      if (kk >= lo && kk <= top) atomicAdd(&sm.hist[cur][(kk - lo) >> shift], 1u);
+    });
     __syncthreads();
     // thread t owns bins [2048 - kPer(t+1), 2048 - kPer*t): low t = high bins
     const int hb = kTopkBins - kPer * threadIdx.x - 1;
     uint32_t local = 0;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) local += sm.hist[hb - j];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan<kT>(local, &tot, sm);
+    for (int j = 0; j < kPer; ++j) local += sm.hist[cur][hb - j];
+    const uint32_t incl = wave_incl_scan(local);
+    if (lane == 63) sm.wsum[0][wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < TopkSmem<kT>::kW; ++w)
+      if (w < wave) before += sm.wsum[0][w];
+    const uint32_t above = before + incl - local;
     if (above < krem && above + local >= krem) {
       uint32_t cum = above;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const uint32_t c = sm.hist[hb - j];
+        const uint32_t c = sm.hist[cur][hb - j];
         if (cum + c >= krem) {
-          sm.sel_bin = (uint32_t)(hb - j);
-          sm.krem = krem - cum;
+          sm.sel_bin[cur] = (uint32_t)(hb - j);
+          sm.krem[cur] = krem - cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    if (first && k2 > 0 && above < (uint32_t)k2 && above + local >= (uint32_t)k2) {
+      uint32_t cum = above;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t c = sm.hist[cur][hb - j];
+        if (cum + c >= (uint32_t)k2) {
+          sm.bound_lo = lo + ((uint32_t)(hb - j) << shift);
+          sm.bound_cnt = cum + c;
           break;
         }
         cum += c;
       }
     }
     __syncthreads();
-    const uint32_t b = sm.sel_bin;
-    krem = sm.krem;
-    __syncthreads();
+    const uint32_t b = sm.sel_bin[cur];
+    krem = sm.krem[cur];
+    if (first && k2 > 0) {
+      *L2_out = sm.bound_lo;
+      *g2_out = sm.bound_cnt;
+    }
+    first = false;
     const uint32_t blo = lo + (b << shift);
     const uint32_t bspan = shift == 0 ? 0u : ((1u << shift) - 1u);
     span = min(bspan, top - blo);
     lo = blo;
+    cur ^= 1;
   }
   *T_out = lo;
   *take_out = krem;
 }
 
 // Walk src[0:n) in index order and call out(pos, i, key) for the selected keys: key > T,
-// or key == T among the first take_eq such keys.  Stops after k selections.
+// or key == T among the first take_eq such keys, pos = the key's rank in index order.
+// The row is cut into 256-key segments, one wave each, 4 consecutive keys per lane.  A
+// first sweep counts every segment's keys above / equal to T; one block scan over the
+// segment counts gives each segment its output offset; a second sweep places the keys
+// (a wave scan of the per-lane counts orders them inside the segment).
 template <int kT, class Src, class Out>
 __device__ void ordered_compact(const Src& src, int n, int k, uint32_t T, uint32_t take_eq, TopkSmem<kT>& sm,
                                 Out out) {
+  constexpr int kW = TopkSmem<kT>::kW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t sel_seen = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += kT) {
-    const int i = base + threadIdx.x;
-    const bool valid = i < n;
-    const uint32_t kk = valid ? src.key(i) : 0u;
-    const bool gt = valid && kk > T;
-    const bool eq = valid && kk == T;
-    const uint64_t mgt = __ballot(gt), meq = __ballot(eq);
-    if (lane == 0) {
-      sm.wgt[wave] = (uint32_t)__popcll(mgt);
-      sm.weq[wave] = (uint32_t)__popcll(meq);
-    }
-    __syncthreads();
-    uint32_t sel_before = sel_seen, tot_sel = 0, tot_eq = 0, my_take = 0;
+  uint32_t gt_base = 0, eq_base = 0;  // counts before the current sweep (block-uniform)
+  for (int base = 0; base < n; base += kSegKeys * kSegMax) {
+    const int nseg = min(kSegMax, (n - base + kSegKeys - 1) / kSegKeys);
+    for (int s = wave; s < nseg; s += kW) {
+      const int i = base + kSegKeys * s + 4 * lane;
+      uint32_t kk[4] = {0u, 0u, 0u, 0u};
+      keys4(src, i, n, kk);
+      uint32_t c = 0;
 #pragma unroll
-    for (int w = 0; w < TopkSmem<kT>::kW; ++w) {
-      const uint32_t e_before_w = eq_seen + tot_eq;
-      const uint32_t take_w = take_eq > e_before_w ? min(take_eq - e_before_w, sm.weq[w]) : 0u;
-      if (w < wave) sel_before += sm.wgt[w] + take_w;
-      if (w == wave) my_take = take_w;
-      tot_sel += sm.wgt[w] + take_w;
-      tot_eq += sm.weq[w];
+      for (int j = 0; j < 4; ++j)
+        if (i + j < n) c += kk[j] > T ? 1u : (kk[j] == T ? 0x10000u : 0u);
+      const uint32_t tot = wave_total(wave_incl_scan(c));
+      if (lane == 0) sm.seg[s] = tot;
     }
-    const uint64_t lt = lane_lt_mask();
-    const uint32_t eq_rank = (uint32_t)__popcll(meq & lt);
-    if (gt || (eq && eq_rank < my_take)) {
-      const uint32_t pos = sel_before + (uint32_t)__popcll(mgt & lt) + min(eq_rank, my_take);
-      if (pos < (uint32_t)k) out(pos, i, kk);  // always true when the threshold is exact
-    }
-    sel_seen += tot_sel;
-    eq_seen += tot_eq;
     __syncthreads();
-    if (sel_seen >= (uint32_t)k) break;  // uniform: every thread holds the same counts
+    // segment offsets: thread t takes segment t (nseg <= kSegMax <= kT)
+    const uint32_t mine = threadIdx.x < nseg ? sm.seg[threadIdx.x] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<kT>(mine, &total, sm);  // both 16-bit halves at once
+    if (threadIdx.x < nseg) sm.seg[threadIdx.x] = ex;
+    __syncthreads();
+    for (int s = wave; s < nseg; s += kW) {
+      const uint32_t sg = sm.seg[s];
+      uint32_t g = gt_base + (sg & 0xffffu), e = eq_base + (sg >> 16);
+      if (g + min(e, take_eq) >= (uint32_t)k) break;  // wave-uniform; later segments come later
+      const int i = base + kSegKeys * s + 4 * lane;
+      uint32_t kk[4] = {0u, 0u, 0u, 0u};
+      keys4(src, i, n, kk);
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + j < n) c += kk[j] > T ? 1u : (kk[j] == T ? 0x10000u : 0u);
+      const uint32_t ex_lane = wave_incl_scan(c) - c;
+      g += ex_lane & 0xffffu;
+      e += ex_lane >> 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i + j >= n) break;
+        if (kk[j] > T) {
+          const uint32_t pos = g + min(e, take_eq);
+          if (pos < (uint32_t)k) out(pos, i + j, kk[j]);  // always true when the threshold is exact
+          ++g;
+        } else if (kk[j] == T) {
+          if (e < take_eq && g + e < (uint32_t)k) out(g + e, i + j, kk[j]);
+          ++e;
+        }
+      }
+    }
+    gt_base += total & 0xffffu;
+    eq_base += total >> 16;
+    if (gt_base + min(eq_base, take_eq) >= (uint32_t)k) break;  // block-uniform
+    __syncthreads();  // the segment counts are refilled by the next sweep
   }
+}
+
+// Rank of the per-chunk pruning bound in chunked selection: ceil(k / (nchunks - 1)), so
+// that the full chunks alone (all but possibly the last) hold at least k keys at or above
+// their bounds.
+__host__ __device__ __forceinline__ int bound_rank(int k, int nchunks) {
+  const int d = nchunks > 1 ? nchunks - 1 : 1;
+  const int k2 = (k + d - 1) / d;
+  return k2 < k ? k2 : k;
 }
 
 // key sources
 struct KeysLds {
+  static constexpr bool kVec = true;  // 16-byte aligned, readable in groups of 4
+  const uint32_t* keys;
+  __device__ __forceinline__ uint32_t key(int i) const { return keys[i]; }
+  __device__ __forceinline__ uint4 key4(int i) const { return *reinterpret_cast<const uint4*>(keys + i); }
+};
+struct KeysGlobal {  // keys in global memory, any alignment
+  static constexpr bool kVec = false;
   const uint32_t* keys;
   __device__ __forceinline__ uint32_t key(int i) const { return keys[i]; }
 };
 struct KeysScores {
+  static constexpr bool kVec = false;
   const float* scores;
   int force;  // index whose key is forced to the maximum, or -1
   __device__ __forceinline__ uint32_t key(int i) const {
