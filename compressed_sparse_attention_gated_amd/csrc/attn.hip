@@ -5,19 +5,21 @@
 // per head in the softmax denominator; [CSA2 column] "保留了 CSA 的骨架": the selected
 // entries are joined by the latest 128 uncompressed rows of the layer).
 //
-// attn_mfma (bf16 queries, 64-head groups, c = 512, bf16 or FP4 rows):
-//   One workgroup = one query x 64 heads x a contiguous range of row slots (a split).
+// attn_mfma (bf16 queries, groups of 32 heads, c = 512, bf16 or FP4 rows):
+//   One workgroup = one query x 32 heads x a contiguous range of row slots (a split).
 //   Rows are gathered 32 at a time into LDS (FP4 rows dequantised on the way: E2M1 x E4M3
-//   is exact in bf16), double-buffered through registers.  Each of the 4 waves owns 16
-//   heads for S^T = rows x heads on v_mfma_f32_16x16x32_bf16 (q_hat in registers); the C
-//   layout of S^T gives each lane one head and 8 rows, which is exactly the A-operand
-//   layout of P for the PV product, so P never needs a transpose.  For PV each wave owns
-//   128 output channels of all 64 heads; the V operand (rows along K) is read with the
-//   gfx950 LDS transpose read ds_read_b64_tr_b16 from the same row-major tile that fed
-//   S^T (shared K = V, one copy in LDS).  Softmax is online in fp32 (exp2, scale folded
-//   into q_hat).  Tiles are XOR-swizzled in 16-byte chunks so both read patterns are free
-//   of bank conflicts.  With several splits per query the unnormalised partial output and
-//   (max, sum) go to a workspace and attn_combine merges them in a fixed order.
+//   is exact in bf16), double-buffered through registers; the workgroup barriers order
+//   LDS only, so the next tile's loads stay in flight across them.  Wave (hq, mr) computes
+//   the S^T block rows 16*mr.. x heads 16*hq.. on v_mfma_f32_16x16x32_bf16 (q_hat in
+//   registers); the C layout of S^T gives each lane one head and 4 rows, written to LDS in
+//   the A-operand order of P for the PV product.  For PV each wave owns 128 output
+//   channels of all 32 heads; the V operand (rows along K) is read with the gfx950 LDS
+//   transpose read ds_read_b64_tr_b16 from the same row-major tile that fed S^T (shared
+//   K = V, one copy in LDS).  The row pitch is padded by 16 bytes so both read patterns
+//   avoid bank conflicts.  Softmax in fp32 with exp2 (scale folded into q_hat) against a
+//   fixed per-head reference (see kOverflow).  With several splits per query the
+//   unnormalised partial output and (max, sum) go to a workspace and attn_combine merges
+//   them in a fixed order.
 //
 // attn_simple: any head count / width / dtype; one wave per (query, head), fp32 math.
 
@@ -51,14 +53,16 @@ struct AttnDev {
 struct WinRange {
   int lo_row, cnt;
 };
-__device__ __forceinline__ WinRange window_of(const AttnDev& a, int b, int t_pos) {
+__device__ __forceinline__ WinRange window_of_p0(const AttnDev& a, int p0, int t_pos) {
   WinRange w{0, 0};
   if (!a.win || a.n_win <= 0) return w;
-  const int p0 = a.win_pos0[b];
   const int lo = max(t_pos - a.n_win + 1, p0);
   const int hi = min(t_pos, p0 + a.Lw - 1);
   if (hi >= lo) { w.lo_row = lo - p0; w.cnt = hi - lo + 1; }
   return w;
+}
+__device__ __forceinline__ WinRange window_of(const AttnDev& a, int b, int t_pos) {
+  return window_of_p0(a, (a.win && a.n_win > 0) ? a.win_pos0[b] : 0, t_pos);
 }
 
 // ------------------------------------------------------------------ attn_simple
@@ -344,13 +348,13 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
 
   // ---- every global load of the prologue at once: this split's slot ids, and the q rows
   // ---- of this wave's 8 heads
-  if (tile0 < tile1) stage_slots(a, row, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, sm.src);
   uint4 qraw[8];
 #pragma unroll
   for (int hh = 0; hh < 8; ++hh)
     qraw[hh] = *reinterpret_cast<const uint4*>((const uint16_t*)a.q + ((size_t)row * a.H + head0 + 8 * wave + hh) * kC + 8 * lane);
+  if (tile0 < tile1) stage_slots(a, row, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, sm.src);
   stage_rope(a, t_pos, sm.rope_c, sm.rope_s);
-  __syncthreads();
+  lds_barrier();
   // rows of the first tile start travelling while q_hat is formed
   Prefetch<kFP4> pf;
   if (tile0 < tile1) fetch_tile<kFP4>(a, b, sm.src, pf);
@@ -391,12 +395,12 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
     for (int e = 0; e < 8; ++e) f[e] *= mul;
     *reinterpret_cast<uint4*>(qs + (8 * wave + hh) * kPitch + 16 * lane) = pack8(f);
   }
-  __syncthreads();
+  lds_barrier();
   bf16x8 qreg[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks)
     qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qs + (16 * hq + li) * kPitch + 64 * ks + 16 * g));
-  __syncthreads();
+  lds_barrier();
 
   // per-lane LDS byte offsets (tile-relative): A operand row 16*mr + li at chunk g;
   // transpose-read source rows 4g + li/4 (and +16) at channel 128*wave + 4*(li%4)
@@ -409,7 +413,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   f32x4 oacc[2][8];
   for (int pass = 0;; ++pass) {
     if (pass > 0) {  // restart with a larger reference: every wave left the loop together
-      __syncthreads();
+      lds_barrier();
       fetch_tile<kFP4>(a, b, sm.src, pf);
     }
     l_part = 0.f;
@@ -422,7 +426,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
     for (int ti = tile0; ti < tile1; ++ti) {
       const int* src = sm.src + (ti - tile0) * kTile;
       commit_tile<kFP4>(src, pf, sm.tile[buf]);
-      __syncthreads();
+      lds_barrier();
       if (ti + 1 < tile1) fetch_tile<kFP4>(a, b, src + kTile, pf);
       // valid rows of this wave's half: row 16*mr + r <-> bit r
       const uint32_t vm = (uint32_t)__ballot(lane < 16 && src[16 * mr + (lane & 15)] != -1);
@@ -446,7 +450,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
       }
       tmax = rows_max(tmax);
       if (g == 0) sm.wmax[mr][my_head] = tmax;
-      __syncthreads();
+      lds_barrier();
       tmax = fmaxf(sm.wmax[0][my_head], sm.wmax[1][my_head]);  // whole 32-row tile
       if (m_use == -INFINITY) m_use = tmax;  // first valid tile of this head: O is still 0
       const bool ovf = tmax > m_use + kOverflow;
@@ -462,7 +466,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
       *reinterpret_cast<uint2*>(&sm.pbuf[my_head][8 * g + 4 * mr]) =
           make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       if (lane == 0) sm.ovf[wave] = __ballot(ovf) != 0;
-      __syncthreads();
+      lds_barrier();
       if (__builtin_amdgcn_readfirstlane(sm.ovf[0] | sm.ovf[1] | sm.ovf[2] | sm.ovf[3])) {
         overflow = true;
         m_use = fmaxf(m_use, tmax);
@@ -493,7 +497,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
     sm.lpart[mr][my_head] = l_part;
     if (mr == 0) sm.mfin[my_head] = m_use;
   }
-  __syncthreads();
+  lds_barrier();
   if (a.splits > 1) {
     const size_t pidx = ((size_t)row * a.n_hg + hg) * a.splits + split;
     float* po = a.part_o + pidx * kHG * kC;
@@ -546,7 +550,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
     if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + threadIdx.x] * kLog2e - m);
     a.out_mass[(size_t)row * a.H + head0 + threadIdx.x] = l > 0.f ? l / den : 0.f;
   }
-  __syncthreads();
+  lds_barrier();
   uint4* op = reinterpret_cast<uint4*>((uint16_t*)a.out + ((size_t)row * a.H + head0) * kC);
   const uint4* src = reinterpret_cast<const uint4*>(os);
   for (int q = threadIdx.x; q < kHG * kC / 8; q += kThreadsM) op[q] = src[q];
@@ -566,19 +570,42 @@ __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
   stage_rope(a, t_pos, rc, rs);
   const size_t pbase = ((size_t)row * a.n_hg + hg) * a.splits;
   const int head0 = hg * kHG;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.part_ml[(pbase + s) * 2 * kHG + hl]);
-  float l = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (mx != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float ms = a.part_ml[(pbase + s) * 2 * kHG + hl];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - mx);
-      l += wgt * a.part_ml[(pbase + s) * 2 * kHG + kHG + hl];
-      const float4* po = reinterpret_cast<const float4*>(a.part_o + ((pbase + s) * kHG + hl) * kC + c8);
-      const float4 x0 = po[0], x1 = po[1];
-      o[0] += wgt * x0.x; o[1] += wgt * x0.y; o[2] += wgt * x0.z; o[3] += wgt * x0.w;
-      o[4] += wgt * x1.x; o[5] += wgt * x1.y; o[6] += wgt * x1.z; o[7] += wgt * x1.w;
+  // every split's (m, l) and 8 channels are loaded before any is used
+  constexpr int kMaxS = 8;
+  float ms[kMaxS], ls[kMaxS];
+  float4 x0[kMaxS], x1[kMaxS];
+  float mx = -INFINITY, l = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s0 = 0; s0 < a.splits; s0 += kMaxS) {
+#pragma unroll
+    for (int q = 0; q < kMaxS; ++q) {
+      const int s2 = s0 + q;
+      if (s2 < a.splits) {
+        ms[q] = a.part_ml[(pbase + s2) * 2 * kHG + hl];
+        ls[q] = a.part_ml[(pbase + s2) * 2 * kHG + kHG + hl];
+        const float4* po = reinterpret_cast<const float4*>(a.part_o + ((pbase + s2) * kHG + hl) * kC + c8);
+        x0[q] = po[0];
+        x1[q] = po[1];
+      } else {
+        ms[q] = -INFINITY;
+      }
+    }
+    float mnew = mx;
+#pragma unroll
+    for (int q = 0; q < kMaxS; ++q) mnew = fmaxf(mnew, ms[q]);
+    if (mnew == -INFINITY) continue;
+    // rescale what earlier groups accumulated (splits merged in order)
+    const float r = mx == -INFINITY ? 0.f : exp2f(mx - mnew);
+    l *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= r;
+    mx = mnew;
+#pragma unroll
+    for (int q = 0; q < kMaxS; ++q) {
+      if (ms[q] == -INFINITY) continue;
+      const float wgt = exp2f(ms[q] - mx);
+      l += wgt * ls[q];
+      o[0] += wgt * x0[q].x; o[1] += wgt * x0[q].y; o[2] += wgt * x0[q].z; o[3] += wgt * x0[q].w;
+      o[4] += wgt * x1[q].x; o[5] += wgt * x1[q].y; o[6] += wgt * x1[q].z; o[7] += wgt * x1[q].w;
     }
   }
   float den = l;
@@ -593,9 +620,9 @@ __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
       const int ch = c8 + e;
       if (ch >= rope_lo) {
         const float cs = rc[(ch - rope_lo) >> 1], sn = -rs[(ch - rope_lo) >> 1];
-        const float x0 = o[e], x1 = o[e + 1];
-        o[e] = x0 * cs - x1 * sn;
-        o[e + 1] = x0 * sn + x1 * cs;
+        const float y0 = o[e], y1 = o[e + 1];
+        o[e] = y0 * cs - y1 * sn;
+        o[e + 1] = y0 * sn + y1 * cs;
       }
     }
   }
@@ -642,15 +669,23 @@ AttnDev make_dev(const csa2_attn_desc& d) {
   return a;
 }
 
+
+struct AttnPlan {
+  int splits, tps;
+};
+AttnPlan plan_attn(const csa2_attn_desc& d) {
+  AttnPlan p{1, 1};
+  if (mfma_ok(d)) pick_splits(d, &p.splits, &p.tps);
+  return p;
+}
+
 }  // namespace
 
 size_t attn_workspace_bytes(const csa2_attn_desc& d) {
-  if (!mfma_ok(d)) return 0;
-  int splits, tps;
-  pick_splits(d, &splits, &tps);
-  if (splits <= 1) return 0;
-  const size_t units = (size_t)d.B * d.T * (d.H / kHG) * splits;
-  return units * (kHG * kC + 2 * kHG) * sizeof(float);
+  const AttnPlan p = plan_attn(d);
+  if (!mfma_ok(d) || p.splits <= 1) return 0;
+  const size_t units = (size_t)d.B * d.T * (d.H / kHG);
+  return units * p.splits * (kHG * kC + 2 * kHG) * sizeof(float);
 }
 
 hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -671,16 +706,14 @@ hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipSt
       hipLaunchKernelGGL(attn_simple<uint16_t>, dim3(rows * d.H), dim3(64), 0, s, a);
     return hipGetLastError();
   }
-  int splits, tps;
-  pick_splits(d, &splits, &tps);
-  a.splits = splits;
-  a.tiles_per_split = tps;
-  if (splits > 1) {
+  const AttnPlan plan = plan_attn(d);
+  a.splits = plan.splits;
+  a.tiles_per_split = plan.tps;
+  if (plan.splits > 1) {
     if (!ws || ws_bytes < attn_workspace_bytes(d)) return hipErrorInvalidValue;
-    const size_t units = (size_t)rows * a.n_hg * splits;
+    const size_t units = (size_t)rows * a.n_hg;
     a.part_o = (float*)ws;
-    a.part_ml = (float*)((char*)ws + units * kHG * kC * sizeof(float));
-    (void)ws_bytes;
+    a.part_ml = (float*)((char*)ws + units * plan.splits * kHG * kC * sizeof(float));
   }
   const size_t lds = sizeof(MfmaSmem);
   static bool attr_set = false;
@@ -691,6 +724,7 @@ hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipSt
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  const int splits = plan.splits;
   if (d.kv_dtype == CSA2_FP4_E4M3) {
     ScopedProf p(s, "attn_mfma_fp4");
     hipLaunchKernelGGL(attn_mfma<true>, dim3(rows, splits, a.n_hg), dim3(kThreadsM), lds, s, a);

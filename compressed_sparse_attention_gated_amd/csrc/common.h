@@ -87,6 +87,12 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load of the wave (vmcnt 0), which would drain register prefetches
+// issued before it; this one waits for the wave's LDS operations alone, so prefetched
+// tiles stay in flight across it.  Use it where the barrier orders LDS accesses only.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ float swz_xor16(float v) {  // lane l <- lane l^16 (within 32)
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (0x10 << 10) | 0x1F));
 }

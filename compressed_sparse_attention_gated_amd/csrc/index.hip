@@ -350,7 +350,7 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
   // the group's scan length: the largest limit of its queries
   __shared__ int s_lim[kShWaves];
   if (lane == 0) s_lim[wave] = limit;
-  __syncthreads();
+  lds_barrier();
   int glim = 0;
 #pragma unroll
   for (int i = 0; i < kShWaves; ++i) glim = max(glim, s_lim[i]);
@@ -412,7 +412,7 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
 
   fetch(0);
   commit(0);
-  __syncthreads();
+  lds_barrier();
   int st = 0;
   for (int base = 0; base < glim; base += kShTile) {
     const bool more = base + kShTile < glim;
@@ -436,7 +436,7 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
       }
     }
     if (more) commit(st ^ 1);
-    __syncthreads();
+    lds_barrier();
     st ^= 1;
   }
   (void)rows_total;

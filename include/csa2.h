@@ -201,9 +201,9 @@ CSA2_API int csa2_hier_candidates(const csa2_hier_desc *d, void *ws, size_t ws_b
  *   win: NULL or [B, Lw, c] with win_pos0 int32 [B]; window = n_win (0 = no window).
  *   sink: fp32 [H] or NULL (no sink term).  out_mass: fp32 [B, T, H] or NULL: receives
  *     sum_j p_j, the probability mass on real rows.
- *   ws, ws_bytes: workspace of at least csa2_attn_workspace_bytes(d).
+ *   ws, ws_bytes: workspace of at least csa2_attn_workspace_bytes(d) (split partials).
  * Supported: c % 16 == 0, c <= 512, rope_dims even and <= c; FP4 needs bf16 q.
- *   The MFMA path runs for bf16 q, c == 512, H % 64 == 0, rope_dims <= 128; other shapes
+ *   The MFMA paths run for bf16 q, c == 512, H % 32 == 0, rope_dims <= 128; other shapes
  *   use a generic fp32 kernel with the same semantics.
  */
 typedef struct {
