@@ -194,7 +194,7 @@ static size_t index_ws(const csa2_index_desc* d, csa2_mode mode) {
   const size_t rows = (size_t)d->B * d->T;
   if (mode == CSA2_MODE_REUSE || rows == 0) return 0;
   if (use_fused(d, mode)) {
-    const int chunk = scan_select_chunk(d->N, d->k);
+    const int chunk = scan_select_chunk((int)(d->B * d->T), d->N, d->k);
     const size_t nchunks = (size_t)(d->N + chunk - 1) / chunk;
     return align256(rows * nchunks * d->k * sizeof(uint32_t)) + align256(rows * nchunks * d->k * sizeof(int32_t)) +
            align256(rows * nchunks * sizeof(uint2));
@@ -225,7 +225,7 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(CSA2_ERR_WORKSPACE, "index: workspace of %zu bytes required, %zu given", need, ws_bytes);
   if (use_fused(d, mode)) {
-    const int chunk = scan_select_chunk(d->N, d->k);
+    const int chunk = scan_select_chunk((int)(d->B * d->T), d->N, d->k);
     const int nchunks = (d->N + chunk - 1) / chunk;
     uint32_t* keys = (uint32_t*)ws;
     int32_t* slots = (int32_t*)((char*)ws + align256((size_t)rows * nchunks * d->k * sizeof(uint32_t)));

@@ -163,6 +163,39 @@ __device__ __forceinline__ float tile_score(const bf16x8 (*areg)[DI / 16], const
   return s;
 }
 
+// Two 32-entry tiles at once, in two parts that a caller can separate: the MFMAs (into
+// two sets of accumulators) and the epilogue (ReLU, signed head weights, head sum).
+template <int DI, int MT>
+__device__ __forceinline__ void mfma2(const bf16x8 (*areg)[DI / 16], const bf16x8* b0, const bf16x8* b1,
+                                     f32x16* acc0, f32x16* acc1) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    acc0[mt] = f32x16{};
+    acc1[mt] = f32x16{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < DI / 16; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc0[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(areg[mt][ks], b0[ks], acc0[mt], 0, 0, 0);
+      acc1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(areg[mt][ks], b1[ks], acc1[mt], 0, 0, 0);
+    }
+}
+template <int MT>
+__device__ __forceinline__ void epi2(const f32x16* acc0, const f32x16* acc1, const float (*wreg)[16], float* s0,
+                                    float* s1) {
+  float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x0 += wreg[mt][r] * fmaxf(acc0[mt][r], 0.f);
+      x1 += wreg[mt][r] * fmaxf(acc1[mt][r], 0.f);
+    }
+  *s0 = x0 + xor32(x0);
+  *s1 = x1 + xor32(x1);
+}
+
 __device__ __forceinline__ int n_visible(const Dev& a, int row) {
   const int t = a.q_pos[row];
   const int nv = t >= 0 ? t / a.m : 0;
@@ -410,6 +443,21 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
     }
   };
 
+  // Waves 4..7 run one stage behind in their epilogue: at each stage they first finish the
+  // previous stage (VALU) and then issue this stage's MFMAs, while waves 0..3 do MFMAs then
+  // epilogue.  Waves w and w + 4 share a SIMD (waves are dealt round-robin to the 4 SIMDs),
+  // so the two alternate between the matrix core and the VALU instead of both waiting on
+  // the same unit after every workgroup barrier.
+  const bool lag = wave >= kShWaves / 2;
+  f32x16 acc0[MT], acc1[MT];
+  int pending = -1;  // lagging waves: base of the stage whose epilogue is still due
+  auto finish = [&](int sbase) {
+    float s0, s1;
+    epi2<MT>(acc0, acc1, wreg, &s0, &s1);
+    emit<kBlockMax>(a, row, lane, sbase + lane % 32, limit, s0);
+    emit<kBlockMax>(a, row, lane, sbase + 32 + lane % 32, limit, s1);
+  };
+  static_assert(kShTile == 64, "two 32-entry tiles per stage");
   fetch(0);
   commit(0);
   lds_barrier();
@@ -417,28 +465,33 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
   for (int base = 0; base < glim; base += kShTile) {
     const bool more = base + kShTile < glim;
     if (more) fetch(base + kShTile);
+    if (lag && pending >= 0) {
+      finish(pending);
+      pending = -1;
+    }
     if (active && base < limit) {
+      // both 32-entry halves of the stage (the second may lie past this query's limit:
+      // its scores are then simply not written)
+      bf16x8 b0[DI / 16], b1[DI / 16];
+      const int e = lane % 32;
 #pragma unroll
-      for (int sub = 0; sub < kShTile / 32; ++sub) {
-        const int slot0 = base + 32 * sub;
-        if (slot0 < limit) {
-          bf16x8 breg[DI / 16];
-          const int e = 32 * sub + lane % 32;
-#pragma unroll
-          for (int ks = 0; ks < DI / 16; ++ks) {
-            // LDS holds natural dim order; read the dims this lane's A registers hold
-            const int part = dim_of<DI, KF>(ks, h) / 8;
-            breg[ks] = as_bf16x8(tile[st][e * kCPR + (part ^ (e & (kCPR - 1)))]);
-          }
-          const float s = tile_score<DI, MT>(areg, breg, wreg);
-          emit<kBlockMax>(a, row, lane, slot0 + lane % 32, limit, s);
-        }
+      for (int ks = 0; ks < DI / 16; ++ks) {
+        // LDS holds natural dim order; read the dims this lane's A registers hold.  Entry
+        // e + 32 has the same swizzle as entry e, 32 rows further on.
+        const int part = dim_of<DI, KF>(ks, h) / 8;
+        const int idx = e * kCPR + (part ^ (e & (kCPR - 1)));
+        b0[ks] = as_bf16x8(tile[st][idx]);
+        b1[ks] = as_bf16x8(tile[st][idx + 32 * kCPR]);
       }
+      mfma2<DI, MT>(areg, b0, b1, acc0, acc1);
+      if (lag) pending = base;
+      else finish(base);
     }
     if (more) commit(st ^ 1);
     lds_barrier();
     st ^= 1;
   }
+  if (pending >= 0) finish(pending);
   (void)rows_total;
 }
 
@@ -511,10 +564,16 @@ Dev make_dev(const ScanArgs& s) {
 
 }  // namespace
 
-int scan_select_chunk(int N, int k) {
-  // a power of two >= 2048 such that the merge row (nchunks * k) stays <= 16384 keys
+int scan_select_chunk(int rows, int N, int k) {
+  // A power of two >= 2048 such that the merge row (nchunks * k) stays <= 16384 keys.
+  // Larger chunks (up to 8192) while the grid would exceed about one round of resident
+  // workgroups (2 per CU): each workgroup then streams longer before its chunk top-k, and
+  // fewer top-k phases leave the memory system idle.
+  constexpr long long kOneRound = 2 * 256 + 64;
   int chunk = 2048;
-  while ((long long)((N + chunk - 1) / chunk) * k > 16384 && chunk < (1 << 30)) chunk *= 2;
+  auto nch = [&](int c) { return (long long)((N + c - 1) / c); };
+  while ((nch(chunk) * k > 16384 || (chunk < 8192 && rows * nch(chunk) > kOneRound)) && chunk < (1 << 30))
+    chunk *= 2;
   return chunk;
 }
 

@@ -71,7 +71,7 @@ hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int
 // fused decode scan + chunk-local top-k (FULL mode, one query per sequence): the scan
 // writes (key, slot) pairs of each chunk's top-k; topk_merge finishes.  Returns the chunk
 // size used through *chunk_out and the number of chunks through *nchunks_out.
-int scan_select_chunk(int N, int k);
+int scan_select_chunk(int rows, int N, int k);
 hipError_t launch_index_scan_select(const ScanArgs& a, int k, int chunk, int nchunks, uint32_t* keys,
                                     int32_t* slots, uint2* bounds, hipStream_t s);
 
