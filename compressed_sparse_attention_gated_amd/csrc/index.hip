@@ -24,6 +24,7 @@
 #include "internal.h"
 #include "topk_core.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace csa2 {
@@ -122,6 +123,13 @@ __device__ __forceinline__ void to_b(const RawB<DI, KF>& r, int h, bf16x8* breg)
   }
 }
 
+// ReLU of an fp32 as a signed-integer max with 0 on its bit pattern: non-negative floats
+// are non-negative integers and every negative float (and -0) maps to +0.  One instruction,
+// where fmaxf(x, 0) needs a canonicalising max first.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // A operand (q_I of one query) and the head weights in the C layout
 template <int DI, int KF, int MT>
 __device__ __forceinline__ void load_query(const Dev& a, int row, int lane, bf16x8 (*areg)[DI / 16],
@@ -156,7 +164,7 @@ __device__ __forceinline__ float tile_score(const bf16x8 (*areg)[DI / 16], const
     for (int ks = 0; ks < DI / 16; ++ks)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(areg[mt][ks], breg[ks], acc, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wreg[mt][r] * fmaxf(acc[r], 0.f);
+    for (int r = 0; r < 16; ++r) s += wreg[mt][r] * relu_bits(acc[r]);
   }
   // lanes l and l^32 hold the two halves of the head rows of the same entry
   s += xor32(s);
@@ -189,8 +197,8 @@ __device__ __forceinline__ void epi2(const f32x16* acc0, const f32x16* acc1, con
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      x0 += wreg[mt][r] * fmaxf(acc0[mt][r], 0.f);
-      x1 += wreg[mt][r] * fmaxf(acc1[mt][r], 0.f);
+      x0 += wreg[mt][r] * relu_bits(acc0[mt][r]);
+      x1 += wreg[mt][r] * relu_bits(acc1[mt][r]);
     }
   *s0 = x0 + xor32(x0);
   *s1 = x1 + xor32(x1);
@@ -365,11 +373,12 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
 // ---------------------------------------------------------------- shared-B scan (prefill)
 constexpr int kShWaves = 8;
 constexpr int kShThreads = 64 * kShWaves;
-constexpr int kShTile = 64;  // entries per LDS stage
+constexpr int kShTile = 128;  // entries per LDS stage (two pairs of 32-entry tiles)
 
 template <int DI, int KF, int MT, bool kBlockMax>
-__global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total) {
-  // workgroup -> 8 consecutive query rows of one sequence; heavy (late) groups first
+__global__ void __launch_bounds__(kShThreads) scan_shared(Dev a) {
+  // workgroup -> 8 consecutive query rows of one sequence (one per wave); within a sequence
+  // the heavy (late, long causal range) groups come first
   const int groups_per_seq = (a.T + kShWaves - 1) / kShWaves;
   const int gid = blockIdx.x;
   const int b = gid / groups_per_seq;
@@ -457,7 +466,7 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
     emit<kBlockMax>(a, row, lane, sbase + lane % 32, limit, s0);
     emit<kBlockMax>(a, row, lane, sbase + 32 + lane % 32, limit, s1);
   };
-  static_assert(kShTile == 64, "two 32-entry tiles per stage");
+  static_assert(kShTile % 64 == 0, "pairs of 32-entry tiles per stage");
   fetch(0);
   commit(0);
   lds_barrier();
@@ -465,34 +474,37 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a, int rows_total)
   for (int base = 0; base < glim; base += kShTile) {
     const bool more = base + kShTile < glim;
     if (more) fetch(base + kShTile);
-    if (lag && pending >= 0) {
-      finish(pending);
-      pending = -1;
-    }
-    if (active && base < limit) {
-      // both 32-entry halves of the stage (the second may lie past this query's limit:
-      // its scores are then simply not written)
-      bf16x8 b0[DI / 16], b1[DI / 16];
-      const int e = lane % 32;
 #pragma unroll
-      for (int ks = 0; ks < DI / 16; ++ks) {
-        // LDS holds natural dim order; read the dims this lane's A registers hold.  Entry
-        // e + 32 has the same swizzle as entry e, 32 rows further on.
-        const int part = dim_of<DI, KF>(ks, h) / 8;
-        const int idx = e * kCPR + (part ^ (e & (kCPR - 1)));
-        b0[ks] = as_bf16x8(tile[st][idx]);
-        b1[ks] = as_bf16x8(tile[st][idx + 32 * kCPR]);
+    for (int pr = 0; pr < kShTile / 64; ++pr) {
+      const int pbase = base + 64 * pr;
+      if (lag && pending >= 0) {
+        finish(pending);
+        pending = -1;
       }
-      mfma2<DI, MT>(areg, b0, b1, acc0, acc1);
-      if (lag) pending = base;
-      else finish(base);
+      if (active && pbase < limit) {
+        // both 32-entry tiles of the pair (the second may lie past this query's limit:
+        // its scores are then simply not written)
+        bf16x8 b0[DI / 16], b1[DI / 16];
+        const int e = 64 * pr + lane % 32;
+#pragma unroll
+        for (int ks = 0; ks < DI / 16; ++ks) {
+          // LDS holds natural dim order; read the dims this lane's A registers hold.  Entry
+          // e + 32 has the same swizzle as entry e, 32 rows further on.
+          const int part = dim_of<DI, KF>(ks, h) / 8;
+          const int idx = e * kCPR + (part ^ (e & (kCPR - 1)));
+          b0[ks] = as_bf16x8(tile[st][idx]);
+          b1[ks] = as_bf16x8(tile[st][idx + 32 * kCPR]);
+        }
+        mfma2<DI, MT>(areg, b0, b1, acc0, acc1);
+        if (lag) pending = pbase;
+        else finish(pbase);
+      }
     }
     if (more) commit(st ^ 1);
     lds_barrier();
     st ^= 1;
   }
   if (pending >= 0) finish(pending);
-  (void)rows_total;
 }
 
 template <int DI, int KF, int MT>
@@ -501,10 +513,9 @@ hipError_t launch3(const ScanArgs& s, const Dev& d, hipStream_t st) {
   const bool cand = s.cand != nullptr;
   const bool bm = s.block_max != nullptr;
   if (!cand && s.T >= kShWaves) {
-    const int gps = (s.T + kShWaves - 1) / kShWaves;
-    dim3 grid(gps * s.B);
-    if (bm) hipLaunchKernelGGL((scan_shared<DI, KF, MT, true>), grid, dim3(kShThreads), 0, st, d, rows);
-    else hipLaunchKernelGGL((scan_shared<DI, KF, MT, false>), grid, dim3(kShThreads), 0, st, d, rows);
+    dim3 grid(((s.T + kShWaves - 1) / kShWaves) * s.B);
+    if (bm) hipLaunchKernelGGL((scan_shared<DI, KF, MT, true>), grid, dim3(kShThreads), 0, st, d);
+    else hipLaunchKernelGGL((scan_shared<DI, KF, MT, false>), grid, dim3(kShThreads), 0, st, d);
     return hipGetLastError();
   }
   const int len = cand ? s.cand_stride : s.N;
