@@ -37,9 +37,17 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source code-generation options.  The indexer scan reads its MFMA accumulators with
+# ordinary VALU instructions in the epilogue; the VGPR form of the MFMA writes them where
+# those instructions read, instead of to accumulation registers that need a copy each.
+SOURCE_FLAGS = {
+    "index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

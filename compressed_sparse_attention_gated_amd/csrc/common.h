@@ -88,6 +88,10 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16 lanes
 
+// Index of the calling wave in its workgroup as a scalar: the compiler cannot prove that
+// threadIdx.x / 64 is the same across a wave, so loops bounded by it would otherwise
+// compile to exec-masked (divergent) control flow.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x / 64); }
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
 // outstanding global load of the wave (vmcnt 0), which would drain register prefetches
 // issued before it; this one waits for the wave's LDS operations alone, so prefetched

@@ -204,6 +204,29 @@ __device__ __forceinline__ void epi2(const f32x16* acc0, const f32x16* acc1, con
   *s1 = x1 + xor32(x1);
 }
 
+// One 32-entry tile split the same way: MFMAs into acc, then the epilogue.  A wave that
+// issues tile t's MFMAs before tile t-1's epilogue keeps the matrix core and the VALU
+// busy together; the epilogue never waits on the MFMAs just issued.
+template <int DI, int MT>
+__device__ __forceinline__ void mfma1(const bf16x8 (*areg)[DI / 16], const bf16x8* b, f32x16* acc) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < DI / 16; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(areg[mt][ks], b[ks], acc[mt], 0, 0, 0);
+}
+template <int MT>
+__device__ __forceinline__ float epi1(const f32x16* acc, const float (*wreg)[16]) {
+  float x = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x += wreg[mt][r] * relu_bits(acc[mt][r]);
+  return x + xor32(x);
+}
+
 __device__ __forceinline__ int n_visible(const Dev& a, int row) {
   const int t = a.q_pos[row];
   const int nv = t >= 0 ? t / a.m : 0;
@@ -230,13 +253,53 @@ __device__ __forceinline__ void emit(const Dev& a, int row, int lane, int slot, 
   if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, limit, s);
 }
 
+// This wave's tiles tb = t0, t0 + stride, ... < c1 through a kDepth-deep register pipeline:
+// tile t is consumed while the next kDepth - 1 tiles load.  load(tile, raw) issues one
+// tile's loads (a tile past c1 must load something in bounds); consume(raw, tile) uses it.
+// The loop body has no early exit: every path back to its head has issued the same loads
+// in the same order as the prologue, so the compiler's wait before each use covers only
+// the tile being used (an exit inside the body would join the back edge with fewer loads
+// and force a wait for all of them).  The last kDepth - 1 tiles drain after the loop.
+template <int kDepth, class Raw, class Load, class Consume>
+__device__ __forceinline__ void tile_pipeline(int t0, int c1, int stride, Load&& load, Consume&& consume) {
+  Raw buf[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    load(t0 + i * stride, buf[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int tb = t0;
+  for (; tb + (kDepth - 1) * stride < c1; tb += kDepth * stride) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      load(tb + (i + kDepth - 1) * stride, buf[(i + kDepth - 1) % kDepth]);
+      consume(buf[i], tb + i * stride);
+    }
+  }
+  // buf[i] holds tile tb + i * stride; fewer than kDepth of them are below c1
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    if (tb + i * stride >= c1) break;
+    consume(buf[i], tb + i * stride);
+  }
+}
+
+// Pipeline depth of the private scans.  A raw MXFP4 tile is 9 registers (2.2 KB per wave)
+// and affords a deeper pipeline than a bf16 tile (32 registers, 8 KB) at equal occupancy.
+template <int KF>
+constexpr int kPipeDepth = KF == 1 ? 6 : 3;
+// Skewed epilogue (a second accumulator set live): MXFP4 scans are bound by issue, not
+// by HBM, and have the registers for it; a bf16 scan would spill.
+template <int KF>
+constexpr bool kSkewEpilogue = KF == 1;
+
 // ---------------------------------------------------------------- private-B scan
 template <int DI, int KF, int MT, bool kCand, bool kBlockMax>
 __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
   const int row = blockIdx.x;
   const int b = row / a.T;
   const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
+  const int wave = wave_index();
   const int limit = kCand ? min(a.n_cand[row], a.cand_stride) : n_visible(a, row);
   const int c0 = blockIdx.y * chunk;
   const int c1 = min(c0 + chunk, limit);
@@ -256,36 +319,25 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
     return s;
   };
 
-  // three tiles in flight per wave: tile t is consumed while t+1 and t+2 load
   constexpr int kStride = 32 * kWaves;
   const int t0 = c0 + 32 * wave;
   if (t0 >= c1) return;
-  RawB<DI, KF> b0, b1, b2;
-  load_raw<DI, KF>(a, b, entry_of(t0 + lane % 32), h, b0);
-  load_raw<DI, KF>(a, b, entry_of(t0 + kStride + lane % 32), h, b1);
-  auto consume = [&](const RawB<DI, KF>& raw, int tb) {
-    bf16x8 breg[DI / 16];
-    to_b<DI, KF>(raw, h, breg);
-    float s = tile_score<DI, MT>(areg, breg, wreg);
-    if constexpr (kCand) {
-      const int slot = tb + lane % 32;
-      if (slot < c1) {
-        const int e = a.cand[(size_t)row * a.cand_stride + slot];
-        if (e < 0 || e >= a.N) s = -INFINITY;
-      }
-    }
-    emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
-  };
-  for (int tb = t0; tb < c1; tb += 3 * kStride) {
-    load_raw<DI, KF>(a, b, entry_of(tb + 2 * kStride + lane % 32), h, b2);
-    consume(b0, tb);
-    if (tb + kStride >= c1) break;
-    load_raw<DI, KF>(a, b, entry_of(tb + 3 * kStride + lane % 32), h, b0);
-    consume(b1, tb + kStride);
-    if (tb + 2 * kStride >= c1) break;
-    load_raw<DI, KF>(a, b, entry_of(tb + 4 * kStride + lane % 32), h, b1);
-    consume(b2, tb + 2 * kStride);
-  }
+  tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(
+      t0, c1, kStride,
+      [&](int tb, RawB<DI, KF>& raw) { load_raw<DI, KF>(a, b, entry_of(tb + lane % 32), h, raw); },
+      [&](const RawB<DI, KF>& raw, int tb) {
+        bf16x8 breg[DI / 16];
+        to_b<DI, KF>(raw, h, breg);
+        float s = tile_score<DI, MT>(areg, breg, wreg);
+        if constexpr (kCand) {
+          const int slot = tb + lane % 32;
+          if (slot < c1) {
+            const int e = a.cand[(size_t)row * a.cand_stride + slot];
+            if (e < 0 || e >= a.N) s = -INFINITY;
+          }
+        }
+        emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
+      });
 }
 
 // ---------------------------------------------------------------- fused scan + chunk top-k
@@ -302,7 +354,7 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
   uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15));
   const int row = blockIdx.x, c = blockIdx.y;
   const int b = row / a.T;
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64, wave = wave_index();
   const int limit = n_visible(a, row);
   const int c0 = c * chunk;
   const int c1 = min(c0 + chunk, limit);
@@ -319,34 +371,48 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
   float wreg[MT][16];
   load_query<DI, KF, MT>(a, row, lane, areg, wreg);
   const int h = lane / 32;
-  // three tiles in flight per wave: tile t is consumed while t+1 and t+2 load
   constexpr int kStride = 32 * kWaves;
   const int t0 = c0 + 32 * wave;
   if (t0 < c1) {
-    auto ent = [&](int slot) { return min(slot, c1 - 1); };
-    RawB<DI, KF> b0, b1, b2;
-    load_raw<DI, KF>(a, b, ent(t0 + lane % 32), h, b0);
-    load_raw<DI, KF>(a, b, ent(t0 + kStride + lane % 32), h, b1);
-    auto consume = [&](const RawB<DI, KF>& raw, int tb) {
-      bf16x8 breg[DI / 16];
-      to_b<DI, KF>(raw, h, breg);
-      const float s = tile_score<DI, MT>(areg, breg, wreg);
+    // The key store needs no branch: tiles start at multiples of 32 from c0 and the chunk
+    // is a multiple of 32 entries, so every slot of a tile lies inside the chunk's key
+    // array, and keys past the visible end are never read.  With the skewed epilogue,
+    // tile t's epilogue runs after tile t+1's MFMAs are issued; before the first tile the
+    // pending epilogue is a zero tile at t0, which that tile's own epilogue overwrites.
+    f32x16 pacc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) pacc[mt] = f32x16{};
+    int ptb = t0;
+    auto finish = [&](const f32x16* acc, int tb) {
+      const float s = epi1<MT>(acc, wreg);
       const int slot = tb + lane % 32;
-      if (lane < 32 && slot < c1) skeys[slot - c0] = float_key(s);
+      skeys[slot - c0] = float_key(s);
       if constexpr (kScores) {
         if (lane < 32 && slot < c1) a.scores[(size_t)row * a.row_stride + slot] = s;
       }
       if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, c1, s);
     };
-    for (int tb = t0; tb < c1; tb += 3 * kStride) {
-      load_raw<DI, KF>(a, b, ent(tb + 2 * kStride + lane % 32), h, b2);
-      consume(b0, tb);
-      if (tb + kStride >= c1) break;
-      load_raw<DI, KF>(a, b, ent(tb + 3 * kStride + lane % 32), h, b0);
-      consume(b1, tb + kStride);
-      if (tb + 2 * kStride >= c1) break;
-      load_raw<DI, KF>(a, b, ent(tb + 4 * kStride + lane % 32), h, b1);
-      consume(b2, tb + 2 * kStride);
+    auto load = [&](int tb, RawB<DI, KF>& raw) { load_raw<DI, KF>(a, b, min(tb + lane % 32, c1 - 1), h, raw); };
+    if constexpr (kSkewEpilogue<KF>) {
+      tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(t0, c1, kStride, load, [&](const RawB<DI, KF>& raw, int tb) {
+        bf16x8 breg[DI / 16];
+        to_b<DI, KF>(raw, h, breg);
+        f32x16 cacc[MT];
+        mfma1<DI, MT>(areg, breg, cacc);
+        finish(pacc, ptb);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) pacc[mt] = cacc[mt];
+        ptb = tb;
+      });
+      finish(pacc, ptb);
+    } else {
+      tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(t0, c1, kStride, load, [&](const RawB<DI, KF>& raw, int tb) {
+        bf16x8 breg[DI / 16];
+        to_b<DI, KF>(raw, h, breg);
+        f32x16 acc[MT];
+        mfma1<DI, MT>(areg, breg, acc);
+        finish(acc, tb);
+      });
     }
   }
   __syncthreads();
@@ -384,7 +450,7 @@ __global__ void __launch_bounds__(kShThreads) scan_shared(Dev a) {
   const int b = gid / groups_per_seq;
   const int g = groups_per_seq - 1 - (gid % groups_per_seq);
   const int lane = threadIdx.x % 64;
-  const int wave = threadIdx.x / 64;
+  const int wave = wave_index();
   const int t = g * kShWaves + wave;
   const bool active = t < a.T;
   const int row = b * a.T + (active ? t : 0);
