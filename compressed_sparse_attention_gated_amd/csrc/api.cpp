@@ -187,7 +187,8 @@ static int check_index(const csa2_index_desc* d, csa2_mode mode) {
 // decode-style FULL calls (few queries per sequence, long rows) fuse the chunk-local
 // top-k into the scan; the workspace then holds (key, slot) pairs instead of scores
 static bool use_fused(const csa2_index_desc* d, csa2_mode mode) {
-  return mode == CSA2_MODE_FULL && d->T < 8 && d->N > 8192;
+  return mode == CSA2_MODE_FULL && d->T < 8 && d->N > 8192 &&
+         scan_select_chunk((int)(d->B * d->T), d->N, d->k) <= kMaxSelectChunk;
 }
 
 static size_t index_ws(const csa2_index_desc* d, csa2_mode mode) {

@@ -345,6 +345,10 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
 // its scores in LDS, then selects the chunk's top-k there and writes (key, slot) pairs;
 // the chunk union contains the row's top-k, which topk_merge extracts.
 constexpr int kSelThreads = 256;
+// Chunks of up to kRegKeys keys are selected from registers (kRegRows rows of 4 keys
+// per thread); longer ones from LDS.
+constexpr int kRegRows = 8;
+constexpr int kRegKeys = 4 * kSelThreads * kRegRows;
 
 template <int DI, int KF, int MT, bool kBlockMax, bool kScores>
 __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int k, int nchunks,
@@ -424,16 +428,49 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
     if (threadIdx.x == 0) *ob = make_uint2(0u, (uint32_t)len);  // every key >= 0
     return;
   }
-  const KeysLds src{skeys};
-  uint32_t T, take, L2, g2;
   // pruning bound for the merge, from the first radix pass
   const int k2 = bound_rank(k, nchunks);
-  radix_threshold<kSelThreads>(src, len, k, sm, &T, &take, k2, &L2, &g2);
-  if (threadIdx.x == 0) *ob = make_uint2(L2, g2);
-  ordered_compact<kSelThreads>(src, len, k, T, take, sm, [&](uint32_t pos, int i, uint32_t key) {
+  uint32_t T, take, L2, g2;
+  auto direct = [=](uint32_t pos, int i, uint32_t key) {
     ok[pos] = key;
     os[pos] = c0 + i;
-  });
+  };
+  if (len <= kRegKeys) {
+    // the chunk's keys move into registers: the selection passes read no LDS
+    KeyRegs<kSelThreads, kRegRows> r;
+    key_regs_load(r, skeys, len);
+    radix_threshold<kSelThreads>(r, len, k, sm, &T, &take, k2, &L2, &g2);
+    if (T != 0u && k <= kTopkBins) {
+      // selected (key, slot) pairs staged in the histogram space, then stored coalesced
+      uint32_t* sk = sm.hist[0];
+      uint32_t* ss = sm.hist[1];
+      ordered_compact_regs(r, k, T, take, sm, [&](uint32_t pos, int i, uint32_t key) {
+        sk[pos] = key;
+        ss[pos] = (uint32_t)(c0 + i);
+      });
+      lds_barrier();
+      if ((k & 3) == 0) {
+        for (int i = 4 * threadIdx.x; i < k; i += 4 * kSelThreads) {
+          *reinterpret_cast<uint4*>(ok + i) = *reinterpret_cast<const uint4*>(sk + i);
+          *reinterpret_cast<uint4*>(os + i) = *reinterpret_cast<const uint4*>(ss + i);
+        }
+      } else {
+        for (int i = threadIdx.x; i < k; i += kSelThreads) {
+          ok[i] = sk[i];
+          os[i] = (int32_t)ss[i];
+        }
+      }
+    } else if (T != 0u) {
+      ordered_compact_regs(r, k, T, take, sm, direct);
+    } else {  // the zero slots past len could tie with T = 0: compact from LDS, which stops at len
+      ordered_compact<kSelThreads>(KeysLds{skeys}, len, k, T, take, sm, direct);
+    }
+  } else {
+    const KeysLds src{skeys};
+    radix_threshold<kSelThreads>(src, len, k, sm, &T, &take, k2, &L2, &g2);
+    ordered_compact<kSelThreads>(src, len, k, T, take, sm, direct);
+  }
+  if (threadIdx.x == 0) *ob = make_uint2(L2, g2);
 }
 
 // ---------------------------------------------------------------- shared-B scan (prefill)

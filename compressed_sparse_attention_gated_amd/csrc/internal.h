@@ -72,6 +72,9 @@ hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int
 // writes (key, slot) pairs of each chunk's top-k; topk_merge finishes.  Returns the chunk
 // size used through *chunk_out and the number of chunks through *nchunks_out.
 int scan_select_chunk(int rows, int N, int k);
+// Longest chunk the fused scan + chunk top-k handles: its keys (4 bytes each) and the
+// selection state share one workgroup's 160 KiB of LDS.
+constexpr int kMaxSelectChunk = 32768;
 hipError_t launch_index_scan_select(const ScanArgs& a, int k, int chunk, int nchunks, uint32_t* keys,
                                     int32_t* slots, uint2* bounds, hipStream_t s);
 

@@ -97,7 +97,9 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t a, uint32_t* total,
 // every key of src[0:n): thread-strided; with vector sources 4 consecutive keys per step
 template <int kT, class Src, class F>
 __device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
-  if constexpr (Src::kVec) {
+  if constexpr (Src::kRegs) {
+    src.each(f);
+  } else if constexpr (Src::kVec) {
     for (int i = 4 * threadIdx.x; i < n; i += 4 * kT) {
       const uint4 v = src.key4(i);
       f(v.x);
@@ -131,7 +133,7 @@ __device__ __forceinline__ void keys4(const Src& src, int i, int n, uint32_t (&k
 // lower edge L2 of the first pass's bin that holds it, with g2 = the number of keys >= L2
 // (at least k2).  Chunked selection uses it to prune candidates before the merge.
 template <int kT, class Src>
-__device__ void radix_threshold(const Src& src, int n, int k, TopkSmem<kT>& sm, uint32_t* T_out,
+__device__ __forceinline__ void radix_threshold(const Src& src, int n, int k, TopkSmem<kT>& sm, uint32_t* T_out,
                                 uint32_t* take_out, int k2 = 0, uint32_t* L2_out = nullptr,
                                 uint32_t* g2_out = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -231,7 +233,7 @@ __device__ void radix_threshold(const Src& src, int n, int k, TopkSmem<kT>& sm, 
 // segment counts gives each segment its output offset; a second sweep places the keys
 // (a wave scan of the per-lane counts orders them inside the segment).
 template <int kT, class Src, class Out>
-__device__ void ordered_compact(const Src& src, int n, int k, uint32_t T, uint32_t take_eq, TopkSmem<kT>& sm,
+__device__ __forceinline__ void ordered_compact(const Src& src, int n, int k, uint32_t T, uint32_t take_eq, TopkSmem<kT>& sm,
                                 Out out) {
   constexpr int kW = TopkSmem<kT>::kW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -301,17 +303,20 @@ __host__ __device__ __forceinline__ int bound_rank(int k, int nchunks) {
 
 // key sources
 struct KeysLds {
+  static constexpr bool kRegs = false;
   static constexpr bool kVec = true;  // 16-byte aligned, readable in groups of 4
   const uint32_t* keys;
   __device__ __forceinline__ uint32_t key(int i) const { return keys[i]; }
   __device__ __forceinline__ uint4 key4(int i) const { return *reinterpret_cast<const uint4*>(keys + i); }
 };
 struct KeysGlobal {  // keys in global memory, any alignment
+  static constexpr bool kRegs = false;
   static constexpr bool kVec = false;
   const uint32_t* keys;
   __device__ __forceinline__ uint32_t key(int i) const { return keys[i]; }
 };
 struct KeysScores {
+  static constexpr bool kRegs = false;
   static constexpr bool kVec = false;
   const float* scores;
   int force;  // index whose key is forced to the maximum, or -1
@@ -319,5 +324,113 @@ struct KeysScores {
     return i == force ? 0xffffffffu : float_key(scores[i]);
   }
 };
+
+// ---------------------------------------------------------------- keys held in registers
+// A chunk of n <= 4 * kT * kJ keys spread over the block's registers: in row j, thread t
+// holds the keys [4t + 4 kT j, +4) - the layout of the compaction segments above, where
+// row j of wave w is segment kW j + w.  The selection passes then read no LDS; only the
+// histogram counts go there.  Slots at or past n hold 0.
+template <int kT, int kJ>
+struct KeyRegs {
+  static constexpr bool kRegs = true;
+  static constexpr bool kVec = false;
+  uint4 v[kJ];
+  int n, rows;  // rows: the rows that hold keys below n
+
+  // every key below n, in any order
+  template <class F>
+  __device__ __forceinline__ void each(F f) const {
+    const int i0 = 4 * (int)threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      if (4 * kT * (j + 1) <= n) {  // a full row (block-uniform)
+        f(v[j].x); f(v[j].y); f(v[j].z); f(v[j].w);
+      } else if (j < rows) {
+        const int i = i0 + 4 * kT * j;
+        if (i < n) f(v[j].x);
+        if (i + 1 < n) f(v[j].y);
+        if (i + 2 < n) f(v[j].z);
+        if (i + 3 < n) f(v[j].w);
+      }
+    }
+  }
+};
+
+// the n keys of an LDS array (16-byte aligned) into registers
+template <int kT, int kJ>
+__device__ __forceinline__ void key_regs_load(KeyRegs<kT, kJ>& r, const uint32_t* keys, int n) {
+  r.n = n;
+  r.rows = (n + 4 * kT - 1) / (4 * kT);
+  const int i0 = 4 * (int)threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    r.v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < r.rows) {
+      const int i = i0 + 4 * kT * j;
+      if (i + 3 < n) {
+        r.v[j] = *reinterpret_cast<const uint4*>(keys + i);
+      } else if (i < n) {
+        r.v[j].x = keys[i];
+        if (i + 1 < n) r.v[j].y = keys[i + 1];
+        if (i + 2 < n) r.v[j].z = keys[i + 2];
+      }
+    }
+  }
+}
+
+// ordered_compact over register keys (one sweep, n <= kSegKeys * kSegMax).  Requires
+// T > 0, so the zero slots past n are never taken.
+template <int kT, int kJ, class Out>
+__device__ __forceinline__ void ordered_compact_regs(const KeyRegs<kT, kJ>& r, int k, uint32_t T, uint32_t take_eq,
+                                                     TopkSmem<kT>& sm, Out out) {
+  constexpr int kW = TopkSmem<kT>::kW;
+  static_assert(kW * kJ <= kSegMax, "one compaction sweep");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto cnt = [&](uint32_t kk) { return kk > T ? 1u : (kk == T ? 0x10000u : 0u); };
+  uint32_t exl[kJ];  // this lane's exclusive prefix inside its segment of row j
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    exl[j] = 0u;
+    if (j < r.rows) {
+      const uint32_t c = cnt(r.v[j].x) + cnt(r.v[j].y) + cnt(r.v[j].z) + cnt(r.v[j].w);
+      const uint32_t incl = wave_incl_scan(c);
+      exl[j] = incl - c;
+      if (lane == 63) sm.seg[kW * j + wave] = incl;
+    }
+  }
+  __syncthreads();
+  const int nseg = kW * r.rows;
+  const uint32_t mine = (int)threadIdx.x < nseg ? sm.seg[threadIdx.x] : 0u;
+  uint32_t total;
+  const uint32_t ex = block_excl_scan<kT>(mine, &total, sm);
+  if ((int)threadIdx.x < nseg) sm.seg[threadIdx.x] = ex;
+  __syncthreads();
+  const int i0 = 4 * (int)threadIdx.x;
+  bool done = false;  // wave-uniform: every later row lies past the k-th selected key
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    if (done || j >= r.rows) continue;
+    const uint32_t sg = sm.seg[kW * j + wave];
+    uint32_t g = sg & 0xffffu, e = sg >> 16;
+    if (g + min(e, take_eq) >= (uint32_t)k) {
+      done = true;
+      continue;
+    }
+    g += exl[j] & 0xffffu;
+    e += exl[j] >> 16;
+    const uint32_t kk[4] = {r.v[j].x, r.v[j].y, r.v[j].z, r.v[j].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (kk[c] > T) {
+        const uint32_t pos = g + min(e, take_eq);
+        if (pos < (uint32_t)k) out(pos, i0 + 4 * kT * j + c, kk[c]);
+        ++g;
+      } else if (kk[c] == T) {
+        if (e < take_eq && g + e < (uint32_t)k) out(g + e, i0 + 4 * kT * j + c, kk[c]);
+        ++e;
+      }
+    }
+  }
+}
 
 }  // namespace csa2
