@@ -274,7 +274,8 @@ def main():
     if wl.kind == "prefill":
         achieved = sf / (scan_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": scan_name, "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                "traffic": load_traffic(scan_name, TAGS[args.config]),
                 "flops_per_launch": sf}
     else:
         achieved = sb / (scan_ms * 1e-3) / 1e9
