@@ -69,6 +69,9 @@ __device__ __forceinline__ int32_t map_id(const Params& p, int r, int slot) {
 // Keys of a row or chunk staged once into LDS (vector loads); all passes then run from
 // LDS.  Up to kStageMax keys are staged; longer rows are read from global memory.
 constexpr int kStageMax = 32768;
+// Rows of up to kRegSingle keys are selected from registers (16 rows of 4 keys per thread
+// at 256 threads); the LDS then holds only the selection state.
+constexpr int kRegSingle = 16384;
 
 template <int kT>
 __device__ __forceinline__ void stage_keys(const float* scores, int n, int force, uint32_t* keys) {
@@ -109,7 +112,27 @@ __global__ void __launch_bounds__(kT) topk_single(Params p, int stage_cap, int d
   const float* row = p.scores + (size_t)r * p.row_stride;
   const int force = p.force_last ? n - 1 : -1;
   uint32_t T, take;
-  auto direct = [&](uint32_t pos, int i, uint32_t) { out[pos] = map_id(p, r, i); };
+  auto direct = [=](uint32_t pos, int i, uint32_t) { out[pos] = map_id(p, r, i); };
+  if (n <= kRegSingle) {
+    // the row's keys go straight from its scores into registers; LDS holds only the
+    // histograms, so several rows' workgroups share a CU
+    constexpr int kJ = kRegSingle / (4 * kT);
+    KeyRegs<kT, kJ> kr;
+    key_regs_load_scores(kr, row, n, force);
+    radix_threshold<kT>(kr, n, p.k, sm, &T, &take);
+    if (T != 0u && p.k <= 2 * kTopkBins) {
+      // selected positions staged in the histogram space, then mapped and stored coalesced
+      int32_t* ssel = reinterpret_cast<int32_t*>(&sm.hist[0][0]);
+      ordered_compact_regs(kr, p.k, T, take, sm, [=](uint32_t pos, int i, uint32_t) { ssel[pos] = i; });
+      lds_barrier();
+      for (int q = threadIdx.x; q < p.k; q += kT) out[q] = map_id(p, r, ssel[q]);
+    } else if (T != 0u) {
+      ordered_compact_regs(kr, p.k, T, take, sm, direct);
+    } else {  // slots past n could tie with T = 0: compact from the scores, which stop at n
+      ordered_compact<kT>(KeysScores{row, force}, n, p.k, T, take, sm, direct);
+    }
+    return;
+  }
   auto deferred = [&](uint32_t pos, int i, uint32_t) { sel[pos] = i; };
   if (n <= stage_cap) {
     stage_keys<kT>(row, n, force, skeys);
@@ -393,10 +416,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   p.max_len = a.max_len;
   hipError_t e;
   if (a.max_len <= kSingleMax) {
-    const int cap = a.max_len < kStageMax ? a.max_len : kStageMax;
+    // rows that fit the registers need no staged keys (and stage their selection in the
+    // histogram space)
+    const bool regs = a.max_len <= kRegSingle;
+    const int cap = regs ? 0 : (a.max_len < kStageMax ? a.max_len : kStageMax);
     const bool wide = a.rows < kWideBelow;
     size_t lds = smem_keys_off(wide ? sizeof(TopkSmem<kMergeThreads>) : sizeof(TopkSmem<kThreads>)) + (size_t)((cap + 3) & ~3) * 4;
-    const int defer = a.k <= kDeferMax && lds + (size_t)a.k * 4 <= kLdsMax;
+    const int defer = !regs && a.k <= kDeferMax && lds + (size_t)a.k * 4 <= kLdsMax;
     if (defer) lds += (size_t)a.k * 4;
     ScopedProf pr(s, "topk_single");
     if (wide) {

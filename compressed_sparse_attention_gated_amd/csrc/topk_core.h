@@ -378,6 +378,38 @@ __device__ __forceinline__ void key_regs_load(KeyRegs<kT, kJ>& r, const uint32_t
   }
 }
 
+// the keys of n fp32 scores in global memory; key index `force` (if >= 0) is forced to
+// the maximum
+template <int kT, int kJ>
+__device__ __forceinline__ void key_regs_load_scores(KeyRegs<kT, kJ>& r, const float* scores, int n, int force) {
+  r.n = n;
+  r.rows = (n + 4 * kT - 1) / (4 * kT);
+  const bool vec = (((uintptr_t)scores) & 15u) == 0;
+  const int i0 = 4 * (int)threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    r.v[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (j < r.rows) {
+      const int i = i0 + 4 * kT * j;
+      if (vec && i + 3 < n) {
+        const float4 f = *reinterpret_cast<const float4*>(scores + i);
+        r.v[j] = make_uint4(float_key(f.x), float_key(f.y), float_key(f.z), float_key(f.w));
+      } else {
+        if (i < n) r.v[j].x = float_key(scores[i]);
+        if (i + 1 < n) r.v[j].y = float_key(scores[i + 1]);
+        if (i + 2 < n) r.v[j].z = float_key(scores[i + 2]);
+        if (i + 3 < n) r.v[j].w = float_key(scores[i + 3]);
+      }
+      if (force >= i && force < i + 4) {
+        if (force == i) r.v[j].x = 0xffffffffu;
+        else if (force == i + 1) r.v[j].y = 0xffffffffu;
+        else if (force == i + 2) r.v[j].z = 0xffffffffu;
+        else r.v[j].w = 0xffffffffu;
+      }
+    }
+  }
+}
+
 // ordered_compact over register keys (one sweep, n <= kSegKeys * kSegMax).  Requires
 // T > 0, so the zero slots past n are never taken.
 template <int kT, int kJ, class Out>
