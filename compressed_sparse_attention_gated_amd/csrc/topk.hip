@@ -72,6 +72,7 @@ constexpr int kStageMax = 32768;
 // Rows of up to kRegSingle keys are selected from registers (16 rows of 4 keys per thread
 // at 256 threads); the LDS then holds only the selection state.
 constexpr int kRegSingle = 16384;
+constexpr int kRegThreads = 512;  // workgroup size of register rows when there are many rows
 
 template <int kT>
 __device__ __forceinline__ void stage_keys(const float* scores, int n, int force, uint32_t* keys) {
@@ -425,7 +426,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     const int defer = !regs && a.k <= kDeferMax && lds + (size_t)a.k * 4 <= kLdsMax;
     if (defer) lds += (size_t)a.k * 4;
     ScopedProf pr(s, "topk_single");
-    if (wide) {
+    if (regs && !wide) {  // many register rows: 512 threads, half the keys per thread
+      hipLaunchKernelGGL(topk_single<kRegThreads>, dim3(a.rows), dim3(kRegThreads),
+                         smem_keys_off(sizeof(TopkSmem<kRegThreads>)), s, p, 0, 0);
+    } else if (wide) {
       if ((e = set_lds((const void*)topk_single<kMergeThreads>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(topk_single<kMergeThreads>, dim3(a.rows), dim3(kMergeThreads), lds, s, p, cap, defer);
     } else {
