@@ -108,10 +108,17 @@ __device__ __forceinline__ void to_b(const RawB<DI, KF>& r, int h, bf16x8* breg)
     for (int ks = 0; ks < DI / 16; ++ks) breg[ks] = r.v[ks];
   } else {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    // this lane's dims (DI/2)*h .. +DI/2-1 span the scale groups g0 .. g0 + DI/64 - 1; each
+    // scale byte is extracted once
+    constexpr int kGroups = DI / 64 > 0 ? DI / 64 : 1;
+    const int g0 = dim_of<DI, KF>(0, h) / 32;
+    float scale[kGroups];
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q)
+      scale[q] = __builtin_bit_cast(float, __builtin_amdgcn_ubfe(r.s, 8 * (g0 + q), 8) << 23);
 #pragma unroll
     for (int ks = 0; ks < DI / 16; ++ks) {
-      const int g = dim_of<DI, KF>(ks, h) / 32;
-      const float sc = __builtin_bit_cast(float, ((r.s >> (8 * g)) & 0xffu) << 23);
+      const float sc = scale[ks / 4 < kGroups ? ks / 4 : kGroups - 1];  // 4 k-steps of 8 dims per group
       const uint32_t cw = r.c[ks];
       uint4 v;
       v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0));
