@@ -301,15 +301,23 @@ __device__ __forceinline__ void commit_tile(const int* src, const Prefetch<kFP4>
       const int q = threadIdx.x + 256 * i;
       const int r = q >> 4, part = q & 15;
       if (src[r] >= 0) {
-        // 32 codes -> channels 32*part .. 32*part+31; scales of groups 2*part, 2*part+1
+        // 32 codes -> channels 32*part .. 32*part+31; scales of groups 2*part, 2*part+1.
+        // The hardware's FP4 convert (unit scale) gives each code's E2M1 value, two codes
+        // (one byte, low nibble first) per instruction; times the E4M3 scale the product
+        // has at most 6 significant bits, so it is exact in fp32 and in bf16.
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
         const float s0 = e4m3_to_f32(pf.fs[i] & 0xffu), s1 = e4m3_to_f32(pf.fs[i] >> 8);
         const uint32_t words[4] = {pf.fc[i].x, pf.fc[i].y, pf.fc[i].z, pf.fc[i].w};
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
           float f[8];
           const float sc = qq < 2 ? s0 : s1;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = e2m1_to_f32((words[qq] >> (4 * e)) & 15u) * sc;
+          const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[qq], 1.0f, 0);
+          const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[qq], 1.0f, 1);
+          const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[qq], 1.0f, 2);
+          const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[qq], 1.0f, 3);
+          f[0] = v0.x * sc; f[1] = v0.y * sc; f[2] = v1.x * sc; f[3] = v1.y * sc;
+          f[4] = v2.x * sc; f[5] = v2.y * sc; f[6] = v3.x * sc; f[7] = v3.y * sc;
           *reinterpret_cast<uint4*>(tile + r * kPitch + 64 * part + 16 * qq) = pack8(f);
         }
       }
