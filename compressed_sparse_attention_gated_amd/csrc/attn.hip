@@ -258,15 +258,35 @@ __device__ __forceinline__ void stage_slots(const AttnDev& a, int row, int slot0
   }
 }
 
+// Row sources of one sequence, computed once per workgroup: the kernel arguments they come
+// from would otherwise be reloaded after every barrier (its memory clobber) for every row.
+struct RowBases {
+  const uint16_t* kv;       // bf16 cache rows of the sequence
+  const uint16_t* win;      // window rows of the sequence
+  const uint8_t* codes;     // FP4 cache rows: codes
+  const uint8_t* scales;    //                 and E4M3 scales
+};
+__device__ __forceinline__ RowBases row_bases(const AttnDev& a, int b) {
+  RowBases r;
+  r.kv = (const uint16_t*)a.kv + (size_t)b * a.N * kC;
+  r.win = (const uint16_t*)a.win + (size_t)b * a.Lw * kC;
+  r.codes = a.kv_codes + (size_t)b * a.N * (kC / 2);
+  r.scales = a.kv_scales + (size_t)b * a.N * (kC / 16);
+  return r;
+}
+
 template <bool kFP4>
-__device__ __forceinline__ void fetch_tile(const AttnDev& a, int b, const int* src, Prefetch<kFP4>& pf) {
+__device__ __forceinline__ void fetch_tile(const RowBases& rb, const int* src, Prefetch<kFP4>& pf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int srow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) srow[i] = src[wave + 4 * i];  // all slot reads first, one wait
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int sr = __builtin_amdgcn_readfirstlane(src[wave + 4 * i]);  // uniform per wave
+    const int sr = __builtin_amdgcn_readfirstlane(srow[i]);  // uniform per wave
     const uint16_t* base = nullptr;
-    if (sr <= -2) base = (const uint16_t*)a.win + ((size_t)b * a.Lw + (-2 - sr)) * kC;
-    else if (!kFP4 && sr >= 0) base = (const uint16_t*)a.kv + ((size_t)b * a.N + sr) * kC;
+    if (sr <= -2) base = rb.win + (size_t)(-2 - sr) * kC;
+    else if (!kFP4 && sr >= 0) base = rb.kv + (size_t)sr * kC;
     pf.v[i] = base ? reinterpret_cast<const uint4*>(base)[lane] : make_uint4(0, 0, 0, 0);
   }
   if constexpr (kFP4) {
@@ -276,8 +296,8 @@ __device__ __forceinline__ void fetch_tile(const AttnDev& a, int b, const int* s
       const int r = q >> 4, part = q & 15;
       const int sr = src[r];
       if (sr >= 0) {
-        pf.fc[i] = reinterpret_cast<const uint4*>(a.kv_codes + ((size_t)b * a.N + sr) * (kC / 2))[part];
-        pf.fs[i] = *reinterpret_cast<const uint16_t*>(a.kv_scales + ((size_t)b * a.N + sr) * (kC / 16) + 2 * part);
+        pf.fc[i] = reinterpret_cast<const uint4*>(rb.codes + (size_t)sr * (kC / 2))[part];
+        pf.fs[i] = *reinterpret_cast<const uint16_t*>(rb.scales + (size_t)sr * (kC / 16) + 2 * part);
       } else {
         pf.fc[i] = make_uint4(0, 0, 0, 0);
         pf.fs[i] = 0;
@@ -353,6 +373,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
   const int rope_lo = kC - a.rope_dims;
   const int head0 = hg * kHG;
+  const RowBases rb = row_bases(a, b);
 
   // ---- every global load of the prologue at once: this split's slot ids, and the q rows
   // ---- of this wave's 8 heads
@@ -365,7 +386,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   lds_barrier();
   // rows of the first tile start travelling while q_hat is formed
   Prefetch<kFP4> pf;
-  if (tile0 < tile1) fetch_tile<kFP4>(a, b, sm.src, pf);
+  if (tile0 < tile1) fetch_tile<kFP4>(rb, sm.src, pf);
 
   // ---- q_hat = RoPE_t(RMSNorm(q)) * scale * log2(e) -> LDS (bf16) -> B-operand registers
   uint8_t* qs = sm.tile[0];  // [32 heads][kPitch]
@@ -422,7 +443,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   for (int pass = 0;; ++pass) {
     if (pass > 0) {  // restart with a larger reference: every wave left the loop together
       lds_barrier();
-      fetch_tile<kFP4>(a, b, sm.src, pf);
+      fetch_tile<kFP4>(rb, sm.src, pf);
     }
     l_part = 0.f;
 #pragma unroll
@@ -435,7 +456,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
       const int* src = sm.src + (ti - tile0) * kTile;
       commit_tile<kFP4>(src, pf, sm.tile[buf]);
       lds_barrier();
-      if (ti + 1 < tile1) fetch_tile<kFP4>(a, b, src + kTile, pf);
+      if (ti + 1 < tile1) fetch_tile<kFP4>(rb, src + kTile, pf);
       // valid rows of this wave's half: row 16*mr + r <-> bit r
       const uint32_t vm = (uint32_t)__ballot(lane < 16 && src[16 * mr + (lane & 15)] != -1);
 
