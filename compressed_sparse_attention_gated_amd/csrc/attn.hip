@@ -45,8 +45,8 @@ struct AttnDev {
   const float* sink;
   void* out;
   float* out_mass;
-  float* part_o;   // [rows][n_hg][splits][32][c]
-  float* part_ml;  // [rows][n_hg][splits][2][32]
+  uint16_t* part_o;  // [rows][n_hg][splits][32][c] bf16: each split's output / its own sum
+  float* part_ml;    // [rows][n_hg][splits][2][32]: each split's (reference m, sum l)
   RopeFreq rope;   // theta^(-2u/r)
 };
 
@@ -528,20 +528,35 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   }
   lds_barrier();
   if (a.splits > 1) {
+    // The split's output divided by its own sum (a convex combination of rows, so within
+    // the rows' range) goes out as bf16, staged in LDS for 16-byte stores; attn_combine
+    // weighs the splits by their sums.
     const size_t pidx = ((size_t)row * a.n_hg + hg) * a.splits + split;
-    float* po = a.part_o + pidx * kHG * kC;
+    uint16_t* ps = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [32][512], contiguous
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      float inv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int hl = 16 * mt + 4 * g + j;
+        const float l = sm.lpart[0][hl] + sm.lpart[1][hl];
+        inv[j] = l > 0.f ? 1.0f / l : 0.f;
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          po[(size_t)(16 * mt + 4 * g + j) * kC + 128 * wave + 16 * nt + li] = oacc[mt][nt][j];
+          ps[(16 * mt + 4 * g + j) * kC + 128 * wave + 16 * nt + li] = f32_to_bf16_bits(oacc[mt][nt][j] * inv[j]);
+    }
     if (threadIdx.x < kHG) {
       float* pml = a.part_ml + pidx * 2 * kHG;
       pml[threadIdx.x] = sm.mfin[threadIdx.x];
       pml[kHG + threadIdx.x] = sm.lpart[0][threadIdx.x] + sm.lpart[1][threadIdx.x];
     }
+    lds_barrier();
+    uint4* po = reinterpret_cast<uint4*>(a.part_o + pidx * kHG * kC);
+    const uint4* pl = reinterpret_cast<const uint4*>(ps);
+    for (int q = threadIdx.x; q < kHG * kC / 8; q += kThreadsM) po[q] = pl[q];
     return;
   }
   // single split: normalise, inverse-rotate, stage bf16 output in LDS, coalesced store
@@ -602,7 +617,7 @@ __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
   // every split's (m, l) and 8 channels are loaded before any is used
   constexpr int kMaxS = 8;
   float ms[kMaxS], ls[kMaxS];
-  float4 x0[kMaxS], x1[kMaxS];
+  uint4 xr[kMaxS];
   float mx = -INFINITY, l = 0.f, o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int s0 = 0; s0 < a.splits; s0 += kMaxS) {
 #pragma unroll
@@ -611,9 +626,7 @@ __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
       if (s2 < a.splits) {
         ms[q] = a.part_ml[(pbase + s2) * 2 * kHG + hl];
         ls[q] = a.part_ml[(pbase + s2) * 2 * kHG + kHG + hl];
-        const float4* po = reinterpret_cast<const float4*>(a.part_o + ((pbase + s2) * kHG + hl) * kC + c8);
-        x0[q] = po[0];
-        x1[q] = po[1];
+        xr[q] = *reinterpret_cast<const uint4*>(a.part_o + ((pbase + s2) * kHG + hl) * kC + c8);
       } else {
         ms[q] = -INFINITY;
       }
@@ -631,10 +644,13 @@ __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
 #pragma unroll
     for (int q = 0; q < kMaxS; ++q) {
       if (ms[q] == -INFINITY) continue;
-      const float wgt = exp2f(ms[q] - mx);
-      l += wgt * ls[q];
-      o[0] += wgt * x0[q].x; o[1] += wgt * x0[q].y; o[2] += wgt * x0[q].z; o[3] += wgt * x0[q].w;
-      o[4] += wgt * x1[q].x; o[5] += wgt * x1[q].y; o[6] += wgt * x1[q].z; o[7] += wgt * x1[q].w;
+      // the split's unnormalised output is its sum times its stored (normalised) output
+      const float wl = exp2f(ms[q] - mx) * ls[q];
+      l += wl;
+      float x[8];
+      unpack8(xr[q], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += wl * x[e];
     }
   }
   float den = l;
@@ -714,7 +730,7 @@ size_t attn_workspace_bytes(const csa2_attn_desc& d) {
   const AttnPlan p = plan_attn(d);
   if (!mfma_ok(d) || p.splits <= 1) return 0;
   const size_t units = (size_t)d.B * d.T * (d.H / kHG);
-  return units * p.splits * (kHG * kC + 2 * kHG) * sizeof(float);
+  return units * p.splits * (kHG * kC * sizeof(uint16_t) + 2 * kHG * sizeof(float));
 }
 
 hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipStream_t s) {
@@ -741,8 +757,8 @@ hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipSt
   if (plan.splits > 1) {
     if (!ws || ws_bytes < attn_workspace_bytes(d)) return hipErrorInvalidValue;
     const size_t units = (size_t)rows * a.n_hg;
-    a.part_o = (float*)ws;
-    a.part_ml = (float*)((char*)ws + units * plan.splits * kHG * kC * sizeof(float));
+    a.part_o = (uint16_t*)ws;
+    a.part_ml = (float*)((char*)ws + units * plan.splits * kHG * kC * sizeof(uint16_t));
   }
   const size_t lds = sizeof(MfmaSmem);
   static bool attr_set = false;
