@@ -352,12 +352,14 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
 // its scores in LDS, then selects the chunk's top-k there and writes (key, slot) pairs;
 // the chunk union contains the row's top-k, which topk_merge extracts.
 constexpr int kSelThreads = 256;
-// Chunks of up to kRegKeys keys are selected from registers (kRegRows rows of 4 keys
-// per thread); longer ones from LDS.
-constexpr int kRegRows = 8;
-constexpr int kRegKeys = 4 * kSelThreads * kRegRows;
+// A chunk is selected from registers when it fits kRows rows of 4 keys per thread, from
+// LDS otherwise.  kRows = 8 (8192 keys) keeps the scan at two waves per SIMD; the longest
+// chunks (32,768 keys) hold their workgroup alone on a CU for its LDS, so their variant
+// spends the registers of one wave per SIMD on 32 rows instead.
+constexpr int kRegRowsSmall = 8;
+constexpr int kRegRowsLarge = kMaxSelectChunk / (4 * kSelThreads);
 
-template <int DI, int KF, int MT, bool kBlockMax, bool kScores>
+template <int DI, int KF, int MT, bool kBlockMax, bool kScores, int kRows>
 __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int k, int nchunks,
                                                            uint32_t* wkeys, int32_t* wslot, uint2* wbound) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -442,9 +444,9 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
     ok[pos] = key;
     os[pos] = c0 + i;
   };
-  if (len <= kRegKeys) {
+  if (len <= 4 * kSelThreads * kRows) {
     // the chunk's keys move into registers: the selection passes read no LDS
-    KeyRegs<kSelThreads, kRegRows> r;
+    KeyRegs<kSelThreads, kRows> r;
     key_regs_load(r, skeys, len);
     radix_threshold<kSelThreads>(r, len, k, sm, &T, &take, k2, &L2, &g2);
     if (T != 0u && k <= kTopkBins) {
@@ -653,23 +655,35 @@ hipError_t launch1(const ScanArgs& s, const Dev& d, hipStream_t st) {
   return s.k_dtype == CSA2_MXFP4 ? launch2<DI, 1>(s, d, st) : launch2<DI, 0>(s, d, st);
 }
 
+template <int DI, int KF, int MT, int kRows>
+hipError_t launch_sel4(const Dev& d, dim3 grid, size_t lds, bool bm, bool sc, int chunk, int k, int nchunks,
+                       uint32_t* keys, int32_t* slots, uint2* bounds, hipStream_t st) {
+  const void* fn = bm ? (sc ? (const void*)scan_select<DI, KF, MT, true, true, kRows> : (const void*)scan_select<DI, KF, MT, true, false, kRows>)
+                      : (sc ? (const void*)scan_select<DI, KF, MT, false, true, kRows> : (const void*)scan_select<DI, KF, MT, false, false, kRows>);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (bm && sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, true, kRows>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  else if (bm) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, false, kRows>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  else if (sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, false, true, kRows>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  else hipLaunchKernelGGL((scan_select<DI, KF, MT, false, false, kRows>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
+  return hipGetLastError();
+}
+
 template <int DI, int KF, int MT>
 hipError_t launch_sel3(const ScanArgs& s, const Dev& d, int k, int chunk, int nchunks, uint32_t* keys,
                        int32_t* slots, uint2* bounds, hipStream_t st) {
   const size_t lds = ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15) + (size_t)chunk * 4;
   dim3 grid(s.B * s.T, nchunks);
   const bool bm = s.block_max != nullptr, sc = s.scores != nullptr;
-  const void* fn = bm ? (sc ? (const void*)scan_select<DI, KF, MT, true, true> : (const void*)scan_select<DI, KF, MT, true, false>)
-                      : (sc ? (const void*)scan_select<DI, KF, MT, false, true> : (const void*)scan_select<DI, KF, MT, false, false>);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  // the large register variant only for a bf16 K_I with 128 dims and 33..64 heads (the
+  // configuration with chunks that long); others select long chunks from LDS
+  if constexpr (DI == 128 && KF == 0 && MT == 2) {
+    if (chunk > 4 * kSelThreads * kRegRowsSmall)
+      return launch_sel4<DI, KF, MT, kRegRowsLarge>(d, grid, lds, bm, sc, chunk, k, nchunks, keys, slots, bounds, st);
   }
-  if (bm && sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
-  else if (bm) hipLaunchKernelGGL((scan_select<DI, KF, MT, true, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
-  else if (sc) hipLaunchKernelGGL((scan_select<DI, KF, MT, false, true>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
-  else hipLaunchKernelGGL((scan_select<DI, KF, MT, false, false>), grid, dim3(kSelThreads), lds, st, d, chunk, k, nchunks, keys, slots, bounds);
-  return hipGetLastError();
+  return launch_sel4<DI, KF, MT, kRegRowsSmall>(d, grid, lds, bm, sc, chunk, k, nchunks, keys, slots, bounds, st);
 }
 
 Dev make_dev(const ScanArgs& s) {
