@@ -9,13 +9,16 @@
 // whole scan), B = 16 dims x 32 entries loaded straight from HBM into registers (lane l
 // reads 16 bytes of entry l%32), C = 32x32 fp32.  In C each lane holds 16 head-rows of one
 // entry column, so the ReLU, the signed head weight and the head sum are an in-lane
-// epilogue plus one swap between the two half-waves.  No LDS: every K_I byte is read
-// exactly once per query.  MXFP4 rows (E2M1 codes + E8M0 scale per 32) are dequantised
-// into the B registers by the hardware's scaled FP4 convert (exact in bf16).
+// epilogue plus one swap between the two half-waves.  The decode scans stage no K_I in
+// LDS: every K_I byte is read exactly once per query, straight into registers.  MXFP4 rows
+// (E2M1 codes + E8M0 scale per 32) are dequantised into the B registers by the hardware's
+// scaled FP4 convert (exact in bf16).
 //
-// Two variants:
-//  * scan_private: one query per workgroup slice; the 4 waves split the entry range.
-//    Used for decode (one query per sequence) and Reindex.
+// Three variants:
+//  * scan_select: decode FULL - workgroup (query, chunk of entries); the chunk's keys go to
+//    LDS and its exact top-k is selected in the same kernel, so scores never reach HBM.
+//  * scan_private: one query per workgroup slice, scores written out; the 4 waves split
+//    the entry range.  Used for Reindex and for decode rows too short to chunk.
 //  * scan_shared: prefill - a workgroup takes 8 consecutive queries of one sequence (one
 //    per wave) and streams the K_I tiles they share through LDS, so each tile is read from
 //    L2 once per 8 queries; the causal limit is per query.
@@ -24,7 +27,6 @@
 #include "internal.h"
 #include "topk_core.h"
 
-#include <algorithm>
 #include <type_traits>
 
 namespace csa2 {

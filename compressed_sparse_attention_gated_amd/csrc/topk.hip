@@ -2,17 +2,20 @@
 // of selected blocks into the hierarchical candidate pool ([CSA2 column]
 // "解码器里的分层索引"; [Evolution blog] §4.4).
 //
-// Scores become order-preserving uint32 keys (-0 maps to +0).  Three histogram passes
-// over 11/11/10-bit digits (LDS histograms, one workgroup per row or row chunk) find the
-// exact k-th largest key T and how many keys equal to T must be taken.  A final pass walks
-// the row in index order; one ballot per wave plus a cross-wave prefix in LDS gives every
-// selected element its output slot, so the output is ascending and ties go to the lower
-// index, deterministically.
+// Scores become order-preserving uint32 keys (-0 maps to +0).  Range-adaptive histogram
+// passes (at most 2048 LDS bins each, over the live key range) find the exact k-th largest
+// key T and how many keys equal to T are taken (topk_core.h).  A compaction then walks the
+// row in index order: per-segment counts, one block scan, and a wave scan inside each
+// segment give every selected element its output slot, so the output is ascending and
+// ties go to the lower index, deterministically.
 //
-// Rows longer than kSingleMax use two levels: chunks of a row are reduced to their own
-// top-k (exact: the global top-k is contained in the union of the chunks' top-k), written
-// as (key, slot) pairs in index order, then a second pass selects from the pairs; slot
-// order of the pairs equals index order, so the tie rule carries over.
+// Rows of up to 16,384 keys are loaded from their scores straight into registers and
+// selected there (the LDS holds only histograms); longer rows up to kSingleMax are staged
+// in LDS or read from global memory.  Rows longer than kSingleMax use two levels: chunks of
+// a row are reduced to their own top-k (exact: the global top-k is contained in the union
+// of the chunks' top-k), written as (key, slot) pairs in index order, then topk_merge
+// selects from the pairs, pruned by each chunk's first-pass bound; slot order of the pairs
+// equals index order, so the tie rule carries over.
 
 #include "common.h"
 #include "internal.h"

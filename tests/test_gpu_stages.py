@@ -176,6 +176,26 @@ def test_index_ties_and_zeros(C):
     _check_full(C, d, np.array([[2000]], np.int32), 1, 300, what="ties")
 
 
+def test_index_topk_row_paths(C):
+    banner("index FULL top-512 per query: register rows at 16,384 keys, LDS rows past it, short rows")
+    g = W.rng(21)
+    # 8 queries of one sequence (not the fused decode path): rows of n_vis = t entries
+    d = W.indexer_inputs(g, 1, 8, 16400, 64, 128, (1.0, -1.0, 0.5, -0.5))
+    q_pos = np.array([[16384, 16385, 16400, 513, 5000, 512, 1, 0]], np.int32)
+    _check_full(C, d, q_pos, 1, 512, what="row lengths around the register capacity")
+    # heavy ties in a full register row
+    d = W.indexer_inputs(g, 1, 8, 16384, 64, 128, (1.0, -1.0), lo=0, hi=1)
+    _check_full(C, d, np.full((1, 8), 16384, np.int32), 1, 512, what="ties, 16,384 keys")
+
+
+def test_index_topk_many_rows(C):
+    banner("index FULL top-128 for 256 queries of 3000 entries (many-row register launch)")
+    g = W.rng(22)
+    d = W.indexer_inputs(g, 1, 256, 3000, 32, 64, (1.0, -0.5))
+    q_pos = np.sort(np.random.default_rng(5).integers(0, 3200, size=(1, 256))).astype(np.int32)
+    _check_full(C, d, q_pos, 1, 128, what="many rows")
+
+
 def test_reindex_reuse_and_hier(C):
     banner("hier pool + REINDEX + REUSE: B=2 N=20000, 64 blocks kept, k=128")
     g = W.rng(15)
