@@ -221,11 +221,12 @@ struct MfmaSmem {
   // and the bf16 output tile ([32][512]) after it
   alignas(16) uint8_t tile[2][kTile * kPitch];
   alignas(16) uint16_t pbuf[kHG][kPPitch];  // P in PV A-operand order (bf16)
-  float wmax[2][kHG];                       // per row half: tile max per head
+  float wmax[2][kHG];                       // per row half: tile max per head (first valid tile)
+  float omax[2][kHG];                       // per row half: tile max per head (overflow check)
   float lpart[2][kHG];                      // per row half: sum of p per head
   float mfin[kHG];
   float rope_c[64], rope_s[64];             // cos/sin of the query position, per frequency
-  int ovf[4];                               // per wave: a head overflowed its reference
+  alignas(16) int ovf[4];                   // per wave: a head overflowed its reference
   int src[kMaxSplitTiles * kTile];          // per slot: >= 0 kv entry id, -2-w window row w, -1 empty
 };
 static_assert(sizeof(MfmaSmem) <= 80 * 1024, "two workgroups per CU");
@@ -240,19 +241,32 @@ struct Prefetch {
   uint32_t fs[kFP4 ? 2 : 1];
 };
 
-// slot -> row source, for the slots [slot0, slot0 + n) of this split
-__device__ __forceinline__ void stage_slots(const AttnDev& a, int row, int slot0, int n, int R,
-                                            const WinRange& wr, int* src) {
-  for (int i = threadIdx.x; i < n; i += kThreadsM) {
+// Slot -> row source for this split's slots [slot0, slot0 + n): index slot s < k holds its
+// entry id (-1 if empty or out of range), slot k + w window row lo_row + w as -2 - row,
+// slots past R are empty.  The index slots do not depend on the query position, so their
+// ids are loaded first (ids_of_split) and only combined with the window here.
+constexpr int kSlotsPerThread = kMaxSplitTiles * kTile / kThreadsM;
+static_assert(kMaxSplitTiles * kTile == kSlotsPerThread * kThreadsM, "slot ids per thread");
+__device__ __forceinline__ void ids_of_split(const AttnDev& a, int row, int slot0, int n,
+                                             int (&ids)[kSlotsPerThread]) {
+#pragma unroll
+  for (int u = 0; u < kSlotsPerThread; ++u) {
+    const int i = threadIdx.x + kThreadsM * u;
+    const int s = slot0 + i;
+    ids[u] = (i < n && s < a.k) ? a.idx[(size_t)row * a.k + s] : -1;
+  }
+}
+__device__ __forceinline__ void stage_slots(const AttnDev& a, int slot0, int n, int R, const WinRange& wr,
+                                            const int (&ids)[kSlotsPerThread], int* src) {
+#pragma unroll
+  for (int u = 0; u < kSlotsPerThread; ++u) {
+    const int i = threadIdx.x + kThreadsM * u;
+    if (i >= n) break;
     const int s = slot0 + i;
     int v = -1;
     if (s < R) {
-      if (s < a.k) {
-        const int e = a.idx[(size_t)row * a.k + s];
-        v = (e >= 0 && e < a.N) ? e : -1;
-      } else {
-        v = -2 - (wr.lo_row + (s - a.k));
-      }
+      if (s < a.k) v = (ids[u] >= 0 && ids[u] < a.N) ? ids[u] : -1;
+      else v = -2 - (wr.lo_row + (s - a.k));
     }
     src[i] = v;
   }
@@ -365,23 +379,25 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int hq = wave & 1, mr = wave >> 1;
-  const int t_pos = a.q_pos[row];
-  const WinRange wr = window_of(a, b, t_pos);
-  const int R = a.k + wr.cnt;
-  const int n_tiles = (R + kTile - 1) / kTile;
   const int tile0 = split * a.tiles_per_split;
-  const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
   const int rope_lo = kC - a.rope_dims;
   const int head0 = hg * kHG;
   const RowBases rb = row_bases(a, b);
 
-  // ---- every global load of the prologue at once: this split's slot ids, and the q rows
-  // ---- of this wave's 8 heads
+  // ---- every global load of the prologue at once: the q rows of this wave's 8 heads, the
+  // ---- split's index slots, the query position
   uint4 qraw[8];
 #pragma unroll
   for (int hh = 0; hh < 8; ++hh)
     qraw[hh] = *reinterpret_cast<const uint4*>((const uint16_t*)a.q + ((size_t)row * a.H + head0 + 8 * wave + hh) * kC + 8 * lane);
-  if (tile0 < tile1) stage_slots(a, row, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, sm.src);
+  int ids[kSlotsPerThread];
+  ids_of_split(a, row, tile0 * kTile, a.tiles_per_split * kTile, ids);
+  const int t_pos = a.q_pos[row];
+  const WinRange wr = window_of(a, b, t_pos);
+  const int R = a.k + wr.cnt;
+  const int n_tiles = (R + kTile - 1) / kTile;
+  const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
+  if (tile0 < tile1) stage_slots(a, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, ids, sm.src);
   stage_rope(a, t_pos, sm.rope_c, sm.rope_s);
   lds_barrier();
   // rows of the first tile start travelling while q_hat is formed
@@ -477,12 +493,19 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
         valid[j] = (vm >> (4 * g + j)) & 1u;
         if (valid[j]) tmax = fmaxf(tmax, sacc[j]);
       }
-      tmax = rows_max(tmax);
-      if (g == 0) sm.wmax[mr][my_head] = tmax;
-      lds_barrier();
-      tmax = fmaxf(sm.wmax[0][my_head], sm.wmax[1][my_head]);  // whole 32-row tile
-      if (m_use == -INFINITY) m_use = tmax;  // first valid tile of this head: O is still 0
+      tmax = rows_max(tmax);  // this wave's 16 rows
+      // The reference is fixed by the first tile holding a valid row, the max over all 32
+      // of its rows (exchanged between the two row halves).  Validity is per row, the same
+      // for every head, so the branch is uniform over the workgroup.  Later tiles only
+      // check their own half against it; the overflow flag is exchanged with P below.
+      if (m_use == -INFINITY) {
+        if (g == 0) sm.wmax[mr][my_head] = tmax;
+        lds_barrier();
+        tmax = fmaxf(sm.wmax[0][my_head], sm.wmax[1][my_head]);
+        m_use = tmax;  // O is still 0
+      }
       const bool ovf = tmax > m_use + kOverflow;
+      if (g == 0) sm.omax[mr][my_head] = tmax;
       float p[4];
       float psum = 0.f;
 #pragma unroll
@@ -496,9 +519,10 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
           make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       if (lane == 0) sm.ovf[wave] = __ballot(ovf) != 0;
       lds_barrier();
-      if (__builtin_amdgcn_readfirstlane(sm.ovf[0] | sm.ovf[1] | sm.ovf[2] | sm.ovf[3])) {
+      const int4 ov = *reinterpret_cast<const int4*>(sm.ovf);
+      if (__builtin_amdgcn_readfirstlane(ov.x | ov.y | ov.z | ov.w)) {
         overflow = true;
-        m_use = fmaxf(m_use, tmax);
+        m_use = fmaxf(m_use, fmaxf(sm.omax[0][my_head], sm.omax[1][my_head]));  // whole tile
         break;
       }
 

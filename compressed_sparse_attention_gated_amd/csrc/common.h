@@ -123,14 +123,33 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
 }
-// sum / max over the 4 lanes l, l^16, l^32, l^48 (the four 16-lane rows)
+// gfx950 VALU lane swaps, no LDS round trip.  v_permlane16_swap exchanges the odd 16-lane
+// rows of one register with the even rows of another, v_permlane32_swap the upper half of
+// one with the lower half of the other.  Given two copies of v, each lane gets back its own
+// value and that of lane l ^ 16 (or l ^ 32), in an order that depends on the lane, so they
+// serve symmetric reductions only (a + b == b + a exactly, likewise max).
+__device__ __forceinline__ void pair_xor16(float v, float* a, float* b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_xor32(float v, float* a, float* b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+// sum / max over the 4 lanes l, l^16, l^32, l^48 (the four 16-lane rows); every lane active
 __device__ __forceinline__ float rows_sum(float v) {
-  v += swz_xor16(v);
-  return v + xor32(v);
+  float a, b;
+  pair_xor16(v, &a, &b);
+  pair_xor32(a + b, &a, &b);
+  return a + b;
 }
 __device__ __forceinline__ float rows_max(float v) {
-  v = fmaxf(v, swz_xor16(v));
-  return fmaxf(v, xor32(v));
+  float a, b;
+  pair_xor16(v, &a, &b);
+  pair_xor32(fmaxf(a, b), &a, &b);
+  return fmaxf(a, b);
 }
 // sum over aligned groups of G lanes (G a power of two <= 64)
 template <int G>
