@@ -152,6 +152,37 @@ def compress(c_a, z_a, m, *, b_a=None, c_b=None, z_b=None, b_b=None, overlap=Fal
     return out, k_index
 
 
+def write_cache(entries, k_index, dst_row, n_rows):
+    """The write path into a decode cache: [CSA2 column] "890 字节是怎么来的" stores each
+    main-KV entry in 4 bits (E2M1 codes, one E4M3 scale per 16 channels) and the indexer
+    key in MXFP4 (E2M1 codes, one E8M0 scale per 32 dims); [Evolution blog] §4.1 writes
+    an entry after its norm and position encoding, then quantises it.  `entries` [ne, c]
+    and `k_index` [ne, d] (or None) are what `compress` returns; entry i lands in cache
+    row dst_row + i, rows outside [0, n_rows) are dropped, untouched rows stay zero.
+    The rounding rule (nearest, ties to the even code) is the one in `formats`.
+    Returns (codes [n_rows, c/2], scales [n_rows, c/16], ik_codes [n_rows, d/2] or None,
+    ik_scales [n_rows, d/32] or None)."""
+    from . import formats as F
+
+    e = np.asarray(entries, np.float64)
+    ne, c = e.shape
+    codes = np.zeros((n_rows, c // 2), np.uint8)
+    scales = np.zeros((n_rows, c // F.MAIN_KV_GROUP), np.uint8)
+    ik_codes = ik_scales = None
+    if k_index is not None:
+        d = np.asarray(k_index).shape[1]
+        ik_codes = np.zeros((n_rows, d // 2), np.uint8)
+        ik_scales = np.zeros((n_rows, d // F.MX_GROUP), np.uint8)
+    for i in range(ne):
+        r = dst_row + i
+        if not 0 <= r < n_rows:
+            continue
+        codes[r], scales[r] = F.quantize_fp4_main(e[i])
+        if k_index is not None:
+            ik_codes[r], ik_scales[r] = F.quantize_mxfp4(np.asarray(k_index[i], np.float64))
+    return codes, scales, ik_codes, ik_scales
+
+
 # ============================================================ causal rule
 def n_visible(t, n_entries, m):
     """Compressed entry j (tokens [m*j, m*j+m)) is visible to query position t iff
@@ -313,7 +344,7 @@ def sparse_attn(q, q_pos, kv, idx, win=None, win_pos0=None, window=128, sink=Non
 
 
 __all__ = [
-    "gated_pool", "gated_pool_weights", "rms_norm", "rope_angles", "rope", "compress",
+    "gated_pool", "gated_pool_weights", "rms_norm", "rope_angles", "rope", "compress", "write_cache",
     "n_visible", "indexer_scores", "topk_indices", "index_topk_full", "block_max",
     "hier_candidates", "reindex_topk", "reindex_topk_masked", "reuse", "window_rows",
     "attend_one", "sparse_attn",

@@ -441,3 +441,70 @@ def test_generators_are_seeded():
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
     assert set(np.unique(a["k_idx"])) <= set(range(-3, 4))
+
+
+# =================================================================== write path
+def test_cache_rounding_hand_values():
+    g = G.load("ocp_rounding.txt")
+    for tok in g["e2m1_rne"].split():
+        x, code = tok.split(":")
+        assert F.e2m1_encode(np.array([float(x)]))[0] == int(code), tok
+    for tok in g["e4m3_scale"].split():
+        a, byte = tok.split(":")
+        x = np.zeros(16)
+        x[5] = -float(a)  # the sign of the largest value does not matter
+        _, sc = F.quantize_fp4_main(x)
+        assert sc[0] == int(byte, 0), tok
+    for tok in g["mx_scale"].split():
+        a, byte = tok.split(":")
+        x = np.zeros(32)
+        x[7] = float(a)
+        _, sc = F.quantize_mxfp4(x)
+        assert sc[0] == int(byte), tok
+    for key in ("mx_group_amax6", "mx_group_amax3.99"):
+        pairs = [t.split(":") for t in g[key].split()]
+        x = np.zeros(32)
+        x[:len(pairs)] = [float(v) for v, _ in pairs]
+        codes, _ = F.quantize_mxfp4(x)
+        nib = F.unpack_nibbles(codes)
+        assert list(nib[:len(pairs)]) == [int(c) for _, c in pairs], key
+
+
+@pytest.mark.parametrize("m,overlap", [(1, False), (2, False), (2, True)])
+def test_write_cache_streaming_equals_bulk(m, overlap):
+    # A decode step appends one entry per completed block at the cache's length; the cache
+    # it builds equals the one written from the whole sequence at once (each entry depends
+    # only on its block and, with overlap, the block before: [DSA-to-CSA notes] eq. (11)-(12)).
+    r = _rng(31 + m + overlap)
+    n, c, d = 10, 64, 32
+    ca, za, cb, zb = (r.standard_normal((n, c)) for _ in range(4))
+    w_ik = r.standard_normal((c, d)) / 8
+    kw = dict(norm=True, rope_dims=16, w_ik=w_ik)
+    if overlap:
+        kw.update(c_b=cb, z_b=zb, overlap=True)
+    ent, kix = O.compress(ca, za, m, **kw)
+    n_rows = n // m + 2
+    bulk = O.write_cache(ent, kix, 0, n_rows)
+    stream = [np.zeros_like(p) for p in bulk]
+    for i in range(n // m):
+        lo = m * max(i - 1, 0)  # the open block plus, with overlap, the block before
+        sl = slice(lo, m * (i + 1))
+        kwi = dict(kw)
+        if overlap:
+            kwi.update(c_b=cb[sl], z_b=zb[sl])
+        e_i, k_i = O.compress(ca[sl], za[sl], m, pos0=lo, **kwi)
+        np.testing.assert_allclose(e_i[-1], ent[i], rtol=0, atol=1e-12)
+        part = O.write_cache(e_i[-1:], k_i[-1:], i, n_rows)
+        for s_, p_ in zip(stream, part):
+            s_[i] = p_[i]
+    for s_, b_ in zip(stream, bulk):
+        np.testing.assert_array_equal(s_, b_)
+    # rows past the entries stay zero; out-of-range destinations are dropped
+    assert not bulk[0][n // m:].any() and not bulk[1][n // m:].any()
+    tail = O.write_cache(ent, kix, n_rows - 1, n_rows)
+    np.testing.assert_array_equal(tail[0][n_rows - 1], bulk[0][0])
+    assert not tail[0][:n_rows - 1].any()
+    # dequantised rows are within one scale unit of the entries
+    deq = F.fp4_main_decode(bulk[0][:n // m], bulk[1][:n // m])
+    step = np.repeat(F.e4m3_decode(bulk[1][:n // m]), 16, axis=-1)
+    assert np.all(np.abs(deq - ent) <= step + 1e-12)
