@@ -27,7 +27,9 @@ class CompressDesc(C.Structure):
                 ("ca", _vp), ("za", _vp), ("cb", _vp), ("zb", _vp), ("ba", _vp), ("bb", _vp),
                 ("pos0", _vp), ("norm", _i), ("eps", _f), ("rope_dims", _i), ("rope_theta", _f),
                 ("out", _vp), ("out_batch_stride", _i64), ("w_ik", _vp), ("d_index", _i),
-                ("out_ik", _vp), ("out_ik_batch_stride", _i64)]
+                ("out_ik", _vp), ("out_ik_batch_stride", _i64), ("dst_row", _vp),
+                ("out_codes", _vp), ("out_scales", _vp), ("ik_codes", _vp), ("ik_scales", _vp),
+                ("q_rows", _i64), ("cb0", _vp), ("zb0", _vp)]
 
 
 class IndexDesc(C.Structure):
@@ -130,23 +132,37 @@ def version() -> int:
 # ---------------------------------------------------------------------------- compress
 def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, norm=True,
                   eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None, w_ik=None, out_ik=None,
-                  stream=None):
-    """ca, za (cb, zb): [B, n, c] fp32/bf16 -> (out [B, n//m, c], out_ik [B, n//m, d_I] or None)."""
+                  dst_row=None, out_codes=None, out_scales=None, ik_codes=None, ik_scales=None,
+                  cb0=None, zb0=None, plain_out=True, stream=None):
+    """ca, za (cb, zb): [B, n, c] fp32/bf16 -> (out [B, n//m, c], out_ik [B, n//m, d_I] or None).
+
+    Write path: out_codes / out_scales [B, rows, c/2] / [B, rows, c/16] (FP4 entries) and
+    ik_codes / ik_scales [B, rows, d_I/2] / [B, rows, d_I/32] (MXFP4 K_I), entry i of
+    sequence b at row dst_row[b] + i; cb0 / zb0 [B, m, c]: with overlap, the history rows of
+    entry 0 (the block before it).  With plain_out=False and quantised planes given, the
+    plain outputs are not allocated (returned as None) unless passed."""
     B, n, c = ca.shape
     ne = n // m
-    if out is None:
+    q_rows = 0
+    for t in (out_codes, ik_codes):
+        if t is not None:
+            q_rows = t.shape[1]
+    if out is None and (plain_out or out_codes is None):
         out = torch.empty((B, ne, c), dtype=ca.dtype, device=ca.device)
     d_index = 0
     if w_ik is not None:
         d_index = w_ik.shape[1]
-        if out_ik is None:
+        if out_ik is None and (plain_out or ik_codes is None):
             out_ik = torch.empty((B, ne, d_index), dtype=ca.dtype, device=ca.device)
     d = CompressDesc(B=B, n=n, c=c, m=m, overlap=int(cb is not None), dtype=_DT[ca.dtype],
                      ca=_p(ca), za=_p(za), cb=_p(cb), zb=_p(zb), ba=_p(ba), bb=_p(bb), pos0=_p(pos0),
                      norm=int(norm), eps=eps, rope_dims=rope_dims, rope_theta=rope_theta, out=_p(out),
-                     out_batch_stride=out.stride(0) if out.dim() == 3 else 0, w_ik=_p(w_ik),
-                     d_index=d_index, out_ik=_p(out_ik),
-                     out_ik_batch_stride=out_ik.stride(0) if out_ik is not None else 0)
+                     out_batch_stride=out.stride(0) if out is not None and out.dim() == 3 else 0,
+                     w_ik=_p(w_ik), d_index=d_index, out_ik=_p(out_ik),
+                     out_ik_batch_stride=out_ik.stride(0) if out_ik is not None else 0,
+                     dst_row=_p(dst_row), out_codes=_p(out_codes), out_scales=_p(out_scales),
+                     ik_codes=_p(ik_codes), ik_scales=_p(ik_scales), q_rows=q_rows, cb0=_p(cb0),
+                     zb0=_p(zb0))
     _check(lib().csa2_compress(C.byref(d), _stream(stream)))
     return out, out_ik
 

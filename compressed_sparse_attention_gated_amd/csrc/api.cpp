@@ -127,17 +127,31 @@ static int check_compress(const csa2_compress_desc* d) {
   if (d->norm && !(d->eps >= 0.f)) return fail(CSA2_ERR_INVALID, "compress: eps must be >= 0");
   const long long n_ent = (long long)d->B * (d->n / d->m);
   if (n_ent == 0) return CSA2_OK;
-  if (!d->ca || !d->za || !d->out) return fail(CSA2_ERR_INVALID, "compress: ca, za and out are required");
+  if (!d->ca || !d->za) return fail(CSA2_ERR_INVALID, "compress: ca and za are required");
+  if (!d->out && !d->out_codes) return fail(CSA2_ERR_INVALID, "compress: out or out_codes is required");
+  if (!d->out_codes != !d->out_scales)
+    return fail(CSA2_ERR_INVALID, "compress: out_codes and out_scales go together");
+  if (d->out_codes && d->c % 16 != 0)
+    return fail(CSA2_ERR_UNSUPPORTED, "compress: FP4 planes need c %% 16 == 0");
+  if (!d->ik_codes != !d->ik_scales) return fail(CSA2_ERR_INVALID, "compress: ik_codes and ik_scales go together");
+  if (d->ik_codes && !d->w_ik) return fail(CSA2_ERR_INVALID, "compress: ik_codes need w_ik");
+  if (d->q_rows < 0) return fail(CSA2_ERR_INVALID, "compress: q_rows must be >= 0");
   if (d->overlap && (!d->cb || !d->zb)) return fail(CSA2_ERR_INVALID, "compress: overlap needs cb and zb");
+  if (!d->cb0 != !d->zb0) return fail(CSA2_ERR_INVALID, "compress: cb0 and zb0 go together");
+  if (d->cb0 && !d->overlap) return fail(CSA2_ERR_INVALID, "compress: cb0 and zb0 need overlap");
   if (d->w_ik) {
-    if (!d->out_ik) return fail(CSA2_ERR_INVALID, "compress: w_ik needs out_ik");
+    if (!d->out_ik && !d->ik_codes) return fail(CSA2_ERR_INVALID, "compress: w_ik needs out_ik or ik_codes");
     if (d->d_index != 32 && d->d_index != 64 && d->d_index != 128)
       return fail(CSA2_ERR_UNSUPPORTED, "compress: d_index must be 32, 64 or 128");
   }
   const int64_t n_per = d->n / d->m;
-  if (d->out_batch_stride != 0 && d->out_batch_stride < n_per * d->c)
+  if (d->out_batch_stride != 0 && d->out_batch_stride < d->c)
+    return fail(CSA2_ERR_INVALID, "compress: out_batch_stride smaller than one row");
+  if (!d->dst_row && d->out_batch_stride != 0 && d->out_batch_stride < n_per * d->c)
     return fail(CSA2_ERR_INVALID, "compress: out_batch_stride smaller than (n/m)*c");
-  if (d->w_ik && d->out_ik_batch_stride != 0 && d->out_ik_batch_stride < n_per * d->d_index)
+  if (d->w_ik && d->out_ik_batch_stride != 0 && d->out_ik_batch_stride < d->d_index)
+    return fail(CSA2_ERR_INVALID, "compress: out_ik_batch_stride smaller than one row");
+  if (!d->dst_row && d->w_ik && d->out_ik_batch_stride != 0 && d->out_ik_batch_stride < n_per * d->d_index)
     return fail(CSA2_ERR_INVALID, "compress: out_ik_batch_stride smaller than (n/m)*d_index");
   return CSA2_OK;
 }

@@ -48,6 +48,65 @@ struct Ld<uint16_t> {
   static __device__ __forceinline__ void store1(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
 };
 
+// ------------------------------------------------------------------ cache quantisers
+// Every rounding decision below compares a value with a threshold times its scale, and
+// each such product is exact in fp32 (at most 8 significant bits), so the bytes written
+// are the exact round-to-nearest-even of the fp32 entry values: bit-for-bit what any
+// exact implementation of the same rule gives for the same inputs.
+//
+// E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} (codes 0..7): the midpoints between
+// neighbours are the thresholds; at a midpoint the even code wins.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float scale) {
+  const float a = fabsf(x);
+  constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t code = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    const float t = kMid[k] * scale;
+    code += (a > t) ? 1u : 0u;
+    if (k & 1) code += (a == t) ? 1u : 0u;  // tie between codes k and k+1: k+1 is even
+  }
+  return (x < 0.f && code != 0) ? (code | 8u) : code;
+}
+// value of a non-negative OCP E4M3FN byte (0x00..0x7e)
+__device__ __forceinline__ float e4m3_value(int b) {
+  const int e = b >> 3, m = b & 7;
+  return e ? __builtin_amdgcn_ldexpf((float)(8 + m), e - 10) : __builtin_amdgcn_ldexpf((float)m, -9);
+}
+// E4M3 byte nearest to amax / 6 (ties to the even byte, saturating at 448): the largest
+// byte whose value times 6 is <= amax, then the midpoint test against its successor
+__device__ __forceinline__ int e4m3_scale_byte(float amax) {
+  int lo = 0, hi = 0x7e;
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    const int mid = (lo + hi + 1) >> 1;
+    const bool le = 6.0f * e4m3_value(mid) <= amax;
+    lo = le ? mid : lo;
+    hi = le ? hi : mid - 1;
+  }
+  if (lo >= 0x7e) return 0x7e;
+  const float t = 3.0f * (e4m3_value(lo) + e4m3_value(lo + 1));  // 6 x midpoint
+  if (amax > t) return lo + 1;
+  if (amax < t) return lo;
+  return (lo & 1) ? lo + 1 : lo;
+}
+// MXFP4 shared exponent of a group with max magnitude amax > 0: floor(log2 amax) - 2,
+// clamped to [-127, 127] (read off the fp32 exponent; subnormal amax gives -127)
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int E = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return E == 0 ? -127 : max(E - 129, -127);
+}
+// max over aligned groups of 32 lanes
+__device__ __forceinline__ float max32(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  float a, b;
+  pair_xor16(v, &a, &b);
+  return fmaxf(a, b);
+}
+
 // online per-channel softmax accumulation of one token row (8 channels)
 __device__ __forceinline__ void accum8(float* mx, float* den, float* acc, const float* z, const float* cv) {
 #pragma unroll
@@ -64,10 +123,14 @@ __device__ __forceinline__ void accum8(float* mx, float* den, float* acc, const 
 template <typename T, int G, int kDI>
 __global__ void __launch_bounds__(kThreads) compress_kernel(
     int n, int c, int m, int overlap, const T* __restrict__ ca, const T* __restrict__ za,
-    const T* __restrict__ cb, const T* __restrict__ zb, const float* __restrict__ ba,
+    const T* __restrict__ cb, const T* __restrict__ zb, const T* __restrict__ cb0,
+    const T* __restrict__ zb0, const float* __restrict__ ba,
     const float* __restrict__ bb, const int32_t* __restrict__ pos0, int norm, float eps,
-    int rope_dims, RopeFreq rope, T* __restrict__ out, int64_t out_bstride,
-    const T* __restrict__ w_ik, int d_index, T* __restrict__ out_ik, int64_t out_ik_bstride) {
+    int rope_dims, RopeFreq rope, T* __restrict__ out, int64_t out_bstride, int64_t out_cap,
+    const T* __restrict__ w_ik, int d_index, T* __restrict__ out_ik, int64_t out_ik_bstride,
+    int64_t ik_cap, const int32_t* __restrict__ dst_row, uint8_t* __restrict__ out_codes,
+    uint8_t* __restrict__ out_scales, uint8_t* __restrict__ ik_codes, uint8_t* __restrict__ ik_scales,
+    int64_t q_rows) {
   constexpr bool kProj = kDI > 0;
   extern __shared__ float xs[];  // [kRowsPerWG][c] pre-RoPE normalised entries (kProj only)
   const int n_ent = n / m;
@@ -78,6 +141,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
   constexpr int kRowsPerPass = kThreads / G;
   const int ch = lane_in_row * 8;
   const size_t seq_off = (size_t)b * n * c;
+  const int64_t dst0 = dst_row ? (int64_t)dst_row[b] : 0;  // output row of entry 0
 
   for (int lr = row_slot; lr < kRowsPerWG; lr += kRowsPerPass) {
     const int i = row0 + lr;
@@ -95,11 +159,15 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
       }
       accum8(mx, den, acc, z, cv);
     }
-    if (overlap && i > 0) {  // entry 0 has no history: its -inf logits carry zero weight
+    // history: the previous block's b-branch rows; entry 0 takes them from cb0 / zb0 when
+    // given, else it has none (its -inf logits carry zero weight)
+    if (overlap && (i > 0 || cb0)) {
+      const T* hc = i > 0 ? cb + seq_off + (size_t)m * (i - 1) * c : cb0 + (size_t)b * m * c;
+      const T* hz = i > 0 ? zb + seq_off + (size_t)m * (i - 1) * c : zb0 + (size_t)b * m * c;
       for (int j = 0; j < m; ++j) {
-        const size_t off = seq_off + (size_t)(m * (i - 1) + j) * c + ch;
-        Ld<T>::load8(zb + off, z);
-        Ld<T>::load8(cb + off, cv);
+        const size_t off = (size_t)j * c + ch;
+        Ld<T>::load8(hz + off, z);
+        Ld<T>::load8(hc + off, cv);
         if (bb) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) z[e] += bb[j * c + ch + e];
@@ -137,7 +205,27 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
         }
       }
     }
-    Ld<T>::store8(out + (size_t)b * out_bstride + (size_t)i * c + ch, y);
+    const int64_t r_out = dst0 + i;
+    if (out && r_out >= 0 && r_out < out_cap) Ld<T>::store8(out + (size_t)b * out_bstride + (size_t)r_out * c + ch, y);
+    if (out_codes) {
+      // FP4 entry: 16-channel groups are lane pairs of the row
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
+      am = fmaxf(am, dpp<kDppXor1>(am));
+      const int sb = e4m3_scale_byte(am);
+      const float sc = e4m3_value(sb);
+      uint32_t word = 0;
+      if (sc > 0.f) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) word |= e2m1_code(y[e], sc) << (4 * e);
+      }
+      if (r_out >= 0 && r_out < q_rows) {
+        const size_t qr = (size_t)b * q_rows + r_out;
+        *reinterpret_cast<uint32_t*>(out_codes + qr * (c / 2) + ch / 2) = word;
+        if ((lane_in_row & 1) == 0) out_scales[qr * (c / 16) + ch / 16] = (uint8_t)sb;
+      }
+    }
   }
 
   if (kProj) {
@@ -159,7 +247,22 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
 #pragma unroll
     for (int r = 0; r < kRowsPerGroup; ++r) {
       const int i = row0 + rg * kRowsPerGroup + r;
-      if (i < n_ent) Ld<T>::store1(out_ik + (size_t)b * out_ik_bstride + (size_t)i * kDIc + d, accp[r]);
+      const int64_t r_out = dst0 + i;
+      if (out_ik && i < n_ent && r_out >= 0 && r_out < ik_cap)
+        Ld<T>::store1(out_ik + (size_t)b * out_ik_bstride + (size_t)r_out * kDIc + d, accp[r]);
+      if (ik_codes) {
+        // MXFP4: a 32-value group is an aligned half of the wave (d = lane % 32 + 32 j);
+        // neighbouring lanes' codes are gathered so each even lane stores one byte
+        const float am = max32(fabsf(accp[r]));
+        const int e = am > 0.f ? mx_exponent(am) : 0;
+        const uint32_t code = am > 0.f ? e2m1_code(__builtin_amdgcn_ldexpf(accp[r], -e), 1.0f) : 0u;
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, kDppXor1, 0xF, 0xF, false);
+        if (i < n_ent && r_out >= 0 && r_out < q_rows) {
+          const size_t qr = (size_t)b * q_rows + r_out;
+          if ((d & 1) == 0) ik_codes[qr * (kDIc / 2) + d / 2] = (uint8_t)(code | (hi << 4));
+          if ((d & 31) == 0) ik_scales[qr * (kDIc / 32) + d / 32] = (uint8_t)(e + 127);
+        }
+      }
     }
   }
 }
@@ -170,13 +273,17 @@ hipError_t launch_t(const csa2_compress_desc& d, hipStream_t s) {
   dim3 grid((n_ent + kRowsPerWG - 1) / kRowsPerWG, d.B);
   const int64_t ob = d.out_batch_stride ? d.out_batch_stride : (int64_t)n_ent * d.c;
   const int64_t oib = d.out_ik_batch_stride ? d.out_ik_batch_stride : (int64_t)n_ent * d.d_index;
+  const int64_t out_cap = ob / d.c, ik_cap = d.d_index ? oib / d.d_index : 0;
+  const int64_t q_rows = d.q_rows ? d.q_rows : (int64_t)n_ent;
   const size_t lds = kDI > 0 ? (size_t)kRowsPerWG * d.c * sizeof(float) : 0;
   RopeFreq rope;
   rope_freq_host(&rope, d.rope_dims, d.rope_theta);
   hipLaunchKernelGGL((compress_kernel<T, G, kDI>), grid, dim3(kThreads), lds, s, d.n, d.c, d.m,
-                     d.overlap, (const T*)d.ca, (const T*)d.za, (const T*)d.cb, (const T*)d.zb, d.ba,
-                     d.bb, d.pos0, d.norm, d.eps, d.rope_dims, rope, (T*)d.out, ob,
-                     (const T*)d.w_ik, d.d_index, (T*)d.out_ik, oib);
+                     d.overlap, (const T*)d.ca, (const T*)d.za, (const T*)d.cb, (const T*)d.zb,
+                     (const T*)d.cb0, (const T*)d.zb0, d.ba,
+                     d.bb, d.pos0, d.norm, d.eps, d.rope_dims, rope, (T*)d.out, ob, out_cap,
+                     (const T*)d.w_ik, d.d_index, (T*)d.out_ik, oib, ik_cap, d.dst_row,
+                     d.out_codes, d.out_scales, d.w_ik ? d.ik_codes : nullptr, d.ik_scales, q_rows);
   return hipGetLastError();
 }
 
@@ -210,7 +317,9 @@ hipError_t launch_dt(const csa2_compress_desc& d, hipStream_t s) {
 hipError_t launch_compress(const csa2_compress_desc& d, hipStream_t s) {
   if (d.n / d.m == 0) return hipSuccess;
   // every pointer a kernel dereferences must be set
-  if (!d.ca || !d.za || !d.out || (d.overlap && (!d.cb || !d.zb)) || (d.w_ik && !d.out_ik))
+  if (!d.ca || !d.za || (!d.out && !d.out_codes) || (d.overlap && (!d.cb || !d.zb)) ||
+      (d.w_ik && !d.out_ik && !d.ik_codes) || (!d.out_codes != !d.out_scales) ||
+      (!d.ik_codes != !d.ik_scales) || (d.out_codes && d.c % 16 != 0) || (!d.cb0 != !d.zb0))
     return hipErrorInvalidValue;
   ScopedProf p(s, "compress");
   return d.dtype == CSA2_F32 ? launch_dt<float>(d, s) : launch_dt<uint16_t>(d, s);

@@ -87,8 +87,33 @@ typedef enum {
  *   pos0: int32 [B] position of token 0 of each sequence, or NULL (= 0).
  *   out: [B, n/m, c] at out + b*out_batch_stride (elements; 0 means (n/m)*c).
  *   w_ik: [c, d_index] or NULL; out_ik: [B, n/m, d_index] (batch stride out_ik_batch_stride,
- *     0 means (n/m)*d_index), required iff w_ik.
- * Supported: c/8 a power of two, 8 <= c <= 512; rope_dims even and <= c.
+ *     0 means (n/m)*d_index).
+ * Write path into the decode cache (the 4-bit cache rows of [CSA2 column], "890 字节是怎么来的":
+ * 512 main-KV channels in 288 bytes, 128 indexer-K dims in 68 bytes; [Evolution blog] §4.1
+ * stores an entry after its norm and position encoding, then quantised):
+ *   dst_row: int32 [B] or NULL (= 0).  Entry i of sequence b goes to row dst_row[b] + i of
+ *     every output buffer, so a decode step appends its new entry at the cache's length.
+ *     For m > 1 the caller keeps the tokens of the open block and calls with the block once
+ *     it is complete; with overlap it passes the previous block's C^b, Z^b rows as cb0, zb0.
+ *   cb0, zb0: [B, m, c] of dtype, or NULL: with overlap, the C^b, Z^b rows of the block
+ *     before entry 0, which then pools them as its history like every later entry (NULL:
+ *     entry 0 is the first block of its sequence and has no history).
+ *   out_codes, out_scales: if non-NULL, the entries (after RMSNorm and RoPE) are also
+ *     written as FP4_E4M3 planes, codes [B, q_rows, c/2] and E4M3 scales [B, q_rows, c/16]:
+ *     per 16 channels scale = E4M3(amax / 6) and code = E2M1(x / scale), both rounded to
+ *     nearest with ties to the even code, codes saturated at +-6; scale 0 gives zero codes.
+ *   ik_codes, ik_scales: if non-NULL (with w_ik), K_I is also written as MXFP4 planes,
+ *     codes [B, q_rows, d_index/2] and E8M0 scales [B, q_rows, d_index/32]: per 32 values
+ *     the exponent e = floor(log2 amax) - 2 (clamped to [-127, 127]), code = E2M1(x / 2^e)
+ *     rounded as above; an all-zero group gets scale byte 127 and zero codes.
+ *   q_rows: rows per sequence of the quantised planes (0 = n/m).
+ *   out (and out_ik) may be NULL when the quantised planes are requested instead; at least
+ *   one output of the entries is required, and w_ik needs out_ik or the MXFP4 planes.
+ *   Rows outside an output's capacity (out_batch_stride / c, out_ik_batch_stride / d_index,
+ *   q_rows) or below 0 are not written.  Every rounding decision is exact: the same fp32
+ *   entry values always give the same bytes.
+ * Supported: c/8 a power of two, 8 <= c <= 512 (c % 16 == 0 for FP4 planes); rope_dims even
+ * and <= c.
  */
 typedef struct {
   int B, n, c, m, overlap;
@@ -106,6 +131,11 @@ typedef struct {
   int d_index;
   void *out_ik;
   int64_t out_ik_batch_stride;
+  const int32_t *dst_row;
+  uint8_t *out_codes, *out_scales;
+  uint8_t *ik_codes, *ik_scales;
+  int64_t q_rows;
+  const void *cb0, *zb0;
 } csa2_compress_desc;
 
 CSA2_API int csa2_compress(const csa2_compress_desc *d, void *stream);

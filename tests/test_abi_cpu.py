@@ -95,12 +95,21 @@ def test_compress_validation(L):
         (dict(w_ik=FAKE, d_index=128), csa2.CSA2_ERR_INVALID),  # no out_ik
         (dict(w_ik=FAKE, out_ik=FAKE, d_index=100), csa2.CSA2_ERR_UNSUPPORTED),
         (dict(out_batch_stride=5), csa2.CSA2_ERR_INVALID),
+        # write path into the quantised cache
+        (dict(out=None), csa2.CSA2_ERR_INVALID),  # no output at all
+        (dict(out_codes=FAKE), csa2.CSA2_ERR_INVALID),  # codes without scales
+        (dict(c=8, out_codes=FAKE, out_scales=FAKE), csa2.CSA2_ERR_UNSUPPORTED),  # c % 16
+        (dict(ik_codes=FAKE, ik_scales=FAKE), csa2.CSA2_ERR_INVALID),  # MXFP4 K_I without w_ik
+        (dict(w_ik=FAKE, d_index=128, ik_codes=FAKE), csa2.CSA2_ERR_INVALID),  # no ik_scales
+        (dict(q_rows=-1, out_codes=FAKE, out_scales=FAKE), csa2.CSA2_ERR_INVALID),
+        (dict(cb0=FAKE, zb0=FAKE), csa2.CSA2_ERR_INVALID),  # history without overlap
+        (dict(overlap=1, cb=FAKE, zb=FAKE, cb0=FAKE), csa2.CSA2_ERR_INVALID),  # cb0 without zb0
     ]
     for over, code in cases:
         d = csa2.CompressDesc(**{**base, **over})
         assert L.csa2_compress(C.byref(d), None) == code, (over, csa2.last_error())
     # empty work succeeds without touching the device
-    for over in (dict(B=0), dict(n=1), dict(n=0, ca=None)):
+    for over in (dict(B=0), dict(n=1), dict(n=0, ca=None), dict(n=0, out=None, out_codes=FAKE)):
         d = csa2.CompressDesc(**{**base, **over})
         assert L.csa2_compress(C.byref(d), None) == csa2.CSA2_OK
 
