@@ -244,6 +244,46 @@ def attn_bytes(wl):
     return queries * (wl.k * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2 + wl.k * 4)
 
 
+def write_path_stage(torch, C, wl, d, reps=20):
+    """The write path into the 4-bit decode cache (csa2_compress with FP4 entry planes and
+    the MXFP4 indexer-K projection), timed with HIP events per launch.  Decode workloads
+    append one entry per sequence (m = 1: the new token); the prefill writes every entry of
+    its sequence (m = 2).  Not part of the step: the step's cache is generated directly."""
+    dev = d["q"].device
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    d_I = 128
+    w_ik = (torch.randn((wl.c, d_I), generator=g, device=dev) * wl.c ** -0.5).to(torch.bfloat16)
+    if wl.kind == "prefill":
+        ca, za, m, pos0 = d["ca"], d["za"], wl.m, None
+        what = f"all {wl.n_tokens // wl.m} entries of the {wl.n_tokens}-token sequence (m={wl.m})"
+    else:
+        ca, za, m, pos0 = d["c_new"], d["z_new"], 1, d["q_pos"][:, 0]
+        what = f"one new entry for each of the {wl.B} sequences (m=1), at its cache row"
+    B, n, c = ca.shape
+    ne = n // m
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    planes = dict(out_codes=u8(B, ne, c // 2), out_scales=u8(B, ne, c // 16), ik_codes=u8(B, ne, d_I // 2),
+                  ik_scales=u8(B, ne, d_I // 32))
+
+    def run():
+        C.csa2_compress(ca, za, m, pos0=pos0, rope_dims=wl.rope_dims, w_ik=w_ik, plain_out=False, **planes)
+
+    run()
+    torch.cuda.synchronize()
+    C.csa2_profile_enable(True)
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    recs = C.csa2_profile_collect(1 << 12)
+    C.csa2_profile_enable(False)
+    us = float(np.mean([ms for _, ms in recs])) * 1e3
+    nbytes = B * n * c * 2 * 2 + c * d_I * 2 + B * ne * (c // 2 + c // 16 + d_I // 2 + d_I // 32)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "compress", "what": what + ": RMSNorm, RoPE, K_I projection, FP4 + MXFP4 planes",
+            "avg_us": us, "algorithmic_bytes": nbytes, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -301,6 +341,8 @@ def main():
     stages["attention_total"] = {"ms_per_step": attn_ms, "algorithmic_bytes": ab,
                                  "GB_per_s": ab / (attn_ms * 1e-3) / 1e9,
                                  "frac_hbm": ab / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if wl.kind != "hier":
+        stages["write_path"] = write_path_stage(torch, C, wl, insts[0])
     prefill = wl.kind == "prefill"
     units = wl.n_tokens if prefill else wl.B
     value = units / (ms * 1e-3)

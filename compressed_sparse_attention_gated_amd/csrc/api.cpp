@@ -143,6 +143,8 @@ static int check_compress(const csa2_compress_desc* d) {
     if (!d->out_ik && !d->ik_codes) return fail(CSA2_ERR_INVALID, "compress: w_ik needs out_ik or ik_codes");
     if (d->d_index != 32 && d->d_index != 64 && d->d_index != 128)
       return fail(CSA2_ERR_UNSUPPORTED, "compress: d_index must be 32, 64 or 128");
+    if (d->c * d->d_index < 1024)
+      return fail(CSA2_ERR_UNSUPPORTED, "compress: the projection needs c * d_index >= 1024");
   }
   const int64_t n_per = d->n / d->m;
   if (d->out_batch_stride != 0 && d->out_batch_stride < d->c)

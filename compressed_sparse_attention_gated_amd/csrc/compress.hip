@@ -120,6 +120,46 @@ __device__ __forceinline__ void accum8(float* mx, float* den, float* acc, const 
   }
 }
 
+// One thread's share of the indexer-K projection: sum over channels [c_lo, c_lo + span) of
+// x_hat[row, ch] * W_ik[ch, d] for the rows below nrows (in chunks of 8; a chunk is uniform
+// over the workgroup).  W is read kCB channels at a time, the next block's loads issued
+// before the current block is used, so one L2 round trip covers a whole block.
+template <typename T, int kCB, int kDIc>
+__device__ __forceinline__ void project_part(const float* xs, const T* __restrict__ w_ik, int c, int c_lo,
+                                             int span, int d, int nrows, float (&part_sum)[kRowsPerWG]) {
+  const int nblk = span / kCB;
+  float wcur[kCB], wnxt[kCB];
+#pragma unroll
+  for (int u = 0; u < kCB; ++u) wcur[u] = Ld<T>::scalar(w_ik + (size_t)(c_lo + u) * kDIc + d);
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int cc0 = c_lo + kCB * blk;
+    // the next block (the last iteration reloads its own block: same load count every trip)
+    const int cn = blk + 1 < nblk ? cc0 + kCB : cc0;
+#pragma unroll
+    for (int u = 0; u < kCB; ++u) wnxt[u] = Ld<T>::scalar(w_ik + (size_t)(cn + u) * kDIc + d);
+#pragma unroll
+    for (int rc = 0; rc < kRowsPerWG; rc += 8) {
+      if (rc < nrows) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float acc = part_sum[rc + r];
+#pragma unroll
+          for (int q = 0; q < kCB; q += 4) {
+            const float4 x4 = *reinterpret_cast<const float4*>(&xs[(rc + r) * c + cc0 + q]);
+            acc += x4.x * wcur[q];
+            acc += x4.y * wcur[q + 1];
+            acc += x4.z * wcur[q + 2];
+            acc += x4.w * wcur[q + 3];
+          }
+          part_sum[rc + r] = acc;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCB; ++u) wcur[u] = wnxt[u];
+  }
+}
+
 template <typename T, int G, int kDI>
 __global__ void __launch_bounds__(kThreads) compress_kernel(
     int n, int c, int m, int overlap, const T* __restrict__ ca, const T* __restrict__ za,
@@ -230,32 +270,46 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
 
   if (kProj) {
     __syncthreads();
-    // K_I[row, d] = sum_c x_hat[row, c] * W_ik[c, d]; thread -> (d, row group)
+    // K_I[row, d] = sum_c x_hat[row, c] * W_ik[c, d].  Thread (d, part): the channel range
+    // of its part, rows in chunks of 8 (4 channels per LDS read, W loads shared by the
+    // chunk's rows); the parts' partial sums then meet in LDS and are added in part order.
     constexpr int kDIc = kProj ? kDI : 128;  // placeholder width when there is no projection
-    constexpr int kGroups = kThreads / kDIc;
-    constexpr int kRowsPerGroup = kRowsPerWG / kGroups;
+    constexpr int kParts = kThreads / kDIc;
     const int d = threadIdx.x % kDIc;
-    const int rg = threadIdx.x / kDIc;
-    float accp[kRowsPerGroup];
+    const int part = threadIdx.x / kDIc;
+    const int nrows = min(kRowsPerWG, n_ent - row0);
+    const int span = c / kParts;  // channels per part
+    const int c_lo = part * span;
+    float part_sum[kRowsPerWG];
 #pragma unroll
-    for (int r = 0; r < kRowsPerGroup; ++r) accp[r] = 0.f;
-    for (int cc = 0; cc < c; ++cc) {
-      const float wv = Ld<T>::scalar(w_ik + (size_t)cc * kDIc + d);
+    for (int r = 0; r < kRowsPerWG; ++r) part_sum[r] = 0.f;
+    if (span % 32 == 0)
+      project_part<T, 32, kDIc>(xs, w_ik, c, c_lo, span, d, nrows, part_sum);
+    else
+      project_part<T, 4, kDIc>(xs, w_ik, c, c_lo, span, d, nrows, part_sum);
+    __syncthreads();  // every part has read xs: its space takes the partial sums
+    float* ps = xs;   // [kParts][kRowsPerWG][kDIc]
 #pragma unroll
-      for (int r = 0; r < kRowsPerGroup; ++r) accp[r] += xs[(rg * kRowsPerGroup + r) * c + cc] * wv;
-    }
+    for (int r = 0; r < kRowsPerWG; ++r) ps[(part * kRowsPerWG + r) * kDIc + d] = part_sum[r];
+    __syncthreads();
+    constexpr int kRowsPerPart = kRowsPerWG / kParts;
 #pragma unroll
-    for (int r = 0; r < kRowsPerGroup; ++r) {
-      const int i = row0 + rg * kRowsPerGroup + r;
+    for (int rr = 0; rr < kRowsPerPart; ++rr) {
+      const int r = rr * kParts + part;
+      float kv = 0.f;
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) kv += ps[(p * kRowsPerWG + r) * kDIc + d];
+      const int i = row0 + r;
       const int64_t r_out = dst0 + i;
       if (out_ik && i < n_ent && r_out >= 0 && r_out < ik_cap)
-        Ld<T>::store1(out_ik + (size_t)b * out_ik_bstride + (size_t)r_out * kDIc + d, accp[r]);
+        Ld<T>::store1(out_ik + (size_t)b * out_ik_bstride + (size_t)r_out * kDIc + d, kv);
       if (ik_codes) {
-        // MXFP4: a 32-value group is an aligned half of the wave (d = lane % 32 + 32 j);
-        // neighbouring lanes' codes are gathered so each even lane stores one byte
-        const float am = max32(fabsf(accp[r]));
+        // MXFP4: a 32-value group is an aligned half of the wave (d = lane % 32 + 32 j, one
+        // row per half); neighbouring lanes' codes are gathered so each even lane stores one
+        // byte
+        const float am = max32(fabsf(kv));
         const int e = am > 0.f ? mx_exponent(am) : 0;
-        const uint32_t code = am > 0.f ? e2m1_code(__builtin_amdgcn_ldexpf(accp[r], -e), 1.0f) : 0u;
+        const uint32_t code = am > 0.f ? e2m1_code(__builtin_amdgcn_ldexpf(kv, -e), 1.0f) : 0u;
         const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)code, kDppXor1, 0xF, 0xF, false);
         if (i < n_ent && r_out >= 0 && r_out < q_rows) {
           const size_t qr = (size_t)b * q_rows + r_out;
@@ -275,7 +329,8 @@ hipError_t launch_t(const csa2_compress_desc& d, hipStream_t s) {
   const int64_t oib = d.out_ik_batch_stride ? d.out_ik_batch_stride : (int64_t)n_ent * d.d_index;
   const int64_t out_cap = ob / d.c, ik_cap = d.d_index ? oib / d.d_index : 0;
   const int64_t q_rows = d.q_rows ? d.q_rows : (int64_t)n_ent;
-  const size_t lds = kDI > 0 ? (size_t)kRowsPerWG * d.c * sizeof(float) : 0;
+  // pre-RoPE entries, then (same space) the partial sums of the projection
+  const size_t lds = kDI > 0 ? std::max((size_t)kRowsPerWG * d.c, (size_t)kThreads * kRowsPerWG) * sizeof(float) : 0;
   RopeFreq rope;
   rope_freq_host(&rope, d.rope_dims, d.rope_theta);
   hipLaunchKernelGGL((compress_kernel<T, G, kDI>), grid, dim3(kThreads), lds, s, d.n, d.c, d.m,

@@ -113,7 +113,7 @@ typedef enum {
  *   q_rows) or below 0 are not written.  Every rounding decision is exact: the same fp32
  *   entry values always give the same bytes.
  * Supported: c/8 a power of two, 8 <= c <= 512 (c % 16 == 0 for FP4 planes); rope_dims even
- * and <= c.
+ * and <= c; with w_ik, d_index in {32, 64, 128} and c * d_index >= 1024.
  */
 typedef struct {
   int B, n, c, m, overlap;

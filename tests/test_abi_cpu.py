@@ -94,6 +94,7 @@ def test_compress_validation(L):
         (dict(rope_dims=128, rope_theta=1e4), csa2.CSA2_ERR_INVALID),
         (dict(w_ik=FAKE, d_index=128), csa2.CSA2_ERR_INVALID),  # no out_ik
         (dict(w_ik=FAKE, out_ik=FAKE, d_index=100), csa2.CSA2_ERR_UNSUPPORTED),
+        (dict(c=16, w_ik=FAKE, out_ik=FAKE, d_index=32), csa2.CSA2_ERR_UNSUPPORTED),  # c * d_index < 1024
         (dict(out_batch_stride=5), csa2.CSA2_ERR_INVALID),
         # write path into the quantised cache
         (dict(out=None), csa2.CSA2_ERR_INVALID),  # no output at all
