@@ -140,7 +140,9 @@ def cpu_baseline(torch, wl, d, budget_s):
         d = dict(d, e_oracle=e, k_oracle=torch.from_numpy(k))
     done, spent = 0, 0.0
     kind = wl.kind
-    n_units = wl.n_tokens if kind == "prefill" else wl.B
+    # decode batches are short: the sample cycles over the batch's queries until the budget
+    # is spent (each pass over a query repeats the same work)
+    n_units = wl.n_tokens if kind == "prefill" else 64 * wl.B
     rs = np.random.default_rng(0)
     while spent < budget_s and done < n_units:
         if kind == "prefill":
@@ -163,7 +165,7 @@ def cpu_baseline(torch, wl, d, budget_s):
             O.sparse_attn(q[None, None], np.array([[t]]), entries[sel][None], np.arange(len(sel))[None, None],
                           wr[None], [max(0, t - wl.window + 1)], wl.window, sink, rope_dims=wl.rope_dims)
         else:
-            b = done
+            b = done % wl.B
             hier = kind == "hier"
             layers = d["layers"] if hier else [d]
             fp4 = kind == "decode_fp4"
@@ -200,9 +202,10 @@ def cpu_baseline(torch, wl, d, budget_s):
     unit = "tokens/s" if kind == "prefill" else "queries/s"
     what = {"prefill": f"{done} query tokens of the {wl.n_tokens}-token prefill (their compressor block and "
                        f"window rows, causal scan, top-{wl.k}, attention)",
-            "hier": f"{done} of the {wl.B} queries, each through the whole 5-layer group (full scan of {wl.L}, "
-                    f"pool, Reindex, 5 attentions)",
-            }.get(kind, f"{done} of the {wl.B} decode queries (full scan of {wl.L} entries, top-{wl.k}, attention)")
+            "hier": f"{done} query passes over the batch's {wl.B} queries, each through the whole 5-layer group "
+                    f"(full scan of {wl.L}, pool, Reindex, 5 attentions)",
+            }.get(kind, f"{done} query passes over the batch's {wl.B} decode queries (full scan of {wl.L} entries, "
+                        f"top-{wl.k}, attention)")
     return {"value": done / spent, "unit": unit, "cores": int(_cores()), "kind": "oracle",
             "sample": f"{what} by the fp64 numpy oracle on the host, {spent:.1f} s; each query's inputs are "
                       "copied to the host before its timed region"}
