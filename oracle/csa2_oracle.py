@@ -343,8 +343,28 @@ def sparse_attn(q, q_pos, kv, idx, win=None, win_pos0=None, window=128, sink=Non
     return out, mass
 
 
+def dense_attn(q, q_pos, kv, m_prime, win=None, win_pos0=None, window=128, sink=None,
+               rope_dims=64, theta=10000.0, eps=1e-6, scale=None, q_norm=True):
+    """HCA's attention ([DSA-to-CSA notes] eq. (20)-(26)): no indexer; every compressed
+    entry the query may see is both key and value, CoreAttn(q, C^Comp, C^Comp).  Entry j
+    pools tokens [m'j, m'j+m') and is visible from position m'(j+1) on (section
+    "因果边界与短滑窗", with m replaced by m'); the latest n_win uncompressed rows are joined
+    as in CSA, and the sink logit of eq. (27) applies alike.  That is the shared-KV
+    attention above with the index list 0 .. n_vis-1.  Returns (out, mass)."""
+    B, T = np.asarray(q).shape[:2]
+    N = np.asarray(kv).shape[1]
+    idx = np.full((B, T, max(N, 1)), -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(T):
+            nv = n_visible(int(q_pos[b, t]), N, m_prime)
+            idx[b, t, :nv] = np.arange(nv)
+    return sparse_attn(q, q_pos, kv, idx, win=win, win_pos0=win_pos0, window=window, sink=sink,
+                       rope_dims=rope_dims, theta=theta, eps=eps, scale=scale, q_norm=q_norm)
+
+
 __all__ = [
     "gated_pool", "gated_pool_weights", "rms_norm", "rope_angles", "rope", "compress", "write_cache",
+    "dense_attn",
     "n_visible", "indexer_scores", "topk_indices", "index_topk_full", "block_max",
     "hier_candidates", "reindex_topk", "reindex_topk_masked", "reuse", "window_rows",
     "attend_one", "sparse_attn",

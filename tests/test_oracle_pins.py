@@ -508,3 +508,38 @@ def test_write_cache_streaming_equals_bulk(m, overlap):
     deq = F.fp4_main_decode(bulk[0][:n // m], bulk[1][:n // m])
     step = np.repeat(F.e4m3_decode(bulk[1][:n // m]), 16, axis=-1)
     assert np.all(np.abs(deq - ent) <= step + 1e-12)
+
+
+# =================================================================== HCA (dense over compressed entries)
+def test_hca_causal_boundary_page_example():
+    # [DSA-to-CSA notes] "因果边界与短滑窗" with m' = 128: the first entry pools positions
+    # 0-127; positions 100 and 127 cannot read it, position 128 can.
+    r = _rng(41)
+    H, c, W = 2, 16, 4
+    kv = r.standard_normal((1, 3, c))
+    win = r.standard_normal((1, 300, c))
+    q = r.standard_normal((1, 1, H, c))
+    sink = r.standard_normal(H)
+    for t, n_seen in ((100, 0), (127, 0), (128, 1), (255, 1), (256, 2), (10_000, 3)):
+        out, _ = O.dense_attn(q, np.array([[t]]), kv, 128, win=win, win_pos0=[0], window=W, sink=sink,
+                              rope_dims=0)
+        wrows = win[0, t - W + 1:t + 1]
+        for h in range(H):
+            qh = q[0, 0, h] / np.sqrt((q[0, 0, h] ** 2).mean() + 1e-6)
+            rows = np.concatenate([kv[0, :n_seen], wrows])
+            want = _sdpa_with_sink(qh, rows, sink[h], 1 / math.sqrt(c))
+            np.testing.assert_allclose(out[0, 0, h], want, rtol=1e-12, atol=1e-13, err_msg=f"t={t}")
+
+
+def test_hca_pipeline_pools_128_token_blocks_with_bias():
+    # eq. (22)-(23): per-channel softmax over a non-overlapping block of m' tokens, logits
+    # Z + B; equal logits give the block mean, and a bias column shifts weight to its position
+    r = _rng(42)
+    c, mp = 8, 128
+    C = r.standard_normal((2 * mp, c))
+    ent, _ = O.compress(C, np.zeros((2 * mp, c)), mp, norm=False)
+    np.testing.assert_allclose(ent, C.reshape(2, mp, c).mean(axis=1), rtol=1e-12, atol=1e-14)
+    bias = np.zeros((mp, c))
+    bias[5] = 50.0  # e^50 dominates the other 127 unit terms
+    ent_b, _ = O.compress(C, np.zeros((2 * mp, c)), mp, b_a=bias, norm=False)
+    np.testing.assert_allclose(ent_b, C.reshape(2, mp, c)[:, 5], rtol=0, atol=1e-15)
