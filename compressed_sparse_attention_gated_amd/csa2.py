@@ -51,7 +51,7 @@ class AttnDesc(C.Structure):
                 ("q_dtype", _i), ("q", _vp), ("q_pos", _vp), ("kv_dtype", _i), ("kv", _vp),
                 ("kv_codes", _vp), ("kv_scales", _vp), ("idx", _vp), ("win", _vp), ("Lw", _i),
                 ("win_pos0", _vp), ("n_win", _i), ("sink", _vp), ("out", _vp), ("out_mass", _vp),
-                ("num_splits", _i)]
+                ("num_splits", _i), ("dense_m", _i)]
 
 
 class KernelTime(C.Structure):
@@ -239,7 +239,7 @@ def csa2_hier_workspace_bytes(block_max, q_pos, N, *, m=1, block=8, n_keep=2048)
 # ---------------------------------------------------------------------------- attention
 def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
                win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0, eps=1e-6,
-               scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0):
+               scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0, dense_m=0):
     B, T, H, c = q.shape
     if N is None:
         N = kv.shape[1] if kv is not None else (kv_codes.shape[1] if kv_codes is not None else 0)
@@ -250,20 +250,21 @@ def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None,
                     kv_dtype=kvdt, kv=_p(kv), kv_codes=_p(kv_codes), kv_scales=_p(kv_scales),
                     idx=_p(idx), win=_p(win), Lw=win.shape[1] if win is not None else 0,
                     win_pos0=_p(win_pos0), n_win=n_win if win is not None else 0, sink=_p(sink),
-                    out=_p(out), out_mass=_p(out_mass), num_splits=num_splits)
+                    out=_p(out), out_mass=_p(out_mass), num_splits=num_splits, dense_m=dense_m)
 
 
 def csa2_sparse_attn(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
                      win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0,
                      eps=1e-6, scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0,
-                     workspace=None, stream=None):
-    """q [B, T, H, c] -> out [B, T, H, c] (dtype of q)."""
+                     dense_m=0, workspace=None, stream=None):
+    """q [B, T, H, c] -> out [B, T, H, c] (dtype of q).  dense_m > 0 (idx None): dense
+    attention over every entry visible at the query's position (entries of dense_m tokens)."""
     if out is None:
         out = torch.empty_like(q)
     d = _attn_desc(q, q_pos, idx, kv=kv, kv_codes=kv_codes, kv_scales=kv_scales, N=N, win=win,
                    win_pos0=win_pos0, n_win=n_win, sink=sink, rope_dims=rope_dims,
                    rope_theta=rope_theta, eps=eps, scale=scale, q_norm=q_norm, out=out,
-                   out_mass=out_mass, num_splits=num_splits)
+                   out_mass=out_mass, num_splits=num_splits, dense_m=dense_m)
     nbytes = lib().csa2_attn_workspace_bytes(C.byref(d))
     if workspace is None or workspace.numel() < nbytes:
         workspace = _ws(nbytes, q.device)

@@ -363,7 +363,9 @@ static int check_attn(const csa2_attn_desc* d) {
   if (d->num_splits < 0) return fail(CSA2_ERR_INVALID, "attn: num_splits must be >= 0");
   if ((long long)d->B * d->T * d->H == 0) return CSA2_OK;
   if (!d->q || !d->q_pos || !d->out) return fail(CSA2_ERR_INVALID, "attn: q, q_pos and out are required");
-  if (d->k > 0 && !d->idx) return fail(CSA2_ERR_INVALID, "attn: idx required when k > 0");
+  if (d->dense_m < 0) return fail(CSA2_ERR_INVALID, "attn: dense_m must be >= 0");
+  if (d->dense_m > 0 && d->idx) return fail(CSA2_ERR_INVALID, "attn: dense attention takes no idx");
+  if (d->dense_m == 0 && d->k > 0 && !d->idx) return fail(CSA2_ERR_INVALID, "attn: idx required when k > 0");
   if (d->k > 0 && d->N > 0) {
     if (d->kv_dtype == CSA2_FP4_E4M3 && (!d->kv_codes || !d->kv_scales))
       return fail(CSA2_ERR_INVALID, "attn: FP4 kv needs kv_codes and kv_scales");

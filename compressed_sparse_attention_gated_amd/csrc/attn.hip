@@ -32,6 +32,7 @@ namespace {
 // ------------------------------------------------------------------ shared row bookkeeping
 struct AttnDev {
   int B, T, H, c, k, N, rope_dims, q_norm, Lw, n_win, splits, tiles_per_split, n_hg;
+  int dense_m;  // > 0: the index slots are entries 0 .. N-1, visible up to min(N, t / dense_m)
   float rope_theta, eps, scale_log2;  // scale * log2(e)
   int q_f32, kv_kind;                 // kv_kind: 0 = same as q, 1 = FP4
   const void* q;
@@ -53,6 +54,11 @@ struct AttnDev {
 struct WinRange {
   int lo_row, cnt;
 };
+// entries of the index slots visible to a query at position t_pos: all N with an index list
+// (its ids say which), the completed blocks' entries in dense mode
+__device__ __forceinline__ int slot_limit(const AttnDev& a, int t_pos) {
+  return a.dense_m > 0 ? min(a.N, max(t_pos, 0) / a.dense_m) : a.N;
+}
 __device__ __forceinline__ WinRange window_of_p0(const AttnDev& a, int p0, int t_pos) {
   WinRange w{0, 0};
   if (!a.win || a.n_win <= 0) return w;
@@ -120,6 +126,7 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 
   const WinRange wr = window_of(a, b, t_pos);
   const int R = a.k + wr.cnt;
+  const int lim = slot_limit(a, t_pos);
   float m_run = -INFINITY, l_run = 0.f;
   float o[kSimpleMaxPerLane];
 #pragma unroll
@@ -128,8 +135,8 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
     float rv[kSimpleMaxPerLane];
     bool valid = true;
     if (s < a.k) {
-      const int e = a.idx[(size_t)row * a.k + s];
-      valid = e >= 0 && e < a.N;
+      const int e = a.dense_m > 0 ? s : a.idx[(size_t)row * a.k + s];
+      valid = e >= 0 && e < lim;
       if (!valid) continue;
       if (a.kv_kind == 1) {
         const uint8_t* cp = a.kv_codes + ((size_t)b * a.N + e) * (c / 2);
@@ -253,11 +260,11 @@ __device__ __forceinline__ void ids_of_split(const AttnDev& a, int row, int slot
   for (int u = 0; u < kSlotsPerThread; ++u) {
     const int i = threadIdx.x + kThreadsM * u;
     const int s = slot0 + i;
-    ids[u] = (i < n && s < a.k) ? a.idx[(size_t)row * a.k + s] : -1;
+    ids[u] = (i < n && s < a.k) ? (a.dense_m > 0 ? s : a.idx[(size_t)row * a.k + s]) : -1;
   }
 }
 __device__ __forceinline__ void stage_slots(const AttnDev& a, int slot0, int n, int R, const WinRange& wr,
-                                            const int (&ids)[kSlotsPerThread], int* src) {
+                                            int lim, const int (&ids)[kSlotsPerThread], int* src) {
 #pragma unroll
   for (int u = 0; u < kSlotsPerThread; ++u) {
     const int i = threadIdx.x + kThreadsM * u;
@@ -265,7 +272,7 @@ __device__ __forceinline__ void stage_slots(const AttnDev& a, int slot0, int n, 
     const int s = slot0 + i;
     int v = -1;
     if (s < R) {
-      if (s < a.k) v = (ids[u] >= 0 && ids[u] < a.N) ? ids[u] : -1;
+      if (s < a.k) v = (ids[u] >= 0 && ids[u] < lim) ? ids[u] : -1;
       else v = -2 - (wr.lo_row + (s - a.k));
     }
     src[i] = v;
@@ -397,7 +404,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   const int R = a.k + wr.cnt;
   const int n_tiles = (R + kTile - 1) / kTile;
   const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
-  if (tile0 < tile1) stage_slots(a, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, ids, sm.src);
+  if (tile0 < tile1) stage_slots(a, tile0 * kTile, (tile1 - tile0) * kTile, R, wr, slot_limit(a, t_pos), ids, sm.src);
   stage_rope(a, t_pos, sm.rope_c, sm.rope_s);
   lds_barrier();
   // rows of the first tile start travelling while q_hat is formed
@@ -721,6 +728,13 @@ void pick_splits(const csa2_attn_desc& d, int* splits, int* tps) {
   if (*splits < 1) *splits = 1;
 }
 
+// dense mode reads every entry slot: N index slots, no index list
+csa2_attn_desc effective(const csa2_attn_desc& d0) {
+  csa2_attn_desc d = d0;
+  if (d.dense_m > 0) d.k = d.N;
+  return d;
+}
+
 AttnDev make_dev(const csa2_attn_desc& d) {
   AttnDev a{};
   a.B = d.B; a.T = d.T; a.H = d.H; a.c = d.c; a.k = d.k; a.N = d.N; a.rope_dims = d.rope_dims;
@@ -733,6 +747,7 @@ AttnDev make_dev(const csa2_attn_desc& d) {
   a.q = d.q; a.q_pos = d.q_pos; a.kv = d.kv; a.kv_codes = d.kv_codes; a.kv_scales = d.kv_scales;
   a.idx = d.idx; a.win = d.win; a.win_pos0 = d.win_pos0; a.sink = d.sink; a.out = d.out;
   a.out_mass = d.out_mass;
+  a.dense_m = d.dense_m;
   a.n_hg = d.H / kHG;
   rope_freq_host(&a.rope, d.rope_dims, d.rope_theta);
   return a;
@@ -750,19 +765,21 @@ AttnPlan plan_attn(const csa2_attn_desc& d) {
 
 }  // namespace
 
-size_t attn_workspace_bytes(const csa2_attn_desc& d) {
+size_t attn_workspace_bytes(const csa2_attn_desc& d0) {
+  const csa2_attn_desc d = effective(d0);
   const AttnPlan p = plan_attn(d);
   if (!mfma_ok(d) || p.splits <= 1) return 0;
   const size_t units = (size_t)d.B * d.T * (d.H / kHG);
   return units * p.splits * (kHG * kC * sizeof(uint16_t) + 2 * kHG * sizeof(float));
 }
 
-hipError_t launch_attn(const csa2_attn_desc& d, void* ws, size_t ws_bytes, hipStream_t s) {
+hipError_t launch_attn(const csa2_attn_desc& d0, void* ws, size_t ws_bytes, hipStream_t s) {
+  const csa2_attn_desc d = effective(d0);
   const int rows = d.B * d.T;
   if (rows == 0 || d.H == 0) return hipSuccess;
   // every pointer a kernel dereferences must be set
   const bool rows_needed = d.k > 0 && d.N > 0;
-  if (!d.q || !d.q_pos || !d.out || (d.k > 0 && !d.idx) ||
+  if (!d.q || !d.q_pos || !d.out || (d.k > 0 && !d.idx && d.dense_m == 0) ||
       (rows_needed && d.kv_dtype == CSA2_FP4_E4M3 && (!d.kv_codes || !d.kv_scales)) ||
       (rows_needed && d.kv_dtype != CSA2_FP4_E4M3 && !d.kv) || (d.win && !d.win_pos0))
     return hipErrorInvalidValue;

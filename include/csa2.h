@@ -232,6 +232,12 @@ CSA2_API int csa2_hier_candidates(const csa2_hier_desc *d, void *ws, size_t ws_b
  *   sink: fp32 [H] or NULL (no sink term).  out_mass: fp32 [B, T, H] or NULL: receives
  *     sum_j p_j, the probability mass on real rows.
  *   ws, ws_bytes: workspace of at least csa2_attn_workspace_bytes(d) (split partials).
+ *   dense_m: 0 for the selected entries of idx.  > 0 for dense attention over every
+ *     visible entry, the HCA form ([DSA-to-CSA notes] eq. (20)-(26): a heavily compressed
+ *     history, m' = 128 in V4, read in full without an indexer): idx must be NULL, k is
+ *     ignored, and the rows are entries 0 .. n_vis-1 with n_vis = min(N, floor(p / dense_m))
+ *     (an entry is visible once its block of dense_m tokens has ended: "因果边界与短滑窗"),
+ *     then the window rows as above.
  * Supported: c % 16 == 0, c <= 512, rope_dims even and <= c; FP4 needs bf16 q.
  *   The MFMA paths run for bf16 q, c == 512, H % 32 == 0, rope_dims <= 128; other shapes
  *   use a generic fp32 kernel with the same semantics.
@@ -257,6 +263,7 @@ typedef struct {
   float *out_mass;
   int num_splits; /* row-range splits per query (0 = chosen by the library); a tuning knob
                      that does not change results beyond fp32 rounding order */
+  int dense_m;
 } csa2_attn_desc;
 
 CSA2_API size_t csa2_attn_workspace_bytes(const csa2_attn_desc *d);

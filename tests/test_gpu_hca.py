@@ -1,0 +1,89 @@
+"""GPU parity of HCA ([DSA-to-CSA notes] eq. (20)-(26)): the m' = 128 compressor with its
+position bias, then dense shared-KV attention over every visible compressed entry plus the
+window, through csa2_compress and csa2_sparse_attn(dense_m = m'), against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import formats as F
+from compressed_sparse_attention_gated_amd import workloads as W
+from tests._gpu import assert_close, banner, bf16, f32, host, i32, u8
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = dict(atol=2e-2, rtol=2e-2)
+F32_TOL = dict(atol=1e-4, rtol=1e-4)
+
+
+@pytest.fixture(scope="module")
+def C():
+    from compressed_sparse_attention_gated_amd import csa2
+
+    csa2.lib()
+    return csa2
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "fp4"])
+def test_hca_dense_decode_mfma(C, kv_format):
+    # three queries: all 300 entries visible, 150 visible (position inside block 150), none
+    banner(f"hca dense decode MFMA B=3 N=300 m'=128 H=64 c=512 kv={kv_format}")
+    g = W.rng(61)
+    B, N, mp = 3, 300, 128
+    a = W.attn_inputs(g, B, 1, N, 64, 512, Lw=128, kv_format=kv_format)
+    q_pos = np.array([[mp * N + 5], [mp * 150 + 127], [127]], np.int32)
+    win_pos0 = (q_pos[:, 0] - 127).astype(np.int32)
+    kvkw = (dict(kv=bf16(a["kv"])) if kv_format == "bf16"
+            else dict(kv_codes=u8(a["kv_codes"]), kv_scales=u8(a["kv_scales"])))
+    mass = torch.empty((B, 1, 64), device="cuda")
+    out = C.csa2_sparse_attn(bf16(a["q"]), i32(q_pos), None, win=bf16(a["win"]), win_pos0=i32(win_pos0),
+                             n_win=128, sink=f32(a["sink"]), out_mass=mass, dense_m=mp, **kvkw)
+    torch.cuda.synchronize()
+    kvd = a["kv"] if kv_format == "bf16" else F.fp4_main_decode(a["kv_codes"], a["kv_scales"])
+    want, wm = O.dense_attn(a["q"], q_pos, kvd, mp, win=a["win"], win_pos0=win_pos0, window=128,
+                            sink=a["sink"], rope_dims=64)
+    assert_close(host(out), want, **BF16_TOL, what=f"hca {kv_format}")
+    assert_close(host(mass), wm, atol=1e-2, rtol=1e-2, what="mass")
+
+
+def test_hca_dense_prefill_f32(C):
+    # the generic kernel (fp32 I/O): tokens on both sides of each block boundary
+    banner("hca dense prefill f32 T=64 N=3 m'=128 H=4 c=64 window 16")
+    g = W.rng(62)
+    T, N, mp = 64, 3, 128
+    a = W.attn_inputs(g, 1, T, N, 4, 64, Lw=400, io_dtype="f32")
+    q_pos = np.sort(np.r_[[0, 100, 127, 128, 129, 255, 256, 383, 384, 399],
+                          np.random.default_rng(5).integers(0, 400, T - 10)]).astype(np.int32)[None]
+    win_pos0 = np.array([0], np.int32)
+    out = C.csa2_sparse_attn(f32(a["q"]), i32(q_pos), None, kv=f32(a["kv"]), win=f32(a["win"]),
+                             win_pos0=i32(win_pos0), n_win=16, sink=f32(a["sink"]), rope_dims=16, dense_m=mp)
+    torch.cuda.synchronize()
+    want, _ = O.dense_attn(a["q"], q_pos, a["kv"], mp, win=a["win"], win_pos0=win_pos0, window=16,
+                           sink=a["sink"], rope_dims=16)
+    assert_close(host(out), want, **F32_TOL, what="hca prefill f32")
+
+
+def test_hca_layer_compress_then_dense_attention(C):
+    # the layer: 1,300 tokens -> 10 entries of 128 (ragged tail left to the caller), bias B,
+    # RMSNorm + RoPE at write time; then dense attention for queries across the boundaries
+    banner("hca layer: compress m'=128 with bias, dense attention H=64 c=512 bf16")
+    g = W.rng(63)
+    n, c, mp, H = 1300, 512, 128, 64
+    d = W.compress_inputs(g, n, c, mp, dtype="bf16", bias_std=0.1)
+    ent, _ = C.csa2_compress(bf16(d["ca"]), bf16(d["za"]), mp, ba=f32(d["ba"]), rope_dims=64)
+    e_ref, _ = O.compress(d["ca"][0], d["za"][0], mp, b_a=d["ba"], rope_dims=64)
+    assert_close(host(ent)[0], e_ref, **BF16_TOL, what="hca entries")
+    T = 8
+    q_pos = np.array([[127, 128, 300, 640, 1151, 1152, 1280, 1299]], np.int32)
+    a = W.attn_inputs(g, 1, T, 10, H, c, Lw=n)
+    win, _ = C.csa2_compress(bf16(d["ca"]), bf16(d["ca"]), 1, rope_dims=64)  # per-token window rows
+    w_ref, _ = O.compress(d["ca"][0], d["ca"][0], 1, rope_dims=64)
+    out = C.csa2_sparse_attn(bf16(a["q"]), i32(q_pos), None, kv=ent, win=win, win_pos0=i32(np.zeros(1)),
+                             n_win=128, sink=f32(a["sink"]), rope_dims=64, dense_m=mp)
+    torch.cuda.synchronize()
+    # the oracle reads the library's own bf16 entries and window rows (checked above against
+    # the fp64 compressor), so the attention comparison is not blurred by the write's rounding
+    want, _ = O.dense_attn(a["q"], q_pos, host(ent), mp, win=host(win), win_pos0=[0], window=128,
+                           sink=a["sink"], rope_dims=64)
+    assert_close(host(out), want, **BF16_TOL, what="hca layer")
+    assert_close(host(win)[0], w_ref, **BF16_TOL, what="window rows")
