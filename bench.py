@@ -21,6 +21,8 @@ first pass, without per-kernel events, gives `value`).
   --config 3  the 32,768-token prefill (value in tokens/s; the scan's roofline is bf16 MFMA)
   --config 4  the hierarchical decoder group at 1M context (Full + pool + Reindex + 3 Reuse)
   --config 5  the FP4 / MXFP4 cache decode
+  --config 6  the pages' HCA variant at decode (32 x 1,048,576 tokens -> 8,192 entries of
+              m' = 128, dense attention; not one of the five reference workloads)
 """
 from __future__ import annotations
 
@@ -44,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    p.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5, 6])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="bound of the oracle sample")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -164,6 +166,15 @@ def cpu_baseline(torch, wl, d, budget_s):
             sel = idx[idx >= 0]
             O.sparse_attn(q[None, None], np.array([[t]]), entries[sel][None], np.arange(len(sel))[None, None],
                           wr[None], [max(0, t - wl.window + 1)], wl.window, sink, rope_dims=wl.rope_dims)
+        elif kind == "hca_decode":
+            b = done % wl.B
+            q, win, sink = _h(d["q"][b, 0]), _h(d["win"][b]), _h(d["sink"])
+            kv_h = d["kv"][b].view(torch.int16).cpu().numpy().view(np.uint16)  # raw bits, not timed
+            L = wl.L
+            t0 = time.perf_counter()
+            rows = _bf16_bits_to_f64(kv_h)
+            O.dense_attn(q[None, None], np.array([[L]]), rows[None], wl.m, win=win[None], win_pos0=[L - wl.window + 1],
+                         window=wl.window, sink=sink, rope_dims=wl.rope_dims)
         else:
             b = done % wl.B
             hier = kind == "hier"
@@ -202,6 +213,8 @@ def cpu_baseline(torch, wl, d, budget_s):
     unit = "tokens/s" if kind == "prefill" else "queries/s"
     what = {"prefill": f"{done} query tokens of the {wl.n_tokens}-token prefill (their compressor block and "
                        f"window rows, causal scan, top-{wl.k}, attention)",
+            "hca_decode": f"{done} query passes over the batch's {wl.B} queries (dense attention over "
+                          f"{wl.L // wl.m} entries plus the window)",
             "hier": f"{done} query passes over the batch's {wl.B} queries, each through the whole 5-layer group "
                     f"(full scan of {wl.L}, pool, Reindex, 5 attentions)",
             }.get(kind, f"{done} query passes over the batch's {wl.B} decode queries (full scan of {wl.L} entries, "
@@ -225,7 +238,8 @@ def copy_probe(torch, mib):
 
 
 # ---------------------------------------------------------------------------- main
-TAGS = {2: "decode_full_b32_l65536", 3: "prefill_n32768", 4: "hier_b8_l1048576", 5: "decode_fp4_b64_l262144"}
+TAGS = {2: "decode_full_b32_l65536", 3: "prefill_n32768", 4: "hier_b8_l1048576", 5: "decode_fp4_b64_l262144",
+        6: "hca_decode_b32_l1048576"}
 
 
 def scan_work(wl):
@@ -244,6 +258,8 @@ def scan_work(wl):
 def attn_bytes(wl):
     row_bytes = 288 if wl.kind == "decode_fp4" else wl.c * 2
     queries = wl.n_tokens if wl.kind == "prefill" else wl.B
+    if wl.kind == "hca_decode":  # every visible entry, no index list
+        return queries * ((wl.L // wl.m) * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2)
     return queries * (wl.k * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2 + wl.k * 4)
 
 
@@ -307,7 +323,8 @@ def main():
     torch.cuda.set_device(0)
     wl = W.WORKLOADS[args.config]
     make, Step = {"decode": (W.decode_inputs, S.DecodeStep), "decode_fp4": (W.decode_inputs, S.DecodeStep),
-                  "hier": (W.hier_inputs, S.HierStep), "prefill": (W.prefill_inputs, S.PrefillStep)}[wl.kind]
+                  "hier": (W.hier_inputs, S.HierStep), "prefill": (W.prefill_inputs, S.PrefillStep),
+                  "hca_decode": (W.hca_inputs, S.HcaDecodeStep)}[wl.kind]
     # two independent input instances alternate, so no step finds its rows cache-resident
     n_inst = 2
     insts = [make(wl, 2000 + 17 * i) for i in range(n_inst)]
@@ -320,14 +337,24 @@ def main():
     kern = per_kernel(C, torch, step, args.steps)
     launches_per_step = {k: v["launches"] / args.steps for k, v in kern.items()}
 
-    # the Full layer's scan: the fused scan + chunk top-k at decode, the shared-tile scan at prefill
-    scan_name = "index_scan_prefill" if wl.kind == "prefill" else "index_scan_select"
-    if scan_name not in kern:
-        scan_name = next(n for n in kern if n.startswith("index_scan"))
-    sb, sf, pairs = scan_work(wl)
-    scan_ms = kern[scan_name]["avg_ms"]
     stages = {k: dict(v) for k, v in kern.items()}
-    if wl.kind == "prefill":
+    hca = wl.kind == "hca_decode"
+    if not hca:
+        # the Full layer's scan: the fused scan + chunk top-k at decode, the shared-tile scan at prefill
+        scan_name = "index_scan_prefill" if wl.kind == "prefill" else "index_scan_select"
+        if scan_name not in kern:
+            scan_name = next(n for n in kern if n.startswith("index_scan"))
+        sb, sf, pairs = scan_work(wl)
+        scan_ms = kern[scan_name]["avg_ms"]
+    if hca:
+        # no indexer: the dense attention is the path; its row-reading kernel is the roofline
+        ab_in = wl.B * ((wl.L // wl.m) * wl.c * 2 + wl.window * wl.c * 2 + wl.H * wl.c * 2)
+        a_ms = kern["attn_mfma"]["avg_ms"]
+        achieved = ab_in / (a_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "attn_mfma", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic("attn_mfma", TAGS[args.config]),
+                "bytes_per_launch": ab_in}
+    elif wl.kind == "prefill":
         achieved = sf / (scan_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": scan_name, "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
@@ -344,7 +371,7 @@ def main():
     stages["attention_total"] = {"ms_per_step": attn_ms, "algorithmic_bytes": ab,
                                  "GB_per_s": ab / (attn_ms * 1e-3) / 1e9,
                                  "frac_hbm": ab / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if wl.kind != "hier":
+    if wl.kind not in ("hier", "hca_decode"):
         stages["write_path"] = write_path_stage(torch, C, wl, insts[0])
     prefill = wl.kind == "prefill"
     units = wl.n_tokens if prefill else wl.B
@@ -352,11 +379,17 @@ def main():
     cfg = {"workload": wl.name}
     if prefill:
         cfg.update({"tokens": wl.n_tokens, "m": wl.m, "entries": wl.n_tokens // wl.m})
+    elif hca:
+        cfg.update({"batch_queries": wl.B, "context_tokens": wl.L, "m_prime": wl.m, "entries": wl.L // wl.m})
     else:
         cfg.update({"batch_queries": wl.B, "context_entries": wl.L, "m": wl.m})
-    cfg.update({"indexer": f"{wl.H_I}x{wl.d_I}", "top_k": wl.k, "window": wl.window, "heads": wl.H,
-                "head_dim": wl.c, "kv_cache": "fp4+e4m3" if wl.kind == "decode_fp4" else "bf16",
-                "indexer_k": "mxfp4" if wl.kind == "decode_fp4" else "bf16"})
+    if hca:
+        cfg.update({"window": wl.window, "heads": wl.H, "head_dim": wl.c, "kv_cache": "bf16",
+                    "attention": "dense over every visible entry (no indexer)"})
+    else:
+        cfg.update({"indexer": f"{wl.H_I}x{wl.d_I}", "top_k": wl.k, "window": wl.window, "heads": wl.H,
+                    "head_dim": wl.c, "kv_cache": "fp4+e4m3" if wl.kind == "decode_fp4" else "bf16",
+                    "indexer_k": "mxfp4" if wl.kind == "decode_fp4" else "bf16"})
     if wl.kind == "hier":
         cfg["layers"] = "Full (scan, top-512, block max) + pool (2048 blocks) + Reindex + 3 Reuse"
     res = {
@@ -373,7 +406,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded on-device generator; random-init, no trained weights)",
         "config": cfg,
-        "scores_per_s": pairs / (scan_ms * 1e-3),
+        "scores_per_s": None if hca else pairs / (scan_ms * 1e-3),
         "roofline": roof,
         "stages": stages,
     }

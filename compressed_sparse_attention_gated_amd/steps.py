@@ -112,6 +112,30 @@ class HierStep:
         return self.idx_full, self.cand, self.count, self.idx_re, self.outs
 
 
+class HcaDecodeStep:
+    """HCA decode ([DSA-to-CSA notes] eq. (20)-(26)): the new token's row into the window,
+    then dense attention over every visible m' = 128 entry plus the window.  (The m' = 128
+    compressor runs once per 128 tokens, when a block completes; it is not in this step.)"""
+
+    def __init__(self, wl, d):
+        self.wl = wl
+        dev = d["q"].device
+        self.out = torch.empty((wl.B, 1, wl.H, wl.c), dtype=torch.bfloat16, device=dev)
+        self.ws_attn = _ws(C.csa2_attn_workspace_bytes(d["q"], d["q_pos"], None, kv=d["kv"], win=d["win"],
+                                                       win_pos0=d["win_pos0"], n_win=wl.window, sink=d["sink"],
+                                                       rope_dims=wl.rope_dims, out=self.out, dense_m=wl.m), dev)
+
+    def run(self, d):
+        wl = self.wl
+        win = d["win"]
+        C.csa2_compress(d["c_new"], d["z_new"], 1, pos0=d["q_pos"][:, 0], rope_dims=wl.rope_dims,
+                        out=win[:, wl.window - 1:, :])
+        C.csa2_sparse_attn(d["q"], d["q_pos"], None, kv=d["kv"], win=win, win_pos0=d["win_pos0"],
+                           n_win=wl.window, sink=d["sink"], rope_dims=wl.rope_dims, out=self.out,
+                           workspace=self.ws_attn, dense_m=wl.m)
+        return None, self.out
+
+
 class PrefillStep:
     def __init__(self, wl, d):
         self.wl = wl

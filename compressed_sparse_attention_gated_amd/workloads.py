@@ -58,6 +58,10 @@ WORKLOADS = {
                 "hier", B=8, L=1048576, c=512, m=1),
     5: Workload("FP4 cache decode, B=64 x 262,144 ctx, FP4 main KV + MXFP4 indexer K",
                 "decode_fp4", B=64, L=262144, c=512, m=1),
+    # the pages' HCA variant (not one of the five workloads above): m' = 128 entries read
+    # densely, no indexer; L counts tokens, so each query sees L / 128 entries
+    6: Workload("HCA decode layer, B=32 x 1,048,576 ctx, m'=128 -> 8,192 entries, dense attention",
+                "hca_decode", B=32, L=1048576, c=512, m=128),
 }
 
 
@@ -237,6 +241,22 @@ def decode_inputs(wl, seed, device="cuda"):
     fp4 = wl.kind == "decode_fp4"
     d = dict(indexer_inputs(g, B, 1, L, wl.H_I, wl.d_I, wl.w_values, k_format="mxfp4" if fp4 else "bf16"))
     d.update(attn_inputs(g, B, 1, L, H, c, Lw=wl.window, kv_format="fp4" if fp4 else "bf16"))
+    d["q_pos"] = torch.full((B, 1), L, dtype=torch.int32, device=device)
+    d["win_pos0"] = torch.full((B,), L - wl.window + 1, dtype=torch.int32, device=device)
+    d["c_new"] = g.normal((B, 1, c), dtype="bf16")
+    d["z_new"] = g.normal((B, 1, c), dtype="bf16")
+    return d
+
+
+def hca_inputs(wl, seed, device="cuda"):
+    """One HCA decode instance: the compressed cache [B, L/m', c] ~ N(0,1) (bf16), the query
+    ~ N(0,1), the 128-token window, the sink, the new token's compressor input; every query
+    sits at t = L, so all L/m' entries are visible."""
+    import torch
+
+    g = rng(seed, device=device)
+    B, L, c, H = wl.B, wl.L, wl.c, wl.H
+    d = dict(attn_inputs(g, B, 1, L // wl.m, H, c, Lw=wl.window))
     d["q_pos"] = torch.full((B, 1), L, dtype=torch.int32, device=device)
     d["win_pos0"] = torch.full((B,), L - wl.window + 1, dtype=torch.int32, device=device)
     d["c_new"] = g.normal((B, 1, c), dtype="bf16")

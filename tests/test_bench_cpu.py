@@ -23,11 +23,14 @@ def _small(cfg, **kw):
     (2, dict(B=2, L=300, k=32, window=16), "decode"),
     (5, dict(B=2, L=300, k=32, window=16), "decode"),
     (4, dict(B=2, L=512, k=32, window=16, n_keep_blocks=16), "hier"),
+    (6, dict(B=2, L=128 * 40, window=16), "hca"),
 ])
 def test_cpu_baseline_decode_kinds(cfg, kw, build):
     wl = _small(cfg, **kw)
     if build == "hier":
         d = W.hier_inputs(wl, 3, device="cpu")
+    elif build == "hca":
+        d = W.hca_inputs(wl, 3, device="cpu")
     else:
         d = W.decode_inputs(wl, 3, device="cpu")
     r = bench.cpu_baseline(torch, wl, d, 0.05)
