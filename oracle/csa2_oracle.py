@@ -362,7 +362,25 @@ def dense_attn(q, q_pos, kv, m_prime, win=None, win_pos0=None, window=128, sink=
                        rope_dims=rope_dims, theta=theta, eps=eps, scale=scale, q_norm=q_norm)
 
 
+def grouped_out_proj(o, w1, w2):
+    """Grouped output projection after the core attention ([DSA-to-CSA notes] section
+    "Grouped output projection"): the n_h heads' outputs are split into g groups of n_h/g
+    consecutive heads; group j's c*n_h/g values are projected to d_g, the g results are
+    concatenated and projected to d.  o [M, n_h, c]; w1 [g, d_g, c*n_h/g] and w2 [d, g*d_g]
+    hold each projection as (output, input), so y = x @ w.T.
+    Returns (mid [M, g*d_g], out [M, d])."""
+    o = np.asarray(o, np.float64)
+    w1 = np.asarray(w1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    M, n_h, c = o.shape
+    g = w1.shape[0]
+    x = o.reshape(M, g, (n_h // g) * c)
+    mid = np.concatenate([x[:, j] @ w1[j].T for j in range(g)], axis=1)
+    return mid, mid @ w2.T
+
+
 __all__ = [
+    "grouped_out_proj",
     "gated_pool", "gated_pool_weights", "rms_norm", "rope_angles", "rope", "compress", "write_cache",
     "dense_attn",
     "n_visible", "indexer_scores", "topk_indices", "index_topk_full", "block_max",

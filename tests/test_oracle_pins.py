@@ -543,3 +543,33 @@ def test_hca_pipeline_pools_128_token_blocks_with_bias():
     bias[5] = 50.0  # e^50 dominates the other 127 unit terms
     ent_b, _ = O.compress(C, np.zeros((2 * mp, c)), mp, b_a=bias, norm=False)
     np.testing.assert_allclose(ent_b, C.reshape(2, mp, c)[:, 5], rtol=0, atol=1e-15)
+
+
+# =================================================================== grouped output projection
+def test_grouped_out_proj_hand_example():
+    # n_h = 4 heads of c = 1, g = 2 groups, d_g = 1, d = 2: group 0 sees heads 0-1, group 1
+    # heads 2-3; worked by hand
+    o = np.array([[[1.0], [2.0], [3.0], [4.0]]])
+    w1 = np.array([[[1.0, 10.0]], [[100.0, 1000.0]]])  # [g, d_g, 2]
+    w2 = np.array([[1.0, 1.0], [2.0, -1.0]])            # [d, g*d_g]
+    mid, out = O.grouped_out_proj(o, w1, w2)
+    np.testing.assert_array_equal(mid, [[21.0, 4300.0]])
+    np.testing.assert_array_equal(out, [[4321.0, 42.0 - 4300.0]])
+
+
+def test_grouped_out_proj_is_a_block_diagonal_then_dense_product():
+    # the two levels equal one product with a block-diagonal first matrix; with g = 1 it is
+    # two plain matrix products
+    r = _rng(51)
+    M, n_h, c, g, dg, d = 5, 8, 4, 4, 3, 6
+    o = r.standard_normal((M, n_h, c))
+    w1 = r.standard_normal((g, dg, c * n_h // g))
+    w2 = r.standard_normal((d, g * dg))
+    mid, out = O.grouped_out_proj(o, w1, w2)
+    from scipy.linalg import block_diag
+    bd = block_diag(*[w1[j].T for j in range(g)])  # [n_h*c, g*dg]
+    np.testing.assert_allclose(mid, o.reshape(M, -1) @ bd, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, o.reshape(M, -1) @ bd @ w2.T, rtol=1e-12, atol=1e-12)
+    w1b = r.standard_normal((1, dg, n_h * c))
+    mid1, out1 = O.grouped_out_proj(o, w1b, w2[:, :dg])
+    np.testing.assert_allclose(out1, (o.reshape(M, -1) @ w1b[0].T) @ w2[:, :dg].T, rtol=1e-12)
