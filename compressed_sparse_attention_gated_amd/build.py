@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa2.so")
 BUILD_DIR = os.path.join(os.path.dirname(PKG), "_build")
 
-SOURCES = ["api.cpp", "compress.hip", "index.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.cpp", "compress.hip", "index.hip", "topk.hip", "attn.hip", "proj.hip"]
 ARCH = "gfx950"
 
 

@@ -54,13 +54,18 @@ class AttnDesc(C.Structure):
                 ("num_splits", _i), ("dense_m", _i)]
 
 
+class OutProjDesc(C.Structure):
+    _fields_ = [("M", _i), ("n_h", _i), ("c", _i), ("g", _i), ("d_g", _i), ("d", _i), ("o", _vp),
+                ("w1", _vp), ("w2", _vp), ("mid", _vp), ("out", _vp)]
+
+
 class KernelTime(C.Structure):
     _fields_ = [("name", C.c_char * 48), ("ms", C.c_float)]
 
 
 EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk",
            "csa2_hier_workspace_bytes", "csa2_hier_candidates", "csa2_attn_workspace_bytes",
-           "csa2_sparse_attn", "csa2_version", "csa2_last_error", "csa2_profile_enable",
+           "csa2_sparse_attn", "csa2_out_proj", "csa2_version", "csa2_last_error", "csa2_profile_enable",
            "csa2_profile_collect"]
 
 _lib = None
@@ -86,6 +91,7 @@ def lib():
     L.csa2_attn_workspace_bytes.argtypes = [C.POINTER(AttnDesc)]
     L.csa2_attn_workspace_bytes.restype = C.c_size_t
     L.csa2_sparse_attn.argtypes = [C.POINTER(AttnDesc), _vp, C.c_size_t, _vp]
+    L.csa2_out_proj.argtypes = [C.POINTER(OutProjDesc), _vp]
     L.csa2_last_error.restype = C.c_char_p
     L.csa2_profile_enable.argtypes = [_i]
     L.csa2_profile_collect.argtypes = [C.POINTER(KernelTime), _i]
@@ -275,6 +281,23 @@ def csa2_sparse_attn(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N
 def csa2_attn_workspace_bytes(q, q_pos, idx, **kw):
     d = _attn_desc(q, q_pos, idx, **kw)
     return lib().csa2_attn_workspace_bytes(C.byref(d))
+
+
+# ---------------------------------------------------------------------------- output projection
+def csa2_out_proj(o, w1, w2, *, mid=None, out=None, stream=None):
+    """o [..., n_h, c] bf16; w1 [g, d_g, c*n_h/g]; w2 [d, g*d_g] -> (mid [M, g*d_g], out [M, d])."""
+    n_h, c = o.shape[-2], o.shape[-1]
+    M = o.numel() // (n_h * c)
+    g, d_g = w1.shape[0], w1.shape[1]
+    dd = w2.shape[0]
+    if mid is None:
+        mid = torch.empty((M, g * d_g), dtype=torch.bfloat16, device=o.device)
+    if out is None:
+        out = torch.empty((M, dd), dtype=torch.bfloat16, device=o.device)
+    d = OutProjDesc(M=M, n_h=n_h, c=c, g=g, d_g=d_g, d=dd, o=_p(o), w1=_p(w1), w2=_p(w2), mid=_p(mid),
+                    out=_p(out))
+    _check(lib().csa2_out_proj(C.byref(d), _stream(stream)))
+    return mid, out
 
 
 # ---------------------------------------------------------------------------- kernel timing

@@ -393,3 +393,24 @@ int csa2_sparse_attn(const csa2_attn_desc* d, void* ws, size_t ws_bytes, void* s
 }
 
 }  // extern "C"
+
+// --------------------------------------------------------------- output projection
+static int check_out_proj(const csa2_out_proj_desc* d) {
+  if (!d) return fail(CSA2_ERR_INVALID, "out_proj: null descriptor");
+  if (d->M < 0 || d->n_h < 1 || d->c < 1 || d->g < 1 || d->d_g < 1 || d->d < 1)
+    return fail(CSA2_ERR_INVALID, "out_proj: need M >= 0 and positive n_h, c, g, d_g, d");
+  if (d->n_h % d->g != 0) return fail(CSA2_ERR_INVALID, "out_proj: n_h must be a multiple of g");
+  if ((long long)d->c * (d->n_h / d->g) % 64 != 0 || (long long)d->g * d->d_g % 64 != 0)
+    return fail(CSA2_ERR_UNSUPPORTED, "out_proj: c*n_h/g and g*d_g must be multiples of 64");
+  if (d->M == 0) return CSA2_OK;
+  if (!d->o || !d->w1 || !d->w2 || !d->mid || !d->out)
+    return fail(CSA2_ERR_INVALID, "out_proj: o, w1, w2, mid and out are required");
+  return CSA2_OK;
+}
+
+int csa2_out_proj(const csa2_out_proj_desc* d, void* stream) {
+  int rc = check_out_proj(d);
+  if (rc != CSA2_OK) return rc;
+  if (d->M == 0) return ok();
+  return hip_status(launch_out_proj(*d, (hipStream_t)stream), "out_proj");
+}

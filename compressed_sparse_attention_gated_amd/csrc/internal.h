@@ -19,6 +19,8 @@ struct ScopedProf {
   ~ScopedProf() { prof_end(s); }
 };
 
+// ---- grouped output projection (proj.hip)
+hipError_t launch_out_proj(const csa2_out_proj_desc& d, hipStream_t s);
 // ---- compressor (compress.hip)
 hipError_t launch_compress(const csa2_compress_desc& d, hipStream_t s);
 

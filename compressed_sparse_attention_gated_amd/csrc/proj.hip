@@ -1,0 +1,136 @@
+// Grouped output projection after the core attention ([DSA-to-CSA notes], section "Grouped
+// output projection"): the n_h heads' outputs are split into g groups of n_h/g consecutive
+// heads; group j's c*n_h/g values are projected to d_g, and the g*d_g concatenation is
+// projected to d.  Both levels are C = A * W^T products with the weights stored (output,
+// input), so each operand row is contiguous along the contraction and feeds the MFMA
+// operands straight from memory:
+//   level 1: g products in one launch (blockIdx.z = group), A = the group's slice of the
+//            attention output rows, C = the group's slice of `mid`;
+//   level 2: one product, A = mid.
+//
+// gemm_nt: a wave owns a 32 x 64 tile of C as two v_mfma_f32_32x32x16_bf16 accumulators.
+// Lane l reads row l % 32 of A and of each 32-row W block, 16 bytes at k offset 8 * (l / 32)
+// of every 16-wide k step (the MFMA operand layout), through a 4-deep ring of 32-k steps.  Rows past M or N are read clamped and never stored.  Workgroup
+// = 4 waves: 1 x 4 along N when M <= 32 (decode: each weight row is read once, the
+// launch streams the weights), 2 x 2 otherwise.
+
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kPT = 256;
+constexpr int kKStep = 32;  // k per pipeline step (2 MFMA steps of 16)
+constexpr int kDepth = 4;   // pipeline steps in flight
+
+struct GemmArgs {
+  int M, N, K;
+  const uint16_t* A;
+  int64_t lda, sa;  // row stride, batch stride (elements)
+  const uint16_t* W;
+  int64_t sw;       // batch stride; rows are K long
+  uint16_t* C;
+  int64_t ldc, sc;
+};
+
+template <int WM, int WN>
+__global__ void __launch_bounds__(kPT) gemm_nt(GemmArgs p) {
+  const int z = blockIdx.z;
+  const uint16_t* A = p.A + z * p.sa;
+  const uint16_t* W = p.W + z * p.sw;
+  uint16_t* Cz = p.C + z * p.sc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+  const int m0 = blockIdx.y * 32 * WM + 32 * wm;
+  const int n0 = blockIdx.x * 64 * WN + 64 * wn;
+  const int r = lane & 31, h = lane >> 5;
+  const uint16_t* pa = A + (size_t)min(m0 + r, p.M - 1) * p.lda + 8 * h;
+  const uint16_t* pw0 = W + (size_t)min(n0 + r, p.N - 1) * p.K + 8 * h;
+  const uint16_t* pw1 = W + (size_t)min(n0 + 32 + r, p.N - 1) * p.K + 8 * h;
+  const int nk = p.K / kKStep;
+  f32x16 acc0 = {}, acc1 = {};
+  // k steps of 32 through a kDepth-deep register ring: step t is used while the next
+  // kDepth - 1 load.  Each load goes into the slot just used (no copies for the compiler to
+  // fold back into load-then-wait), every trip issues the same loads (steps past the end
+  // reload the last one, never used), and the last steps drain after the loop.
+  struct Raw {
+    uint4 a[2], w0[2], w1[2];
+  };
+  auto load = [&](int t, Raw& q) {
+    const int k = min(t, nk - 1) * kKStep;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      q.a[s] = *reinterpret_cast<const uint4*>(pa + k + 16 * s);
+      q.w0[s] = *reinterpret_cast<const uint4*>(pw0 + k + 16 * s);
+      q.w1[s] = *reinterpret_cast<const uint4*>(pw1 + k + 16 * s);
+    }
+  };
+  auto use = [&](const Raw& q) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(q.a[s]), as_bf16x8(q.w0[s]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(q.a[s]), as_bf16x8(q.w1[s]), acc1, 0, 0, 0);
+    }
+  };
+  Raw ring[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    load(i, ring[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int t = 0;
+  for (; t + kDepth - 1 < nk; t += kDepth) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      load(t + i + kDepth - 1, ring[(i + kDepth - 1) % kDepth]);
+      use(ring[i]);
+    }
+  }
+  // ring[i] holds step t + i; fewer than kDepth of them are below nk
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    if (t + i >= nk) break;
+    use(ring[i]);
+  }
+  // C layout of a 32 x 32 accumulator: lane l holds column l % 32, register i row
+  // 8 * (i / 4) + 4 * (l / 32) + i % 4
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m0 + 8 * (i / 4) + 4 * h + (i % 4);
+    if (m >= p.M) continue;
+    uint16_t* crow = Cz + (size_t)m * p.ldc;
+    if (n0 + r < p.N) crow[n0 + r] = f32_to_bf16_bits(acc0[i]);
+    if (n0 + 32 + r < p.N) crow[n0 + 32 + r] = f32_to_bf16_bits(acc1[i]);
+  }
+}
+
+hipError_t launch_gemm(const GemmArgs& p, int batch, hipStream_t s, const char* name) {
+  ScopedProf prof(s, name);
+  if (p.M <= 32) {
+    dim3 grid((p.N + 255) / 256, (p.M + 31) / 32, batch);
+    hipLaunchKernelGGL((gemm_nt<1, 4>), grid, dim3(kPT), 0, s, p);
+  } else {
+    dim3 grid((p.N + 127) / 128, (p.M + 63) / 64, batch);
+    hipLaunchKernelGGL((gemm_nt<2, 2>), grid, dim3(kPT), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_out_proj(const csa2_out_proj_desc& d, hipStream_t s) {
+  if (d.M == 0) return hipSuccess;
+  if (!d.o || !d.w1 || !d.w2 || !d.mid || !d.out) return hipErrorInvalidValue;
+  const int kg = d.c * (d.n_h / d.g);  // inputs per group
+  const int k2 = d.g * d.d_g;
+  GemmArgs l1{d.M, d.d_g, kg, (const uint16_t*)d.o, (int64_t)d.n_h * d.c, kg,
+              (const uint16_t*)d.w1, (int64_t)d.d_g * kg, (uint16_t*)d.mid, k2, d.d_g};
+  hipError_t e = launch_gemm(l1, d.g, s, "out_proj_groups");
+  if (e != hipSuccess) return e;
+  GemmArgs l2{d.M, d.d, k2, (const uint16_t*)d.mid, k2, 0, (const uint16_t*)d.w2, 0, (uint16_t*)d.out, d.d, 0};
+  return launch_gemm(l2, 1, s, "out_proj_concat");
+}
+
+}  // namespace csa2

@@ -287,6 +287,27 @@ typedef struct {
 CSA2_API int csa2_profile_enable(int on);
 CSA2_API int csa2_profile_collect(csa2_kernel_time *out, int max);
 
+/* ------------------------------------------------------------------ output projection
+ * csa2_out_proj: the grouped output projection that follows the core attention ([DSA-to-CSA
+ *   notes], section "Grouped output projection"): the n_h heads are split into g groups of
+ *   n_h/g consecutive heads; group j's c*n_h/g output values are projected to d_g, and the
+ *   concatenation of the g results (g*d_g values) is projected to d.
+ * Arguments (all bf16, fp32 accumulation, results rounded to nearest even):
+ *   o: [M, n_h, c], the attention output of M query tokens (csa2_sparse_attn's out).
+ *   w1: [g, d_g, c*n_h/g]: group j's projection stored (output, input): mid_j = o_j w1[j]^T.
+ *   w2: [d, g*d_g], likewise: out = mid w2^T.
+ *   mid: [M, g*d_g], caller-provided: receives the first level (the second reads it back).
+ *   out: [M, d].
+ * Supported: n_h % g == 0; c*n_h/g and g*d_g multiples of 64.
+ */
+typedef struct {
+  int M, n_h, c, g, d_g, d;
+  const void *o, *w1, *w2;
+  void *mid, *out;
+} csa2_out_proj_desc;
+
+CSA2_API int csa2_out_proj(const csa2_out_proj_desc *d, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

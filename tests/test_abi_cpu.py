@@ -46,6 +46,7 @@ def _c_layout():
         "csa2_index_desc": [f[0] for f in csa2.IndexDesc._fields_],
         "csa2_hier_desc": [f[0] for f in csa2.HierDesc._fields_],
         "csa2_attn_desc": [f[0] for f in csa2.AttnDesc._fields_],
+        "csa2_out_proj_desc": [f[0] for f in csa2.OutProjDesc._fields_],
         "csa2_kernel_time": [f[0] for f in csa2.KernelTime._fields_],
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void){"]
@@ -66,7 +67,7 @@ def test_descriptor_layouts_match_header():
     lay = _c_layout()
     for s, cls in [("csa2_compress_desc", csa2.CompressDesc), ("csa2_index_desc", csa2.IndexDesc),
                    ("csa2_hier_desc", csa2.HierDesc), ("csa2_attn_desc", csa2.AttnDesc),
-                   ("csa2_kernel_time", csa2.KernelTime)]:
+                   ("csa2_out_proj_desc", csa2.OutProjDesc), ("csa2_kernel_time", csa2.KernelTime)]:
         assert lay[(s, "size")] == C.sizeof(cls), s
         for f, _ in cls._fields_:
             assert lay[(s, f)] == getattr(cls, f).offset, (s, f)
@@ -201,3 +202,14 @@ def test_attn_validation(L):
 
 def test_profile_collect_empty(L):
     assert csa2.csa2_profile_collect() == []
+
+
+def test_out_proj_validation(L):
+    base = dict(M=4, n_h=8, c=64, g=2, d_g=64, d=64, o=FAKE, w1=FAKE, w2=FAKE, mid=FAKE, out=FAKE)
+    for over, code in [(dict(g=3), csa2.CSA2_ERR_INVALID), (dict(c=8), csa2.CSA2_ERR_UNSUPPORTED),
+                       (dict(d_g=8, g=2), csa2.CSA2_ERR_UNSUPPORTED), (dict(mid=None), csa2.CSA2_ERR_INVALID),
+                       (dict(d=0), csa2.CSA2_ERR_INVALID)]:
+        d = csa2.OutProjDesc(**{**base, **over})
+        assert L.csa2_out_proj(C.byref(d), None) == code, (over, csa2.last_error())
+    d = csa2.OutProjDesc(**{**base, "M": 0, "o": None})
+    assert L.csa2_out_proj(C.byref(d), None) == csa2.CSA2_OK
