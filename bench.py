@@ -303,6 +303,46 @@ def write_path_stage(torch, C, wl, d, reps=20):
             "avg_us": us, "algorithmic_bytes": nbytes, "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
 
 
+def out_proj_stage(torch, C, wl, reps=10):
+    """The grouped output projection after the attention (csa2_out_proj), at the pages'
+    V4-Flash shape (64 heads x 512 -> 8 groups of 1,024 -> 4,096), for the step's query
+    tokens; random bf16 weights.  Not part of the step (the pages put it after the path)."""
+    dev = "cuda"
+    M = wl.n_tokens if wl.kind == "prefill" else wl.B
+    g_, d_g, d = 8, 1024, 4096
+    kg = wl.H * wl.c // g_
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    o = torch.randn((M, wl.H, wl.c), generator=gen, device=dev).to(torch.bfloat16)
+    w1 = (torch.randn((g_, d_g, kg), generator=gen, device=dev) * kg ** -0.5).to(torch.bfloat16)
+    w2 = (torch.randn((d, g_ * d_g), generator=gen, device=dev) * (g_ * d_g) ** -0.5).to(torch.bfloat16)
+    mid = torch.empty((M, g_ * d_g), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    C.csa2_out_proj(o, w1, w2, mid=mid, out=out)
+    torch.cuda.synchronize()
+    C.csa2_profile_enable(True)
+    for _ in range(reps):
+        C.csa2_out_proj(o, w1, w2, mid=mid, out=out)
+    torch.cuda.synchronize()
+    recs = C.csa2_profile_collect(1 << 12)
+    C.csa2_profile_enable(False)
+    per = {}
+    for n, ms in recs:
+        per.setdefault(n, []).append(ms)
+    us = sum(float(np.mean(v)) for v in per.values()) * 1e3
+    flops = 2.0 * M * (wl.H * wl.c * d_g + g_ * d_g * d)
+    nbytes = 2 * (w1.numel() + w2.numel() + o.numel() + 2 * mid.numel() + out.numel())
+    res = {"kernels": {k: float(np.mean(v)) * 1e3 for k, v in per.items()}, "tokens": M,
+           "shape": f"{wl.H}x{wl.c} -> {g_} groups x {d_g} -> {d}", "avg_us": us, "flops": flops,
+           "algorithmic_bytes": nbytes, "TFLOP_per_s": flops / (us * 1e-6) / 1e12,
+           "GB_per_s": nbytes / (us * 1e-6) / 1e9}
+    if wl.kind == "prefill":
+        res["frac_mfma"] = res["TFLOP_per_s"] / BF16_MFMA_PEAK_TFLOPS
+    else:
+        res["frac_hbm"] = res["GB_per_s"] / HBM_PEAK_GBS
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -373,6 +413,8 @@ def main():
                                  "frac_hbm": ab / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if wl.kind not in ("hier", "hca_decode"):
         stages["write_path"] = write_path_stage(torch, C, wl, insts[0])
+    if wl.kind != "hier":
+        stages["out_proj"] = out_proj_stage(torch, C, wl)
     prefill = wl.kind == "prefill"
     units = wl.n_tokens if prefill else wl.B
     value = units / (ms * 1e-3)

@@ -10,9 +10,10 @@
 //
 // gemm_nt: a wave owns a 32 x 64 tile of C as two v_mfma_f32_32x32x16_bf16 accumulators.
 // Lane l reads row l % 32 of A and of each 32-row W block, 16 bytes at k offset 8 * (l / 32)
-// of every 16-wide k step (the MFMA operand layout), through a 4-deep ring of 32-k steps.  Rows past M or N are read clamped and never stored.  Workgroup
-// = 4 waves: 1 x 4 along N when M <= 32 (decode: each weight row is read once, the
-// launch streams the weights), 2 x 2 otherwise.
+// of every 16-wide k step (the MFMA operand layout), through a 4-deep ring of 32-k steps.
+// Rows past M or N are read clamped and never stored.  Workgroup = 4 waves, 2 x 2 (1 x 4
+// along N when M <= 32 and the contraction does not split evenly; gemm_nt_splitk below
+// takes the other few-row products).
 
 #include "common.h"
 #include "internal.h"
@@ -106,9 +107,82 @@ __global__ void __launch_bounds__(kPT) gemm_nt(GemmArgs p) {
   }
 }
 
+// Few rows (decode: one token per sequence): the product is a stream over the weights.  A
+// workgroup of kSplit waves owns one 32 x 32 tile of C; wave w takes the w-th 1/kSplit of
+// the contraction through the same register ring, and the partial tiles meet in LDS, added
+// in wave order (deterministic).  N/32 x batch workgroups, each reading its 32 weight rows
+// once.
+constexpr int kSplit = 8;
+__global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
+  __shared__ float part[kSplit][16][64];
+  const int z = blockIdx.z;
+  const uint16_t* A = p.A + z * p.sa;
+  const uint16_t* W = p.W + z * p.sw;
+  uint16_t* Cz = p.C + z * p.sc;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * 32;
+  const int r = lane & 31, h = lane >> 5;
+  const int kspan = p.K / kSplit;
+  const uint16_t* pa = A + (size_t)min(r, p.M - 1) * p.lda + wave * kspan + 8 * h;
+  const uint16_t* pw = W + (size_t)min(n0 + r, p.N - 1) * p.K + wave * kspan + 8 * h;
+  const int nk = kspan / kKStep;
+  f32x16 acc = {};
+  struct Raw {
+    uint4 a[2], w[2];
+  };
+  auto load = [&](int t, Raw& q) {
+    const int k = min(t, nk - 1) * kKStep;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      q.a[s] = *reinterpret_cast<const uint4*>(pa + k + 16 * s);
+      q.w[s] = *reinterpret_cast<const uint4*>(pw + k + 16 * s);
+    }
+  };
+  auto use = [&](const Raw& q) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(q.a[s]), as_bf16x8(q.w[s]), acc, 0, 0, 0);
+  };
+  Raw ring[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    load(i, ring[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int t = 0;
+  for (; t + kDepth - 1 < nk; t += kDepth) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      load(t + i + kDepth - 1, ring[(i + kDepth - 1) % kDepth]);
+      use(ring[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    if (t + i >= nk) break;
+    use(ring[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) part[wave][i][lane] = acc[i];
+  __syncthreads();
+  // thread (i, l) of the first 16 x 64 adds the waves' register i of lane l, in wave order
+  for (int e = threadIdx.x; e < 16 * 64; e += 64 * kSplit) {
+    const int i = e / 64, l = e % 64;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSplit; ++w) v += part[w][i][l];
+    const int m = 8 * (i / 4) + 4 * (l / 32) + (i % 4), n = n0 + (l & 31);
+    if (m < p.M && n < p.N) Cz[(size_t)m * p.ldc + n] = f32_to_bf16_bits(v);
+  }
+}
+
 hipError_t launch_gemm(const GemmArgs& p, int batch, hipStream_t s, const char* name) {
   ScopedProf prof(s, name);
-  if (p.M <= 32) {
+  if (p.M <= 32 && p.K % (kSplit * kKStep) == 0) {
+    dim3 grid((p.N + 31) / 32, 1, batch);
+    hipLaunchKernelGGL(gemm_nt_splitk, grid, dim3(64 * kSplit), 0, s, p);
+  } else if (p.M <= 32) {
     dim3 grid((p.N + 255) / 256, (p.M + 31) / 32, batch);
     hipLaunchKernelGGL((gemm_nt<1, 4>), grid, dim3(kPT), 0, s, p);
   } else {
