@@ -12,8 +12,8 @@
 // Lane l reads row l % 32 of A and of each 32-row W block, 16 bytes at k offset 8 * (l / 32)
 // of every 16-wide k step (the MFMA operand layout), through a 4-deep ring of 32-k steps.
 // Rows past M or N are read clamped and never stored.  Workgroup = 4 waves, 2 x 2 (1 x 4
-// along N when M <= 32 and the contraction does not split evenly; gemm_nt_splitk below
-// takes the other few-row products).
+// along N when M <= 32).  It serves the shapes the two kernels below do not: few rows with a
+// contraction that does not split evenly (gemm_nt_splitk), many rows (gemm_nt_lds).
 
 #include "common.h"
 #include "internal.h"
@@ -177,11 +177,97 @@ __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
   }
 }
 
+// Many rows (prefill): a 128 x 128 tile of C per workgroup of 4 waves (2 x 2, each 64 x 64
+// as 2 x 2 accumulators), the operands shared through LDS.  A k stage of 64 is loaded
+// coalesced (8 threads per 128-byte row) into registers while the previous stage is used,
+// then stored into the other LDS buffer; one barrier per stage.  Rows are padded to 144
+// bytes so the 16-byte operand reads of 8 consecutive rows fall in distinct banks.
+constexpr int kTM = 128, kTN = 128, kTK = 64;
+constexpr int kLdsPitch = kTK + 8;  // bf16 elements per LDS row
+__global__ void __launch_bounds__(256, 2) gemm_nt_lds(GemmArgs p) {
+  __shared__ __align__(16) uint16_t As[2][kTM][kLdsPitch];
+  __shared__ __align__(16) uint16_t Ws[2][kTN][kLdsPitch];
+  const int z = blockIdx.z;
+  const uint16_t* A = p.A + z * p.sa;
+  const uint16_t* W = p.W + z * p.sw;
+  uint16_t* Cz = p.C + z * p.sc;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+  const int r = lane & 31, h = lane >> 5;
+  // global -> register staging: thread covers 16-byte column (tid % 8) of rows tid / 8 + 32 i
+  const int gc = tid & 7, gr = tid >> 3;
+  const uint16_t* ga[4];
+  const uint16_t* gw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ga[i] = A + (size_t)min(m0 + gr + 32 * i, p.M - 1) * p.lda + 8 * gc;
+    gw[i] = W + (size_t)min(n0 + gr + 32 * i, p.N - 1) * p.K + 8 * gc;
+  }
+  const int nkt = p.K / kTK;
+  uint4 ra[4], rw[4];
+  f32x16 acc[2][2] = {};
+#define CSA2_GLOAD(kt_)                                                        \
+  do {                                                                         \
+    const int k_ = (kt_) * kTK;                                                \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                            \
+      ra[i] = *reinterpret_cast<const uint4*>(ga[i] + k_);                     \
+      rw[i] = *reinterpret_cast<const uint4*>(gw[i] + k_);                     \
+    }                                                                          \
+  } while (0)
+#define CSA2_LSTORE(buf_)                                                      \
+  do {                                                                         \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                            \
+      *reinterpret_cast<uint4*>(&As[buf_][gr + 32 * i][8 * gc]) = ra[i];       \
+      *reinterpret_cast<uint4*>(&Ws[buf_][gr + 32 * i][8 * gc]) = rw[i];       \
+    }                                                                          \
+  } while (0)
+  CSA2_GLOAD(0);
+  CSA2_LSTORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    CSA2_GLOAD(min(kt + 1, nkt - 1));  // the next stage (the last one reloads itself, unused)
+#pragma unroll
+    for (int s = 0; s < kTK / 16; ++s) {
+      bf16x8 af[2], wf[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        af[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&As[cur][64 * wm + 32 * b + r][16 * s + 8 * h]));
+        wf[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ws[cur][64 * wn + 32 * b + r][16 * s + 8 * h]));
+      }
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < 2; ++bn)
+          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], wf[bn], acc[bm][bn], 0, 0, 0);
+    }
+    if (kt + 1 < nkt) CSA2_LSTORE(cur ^ 1);  // the other buffer, last read before the previous barrier
+    __syncthreads();
+  }
+#undef CSA2_GLOAD
+#undef CSA2_LSTORE
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 2; ++bn)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + 64 * wm + 32 * bm + 8 * (i / 4) + 4 * h + (i % 4);
+        const int n = n0 + 64 * wn + 32 * bn + r;
+        if (m < p.M && n < p.N) Cz[(size_t)m * p.ldc + n] = f32_to_bf16_bits(acc[bm][bn][i]);
+      }
+}
+
 hipError_t launch_gemm(const GemmArgs& p, int batch, hipStream_t s, const char* name) {
   ScopedProf prof(s, name);
   if (p.M <= 32 && p.K % (kSplit * kKStep) == 0) {
     dim3 grid((p.N + 31) / 32, 1, batch);
     hipLaunchKernelGGL(gemm_nt_splitk, grid, dim3(64 * kSplit), 0, s, p);
+  } else if (p.M > 32 && p.K % kTK == 0) {
+    dim3 grid((p.N + kTN - 1) / kTN, (p.M + kTM - 1) / kTM, batch);
+    hipLaunchKernelGGL(gemm_nt_lds, grid, dim3(256), 0, s, p);
   } else if (p.M <= 32) {
     dim3 grid((p.N + 255) / 256, (p.M + 31) / 32, batch);
     hipLaunchKernelGGL((gemm_nt<1, 4>), grid, dim3(kPT), 0, s, p);
