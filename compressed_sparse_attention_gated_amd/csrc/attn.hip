@@ -201,10 +201,14 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 
 // ------------------------------------------------------------------ attn_mfma
 constexpr int kC = 512;           // channels
-constexpr int kHG = 32;           // heads per workgroup
+constexpr int kHG = 32;           // heads per split-partial unit (one half of a workgroup)
 constexpr int kTile = 32;         // rows per tile
 constexpr int kRowBytes = kC * 2;
-constexpr int kThreadsM = 256;
+constexpr int kThreadsM = 512;    // 8 waves: two halves of 4, one per 32 heads
+constexpr int kHW = 2 * kHG;       // heads per workgroup
+constexpr int kWaves = kThreadsM / 64;
+constexpr int kPrefRows = kTile / kWaves;          // bf16 rows each wave loads per tile
+constexpr int kFp4Per = kTile * 16 / kThreadsM;    // FP4 16-byte code chunks per thread per tile
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -227,25 +231,26 @@ struct MfmaSmem {
   // two row tiles; the same bytes also stage q_hat ([32 heads][kPitch]) before the loop
   // and the bf16 output tile ([32][512]) after it
   alignas(16) uint8_t tile[2][kTile * kPitch];
-  alignas(16) uint16_t pbuf[kHG][kPPitch];  // P in PV A-operand order (bf16)
-  float wmax[2][kHG];                       // per row half: tile max per head (first valid tile)
-  float omax[2][kHG];                       // per row half: tile max per head (overflow check)
-  float lpart[2][kHG];                      // per row half: sum of p per head
-  float mfin[kHG];
+  alignas(16) uint16_t pbuf[kHW][kPPitch];  // P in PV A-operand order (bf16)
+  float wmax[2][kHW];                       // per row half: tile max per head (first valid tile)
+  float omax[2][kHW];                       // per row half: tile max per head (overflow check)
+  float lpart[2][kHW];                      // per row half: sum of p per head
+  float mfin[kHW];
   float rope_c[64], rope_s[64];             // cos/sin of the query position, per frequency
-  alignas(16) int ovf[4];                   // per wave: a head overflowed its reference
+  alignas(16) int ovf[kWaves];              // per wave: a head overflowed its reference
   int src[kMaxSplitTiles * kTile];          // per slot: >= 0 kv entry id, -2-w window row w, -1 empty
 };
-static_assert(sizeof(MfmaSmem) <= 80 * 1024, "two workgroups per CU");
+static_assert(sizeof(MfmaSmem) <= 80 * 1024, "LDS of one workgroup");
+static_assert(2 * kTile * kPitch >= kHW * kPitch, "q_hat of the workgroup's heads fits the two row tiles");
 
-// registers for one tile in flight.  bf16 rows: wave w owns rows w, w+4, .., w+28 and
-// lane l carries their 16-byte chunk l.  FP4 rows: thread q = tid + 256*i carries code
-// chunk q%16 of row q/16 and the two E4M3 scales of its 32 channels.
+// registers for one tile in flight.  bf16 rows: wave w owns rows w, w+8, .., w+24 and
+// lane l carries their 16-byte chunk l.  FP4 rows: thread q carries code chunk q%16 of row
+// q/16 and the two E4M3 scales of its 32 channels.
 template <bool kFP4>
 struct Prefetch {
-  uint4 v[8];
-  uint4 fc[kFP4 ? 2 : 1];
-  uint32_t fs[kFP4 ? 2 : 1];
+  uint4 v[kPrefRows];
+  uint4 fc[kFP4 ? kFp4Per : 1];
+  uint32_t fs[kFP4 ? kFp4Per : 1];
 };
 
 // Slot -> row source for this split's slots [slot0, slot0 + n): index slot s < k holds its
@@ -299,11 +304,11 @@ __device__ __forceinline__ RowBases row_bases(const AttnDev& a, int b) {
 template <bool kFP4>
 __device__ __forceinline__ void fetch_tile(const RowBases& rb, const int* src, Prefetch<kFP4>& pf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int srow[8];
+  int srow[kPrefRows];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) srow[i] = src[wave + 4 * i];  // all slot reads first, one wait
+  for (int i = 0; i < kPrefRows; ++i) srow[i] = src[wave + kWaves * i];  // all slot reads first, one wait
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kPrefRows; ++i) {
     const int sr = __builtin_amdgcn_readfirstlane(srow[i]);  // uniform per wave
     const uint16_t* base = nullptr;
     if (sr <= -2) base = rb.win + (size_t)(-2 - sr) * kC;
@@ -312,8 +317,8 @@ __device__ __forceinline__ void fetch_tile(const RowBases& rb, const int* src, P
   }
   if constexpr (kFP4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = threadIdx.x + 256 * i;
+    for (int i = 0; i < kFp4Per; ++i) {
+      const int q = threadIdx.x + kThreadsM * i;
       const int r = q >> 4, part = q & 15;
       const int sr = src[r];
       if (sr >= 0) {
@@ -331,15 +336,15 @@ template <bool kFP4>
 __device__ __forceinline__ void commit_tile(const int* src, const Prefetch<kFP4>& pf, uint8_t* tile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = wave + 4 * i;
+  for (int i = 0; i < kPrefRows; ++i) {
+    const int r = wave + kWaves * i;
     const int sr = __builtin_amdgcn_readfirstlane(src[r]);
     if (!kFP4 || sr < 0) *reinterpret_cast<uint4*>(tile + r * kPitch + 16 * lane) = pf.v[i];
   }
   if constexpr (kFP4) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = threadIdx.x + 256 * i;
+    for (int i = 0; i < kFp4Per; ++i) {
+      const int q = threadIdx.x + kThreadsM * i;
       const int r = q >> 4, part = q & 15;
       if (src[r] >= 0) {
         // 32 codes -> channels 32*part .. 32*part+31; scales of groups 2*part, 2*part+1.
@@ -372,11 +377,12 @@ __device__ __forceinline__ void stage_rope(const AttnDev& a, int t_pos, float* r
   if (a.rope_dims > 0 && u < a.rope_dims / 2) rope_cs((double)t_pos, a.rope.f[u], &rc[u], &rs[u]);
 }
 
-// Workgroup = one query x 32 heads x one split of its row slots.  Wave w = (hq, mr):
-// S^T tile rows 16*mr.. x heads 16*hq.. of each 32-row tile; for PV, wave w owns output
-// channels 128*w .. 128*w+127 of all 32 heads.
+// Workgroup = one query x 64 heads x one split of its row slots: two halves of 4 waves,
+// one per 32 heads, share every row tile in LDS (each row is read once per query).  Wave
+// (half, hq, mr): S^T tile rows 16*mr.. x heads 32*half + 16*hq.. of each 32-row tile; for
+// PV, wave (half, w4) owns output channels 128*w4 .. 128*w4+127 of its half's 32 heads.
 template <bool kFP4>
-__global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
+__global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   MfmaSmem& sm = *reinterpret_cast<MfmaSmem*>(smem_raw);
   const int split = blockIdx.y;
@@ -385,10 +391,11 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   const int b = row / a.T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int hq = wave & 1, mr = wave >> 1;
+  const int half = wave >> 2, w4 = wave & 3;
+  const int hq = w4 & 1, mr = w4 >> 1;
   const int tile0 = split * a.tiles_per_split;
   const int rope_lo = kC - a.rope_dims;
-  const int head0 = hg * kHG;
+  const int head0 = hg * kHW;  // the workgroup's first head
   const RowBases rb = row_bases(a, b);
 
   // ---- every global load of the prologue at once: the q rows of this wave's 8 heads, the
@@ -412,7 +419,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   if (tile0 < tile1) fetch_tile<kFP4>(rb, sm.src, pf);
 
   // ---- q_hat = RoPE_t(RMSNorm(q)) * scale * log2(e) -> LDS (bf16) -> B-operand registers
-  uint8_t* qs = sm.tile[0];  // [32 heads][kPitch]
+  uint8_t* qs = sm.tile[0];  // [64 heads][kPitch], across both row tiles
   float qf[8][8];
   float ssq[8];
 #pragma unroll
@@ -451,15 +458,15 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   bf16x8 qreg[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks)
-    qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qs + (16 * hq + li) * kPitch + 64 * ks + 16 * g));
+    qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qs + (32 * half + 16 * hq + li) * kPitch + 64 * ks + 16 * g));
   lds_barrier();
 
   // per-lane LDS byte offsets (tile-relative): A operand row 16*mr + li at chunk g;
   // transpose-read source rows 4g + li/4 (and +16) at channel 128*wave + 4*(li%4)
   const int a_off = (16 * mr + li) * kPitch + 16 * g;
-  const int t_off0 = (4 * g + (li >> 2)) * kPitch + 8 * (li & 3) + 256 * wave;
+  const int t_off0 = (4 * g + (li >> 2)) * kPitch + 8 * (li & 3) + 256 * w4;
   const int t_off1 = t_off0 + 16 * kPitch;
-  const int my_head = 16 * hq + li;  // WG-local head of this lane's S^T column
+  const int my_head = 32 * half + 16 * hq + li;  // WG-local head of this lane's S^T column
 
   float m_use = -INFINITY, l_part = 0.f;  // head my_head, rows of half mr (replicated over g)
   f32x4 oacc[2][8];
@@ -526,20 +533,22 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
           make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       if (lane == 0) sm.ovf[wave] = __ballot(ovf) != 0;
       lds_barrier();
-      const int4 ov = *reinterpret_cast<const int4*>(sm.ovf);
-      if (__builtin_amdgcn_readfirstlane(ov.x | ov.y | ov.z | ov.w)) {
+      const int4 ov0 = *reinterpret_cast<const int4*>(sm.ovf);
+      const int4 ov1 = *reinterpret_cast<const int4*>(sm.ovf + 4);
+      if (__builtin_amdgcn_readfirstlane(ov0.x | ov0.y | ov0.z | ov0.w | ov1.x | ov1.y | ov1.z | ov1.w)) {
         overflow = true;
         m_use = fmaxf(m_use, fmaxf(sm.omax[0][my_head], sm.omax[1][my_head]));  // whole tile
         break;
       }
 
-      // ---- O[:, 128*wave .. +128] += P x V
+      // ---- O[half's heads, 128*w4 .. +128] += P x V
       bf16x8 pa[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) pa[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.pbuf[16 * mt + li][8 * g]));
+      for (int mt = 0; mt < 2; ++mt)
+        pa[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.pbuf[32 * half + 16 * mt + li][8 * g]));
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        // channels 128*wave + 16*nt + (0..15); rows 4g..4g+3 and 16+4g..16+4g+3
+        // channels 128*w4 + 16*nt + (0..15); rows 4g..4g+3 and 16+4g..16+4g+3
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off0 + 32 * nt));
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off1 + 32 * nt));
         const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -560,16 +569,15 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   lds_barrier();
   if (a.splits > 1) {
     // The split's output divided by its own sum (a convex combination of rows, so within
-    // the rows' range) goes out as bf16, staged in LDS for 16-byte stores; attn_combine
-    // weighs the splits by their sums.
-    const size_t pidx = ((size_t)row * a.n_hg + hg) * a.splits + split;
-    uint16_t* ps = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [32][512], contiguous
+    // the rows' range) goes out as bf16, staged in LDS for 16-byte stores, one 32-head unit
+    // per half; attn_combine weighs the splits by their sums.
+    uint16_t* ps = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [64][512], contiguous
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       float inv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int hl = 16 * mt + 4 * g + j;
+        const int hl = 32 * half + 16 * mt + 4 * g + j;
         const float l = sm.lpart[0][hl] + sm.lpart[1][hl];
         inv[j] = l > 0.f ? 1.0f / l : 0.f;
       }
@@ -577,27 +585,32 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          ps[(16 * mt + 4 * g + j) * kC + 128 * wave + 16 * nt + li] = f32_to_bf16_bits(oacc[mt][nt][j] * inv[j]);
+          ps[(32 * half + 16 * mt + 4 * g + j) * kC + 128 * w4 + 16 * nt + li] = f32_to_bf16_bits(oacc[mt][nt][j] * inv[j]);
     }
-    if (threadIdx.x < kHG) {
-      float* pml = a.part_ml + pidx * 2 * kHG;
-      pml[threadIdx.x] = sm.mfin[threadIdx.x];
-      pml[kHG + threadIdx.x] = sm.lpart[0][threadIdx.x] + sm.lpart[1][threadIdx.x];
+    auto pidx_of = [&](int h) { return ((size_t)row * a.n_hg + 2 * hg + h) * a.splits + split; };
+    if (threadIdx.x < kHW) {
+      const int h = threadIdx.x / kHG, hl = threadIdx.x % kHG;
+      float* pml = a.part_ml + pidx_of(h) * 2 * kHG;
+      pml[hl] = sm.mfin[threadIdx.x];
+      pml[kHG + hl] = sm.lpart[0][threadIdx.x] + sm.lpart[1][threadIdx.x];
     }
     lds_barrier();
-    uint4* po = reinterpret_cast<uint4*>(a.part_o + pidx * kHG * kC);
     const uint4* pl = reinterpret_cast<const uint4*>(ps);
-    for (int q = threadIdx.x; q < kHG * kC / 8; q += kThreadsM) po[q] = pl[q];
+    constexpr int kPerHalf = kHG * kC / 8;
+    for (int q = threadIdx.x; q < 2 * kPerHalf; q += kThreadsM) {
+      const int h = q / kPerHalf;
+      reinterpret_cast<uint4*>(a.part_o + pidx_of(h) * kHG * kC)[q - h * kPerHalf] = pl[q];
+    }
     return;
   }
   // single split: normalise, inverse-rotate, stage bf16 output in LDS, coalesced store
-  uint16_t* os = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [32][512], contiguous
+  uint16_t* os = reinterpret_cast<uint16_t*>(sm.tile[0]);  // [64][512], contiguous
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     float inv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int hl = 16 * mt + 4 * g + j;
+      const int hl = 32 * half + 16 * mt + 4 * g + j;
       const float l = sm.lpart[0][hl] + sm.lpart[1][hl], m = sm.mfin[hl];
       float den = l;
       if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + hl] * kLog2e - m);
@@ -605,7 +618,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const int ch = 128 * wave + 16 * nt + li;
+      const int ch = 128 * w4 + 16 * nt + li;
       float cs = 1.f, sn = 0.f;
       const bool rot = a.rope_dims > 0 && ch >= rope_lo;
       if (rot) { cs = sm.rope_c[(ch - rope_lo) >> 1]; sn = -sm.rope_s[(ch - rope_lo) >> 1]; }
@@ -615,11 +628,11 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
         const float other = dpp<kDppXor1>(v);
         float o = v;
         if (rot) o = (ch & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
-        os[(16 * mt + 4 * g + j) * kC + ch] = f32_to_bf16_bits(o);
+        os[(32 * half + 16 * mt + 4 * g + j) * kC + ch] = f32_to_bf16_bits(o);
       }
     }
   }
-  if (a.out_mass && threadIdx.x < kHG) {
+  if (a.out_mass && threadIdx.x < kHW) {
     const float l = sm.lpart[0][threadIdx.x] + sm.lpart[1][threadIdx.x], m = sm.mfin[threadIdx.x];
     float den = l;
     if (a.sink && l > 0.f) den += exp2f(a.sink[head0 + threadIdx.x] * kLog2e - m);
@@ -628,7 +641,7 @@ __global__ void __launch_bounds__(kThreadsM, 2) attn_mfma(AttnDev a) {
   lds_barrier();
   uint4* op = reinterpret_cast<uint4*>((uint16_t*)a.out + ((size_t)row * a.H + head0) * kC);
   const uint4* src = reinterpret_cast<const uint4*>(os);
-  for (int q = threadIdx.x; q < kHG * kC / 8; q += kThreadsM) op[q] = src[q];
+  for (int q = threadIdx.x; q < kHW * kC / 8; q += kThreadsM) op[q] = src[q];
 }
 
 // merge the splits of one query for 4 heads (one head per wave, 8 channels per lane), in
@@ -707,7 +720,7 @@ __global__ void __launch_bounds__(256) attn_combine(AttnDev a) {
 }
 
 bool mfma_ok(const csa2_attn_desc& d) {
-  return d.q_dtype == CSA2_BF16 && d.c == kC && d.H % kHG == 0 &&
+  return d.q_dtype == CSA2_BF16 && d.c == kC && d.H % kHW == 0 &&
          (d.kv_dtype == CSA2_BF16 || d.kv_dtype == CSA2_FP4_E4M3) && d.rope_dims <= 128;
 }
 
@@ -716,8 +729,8 @@ int max_rows(const csa2_attn_desc& d) { return d.k + ((d.win && d.n_win > 0) ? d
 void pick_splits(const csa2_attn_desc& d, int* splits, int* tps) {
   const int rows = d.B * d.T;
   const int n_tiles = (max_rows(d) + kTile - 1) / kTile;
-  const int n_hg = d.H / kHG;
-  int s = d.num_splits > 0 ? d.num_splits : (512 + rows * n_hg - 1) / (rows * n_hg);
+  const int n_wg = d.H / kHW;  // workgroups per (query, split)
+  int s = d.num_splits > 0 ? d.num_splits : (256 + rows * n_wg - 1) / (rows * n_wg);
   if (s < 1) s = 1;
   if (s > n_tiles) s = n_tiles;
   const int min_s = (n_tiles + kMaxSplitTiles - 1) / kMaxSplitTiles;
@@ -813,10 +826,10 @@ hipError_t launch_attn(const csa2_attn_desc& d0, void* ws, size_t ws_bytes, hipS
   const int splits = plan.splits;
   if (d.kv_dtype == CSA2_FP4_E4M3) {
     ScopedProf p(s, "attn_mfma_fp4");
-    hipLaunchKernelGGL(attn_mfma<true>, dim3(rows, splits, a.n_hg), dim3(kThreadsM), lds, s, a);
+    hipLaunchKernelGGL(attn_mfma<true>, dim3(rows, splits, d.H / kHW), dim3(kThreadsM), lds, s, a);
   } else {
     ScopedProf p(s, "attn_mfma");
-    hipLaunchKernelGGL(attn_mfma<false>, dim3(rows, splits, a.n_hg), dim3(kThreadsM), lds, s, a);
+    hipLaunchKernelGGL(attn_mfma<false>, dim3(rows, splits, d.H / kHW), dim3(kThreadsM), lds, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
