@@ -206,48 +206,64 @@ __global__ void __launch_bounds__(256, 2) gemm_nt_lds(GemmArgs p) {
     gw[i] = W + (size_t)min(n0 + gr + 32 * i, p.N - 1) * p.K + 8 * gc;
   }
   const int nkt = p.K / kTK;
-  uint4 ra[4], rw[4];
+  // two register sets of named values (arrays here were placed in scratch memory): stage kt
+  // travels in set kt & 1, loaded one full stage before it is stored into LDS
+  uint4 a00, a01, a02, a03, w00, w01, w02, w03;  // set 0
+  uint4 a10, a11, a12, a13, w10, w11, w12, w13;  // set 1
   f32x16 acc[2][2] = {};
-#define CSA2_GLOAD(kt_)                                                        \
-  do {                                                                         \
-    const int k_ = (kt_) * kTK;                                                \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                            \
-      ra[i] = *reinterpret_cast<const uint4*>(ga[i] + k_);                     \
-      rw[i] = *reinterpret_cast<const uint4*>(gw[i] + k_);                     \
-    }                                                                          \
+#define CSA2_LD(P, i, k_) (*reinterpret_cast<const uint4*>(P[i] + (k_)))
+#define CSA2_GLOAD(S, kt_)                                                               \
+  do {                                                                                   \
+    const int k_ = min((kt_), nkt - 1) * kTK;                                            \
+    a##S##0 = CSA2_LD(ga, 0, k_); a##S##1 = CSA2_LD(ga, 1, k_);                          \
+    a##S##2 = CSA2_LD(ga, 2, k_); a##S##3 = CSA2_LD(ga, 3, k_);                          \
+    w##S##0 = CSA2_LD(gw, 0, k_); w##S##1 = CSA2_LD(gw, 1, k_);                          \
+    w##S##2 = CSA2_LD(gw, 2, k_); w##S##3 = CSA2_LD(gw, 3, k_);                          \
   } while (0)
-#define CSA2_LSTORE(buf_)                                                      \
-  do {                                                                         \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                            \
-      *reinterpret_cast<uint4*>(&As[buf_][gr + 32 * i][8 * gc]) = ra[i];       \
-      *reinterpret_cast<uint4*>(&Ws[buf_][gr + 32 * i][8 * gc]) = rw[i];       \
-    }                                                                          \
+#define CSA2_ST(buf_, i, A_, W_)                                                         \
+  do {                                                                                   \
+    *reinterpret_cast<uint4*>(&As[buf_][gr + 32 * (i)][8 * gc]) = A_;                    \
+    *reinterpret_cast<uint4*>(&Ws[buf_][gr + 32 * (i)][8 * gc]) = W_;                    \
   } while (0)
-  CSA2_GLOAD(0);
-  CSA2_LSTORE(0);
+#define CSA2_LSTORE(S, buf_)                                                             \
+  do {                                                                                   \
+    CSA2_ST(buf_, 0, a##S##0, w##S##0); CSA2_ST(buf_, 1, a##S##1, w##S##1);              \
+    CSA2_ST(buf_, 2, a##S##2, w##S##2); CSA2_ST(buf_, 3, a##S##3, w##S##3);              \
+  } while (0)
+#define CSA2_COMPUTE(cur_)                                                                             \
+  do {                                                                                                 \
+    _Pragma("unroll") for (int s = 0; s < kTK / 16; ++s) {                                             \
+      bf16x8 af[2], wf[2];                                                                             \
+      _Pragma("unroll") for (int b = 0; b < 2; ++b) {                                                  \
+        af[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&As[cur_][64 * wm + 32 * b + r][16 * s + 8 * h])); \
+        wf[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ws[cur_][64 * wn + 32 * b + r][16 * s + 8 * h])); \
+      }                                                                                                \
+      _Pragma("unroll") for (int bm = 0; bm < 2; ++bm)                                                 \
+      _Pragma("unroll") for (int bn = 0; bn < 2; ++bn)                                                 \
+        acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], wf[bn], acc[bm][bn], 0, 0, 0);   \
+    }                                                                                                  \
+  } while (0)
+  CSA2_GLOAD(0, 0);
+  CSA2_LSTORE(0, 0);
+  CSA2_GLOAD(1, 1);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    CSA2_GLOAD(min(kt + 1, nkt - 1));  // the next stage (the last one reloads itself, unused)
-#pragma unroll
-    for (int s = 0; s < kTK / 16; ++s) {
-      bf16x8 af[2], wf[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        af[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&As[cur][64 * wm + 32 * b + r][16 * s + 8 * h]));
-        wf[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&Ws[cur][64 * wn + 32 * b + r][16 * s + 8 * h]));
-      }
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn)
-          acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bm], wf[bn], acc[bm][bn], 0, 0, 0);
-    }
-    if (kt + 1 < nkt) CSA2_LSTORE(cur ^ 1);  // the other buffer, last read before the previous barrier
+  // loads past the last stage reload it (never stored), so every trip issues the same loads
+  for (int kt = 0; kt < nkt; kt += 2) {
+    CSA2_GLOAD(0, kt + 2);                      // set 0 was stored last trip
+    CSA2_COMPUTE(0);
+    if (kt + 1 < nkt) CSA2_LSTORE(1, 1);        // buffer 1: last read before the previous barrier
+    __syncthreads();
+    if (kt + 1 >= nkt) break;
+    CSA2_GLOAD(1, kt + 3);
+    CSA2_COMPUTE(1);
+    if (kt + 2 < nkt) CSA2_LSTORE(0, 0);
     __syncthreads();
   }
+#undef CSA2_LD
 #undef CSA2_GLOAD
+#undef CSA2_ST
 #undef CSA2_LSTORE
+#undef CSA2_COMPUTE
 #pragma unroll
   for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
