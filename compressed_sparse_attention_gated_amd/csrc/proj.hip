@@ -178,9 +178,9 @@ __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
 }
 
 // Many rows (prefill): a 128 x 128 tile of C per workgroup of 4 waves (2 x 2, each 64 x 64
-// as 2 x 2 accumulators), the operands shared through LDS.  A k stage of 64 is loaded
-// coalesced (8 threads per 128-byte row) into registers while the previous stage is used,
-// then stored into the other LDS buffer; one barrier per stage.  Rows are padded to 144
+// as 2 x 2 accumulators), the operands shared through LDS.  k stages of 64 are loaded
+// coalesced (8 threads per 128-byte row) into registers two stages ahead, then stored into
+// the LDS buffer the stage is used from; one barrier per stage.  Rows are padded to 144
 // bytes so the 16-byte operand reads of 8 consecutive rows fall in distinct banks.
 constexpr int kTM = 128, kTN = 128, kTK = 64;
 constexpr int kLdsPitch = kTK + 8;  // bf16 elements per LDS row
