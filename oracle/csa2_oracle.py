@@ -152,6 +152,30 @@ def compress(c_a, z_a, m, *, b_a=None, c_b=None, z_b=None, b_b=None, overlap=Fal
     return out, k_index
 
 
+def compress_packed(c_a, z_a, m, cu_seqlens, *, c_b=None, z_b=None, **kw):
+    """The compressor over packed samples ([DSA-to-CSA notes], the note after the minimal
+    compressor code and the checklist "怎样验证"): samples that share one token stream must not
+    share a compression window, and a sample's tail shorter than m is not completed by the
+    next sample.  Sample s holds tokens [cu[s], cu[s+1]); it is compressed on its own
+    (positions from 0, no history for its first entry) and its floor(len/m) entries follow
+    those of the samples before it.  Returns (entries, k_index or None, cu_entries)."""
+    cu = [int(x) for x in cu_seqlens]
+    outs, iks, cu_e = [], [], [0]
+    for s in range(len(cu) - 1):
+        sl = slice(cu[s], cu[s + 1])
+        extra = dict(kw)
+        if c_b is not None:
+            extra.update(c_b=np.asarray(c_b)[sl], z_b=np.asarray(z_b)[sl], overlap=True)
+        e, k = compress(np.asarray(c_a)[sl], np.asarray(z_a)[sl], m, **extra)
+        outs.append(e)
+        iks.append(k)
+        cu_e.append(cu_e[-1] + e.shape[0])
+    c = np.asarray(c_a).shape[-1]
+    ent = np.concatenate(outs, axis=0) if outs else np.zeros((0, c))
+    kix = None if kw.get("w_ik") is None else np.concatenate(iks, axis=0)
+    return ent, kix, np.array(cu_e, dtype=np.int64)
+
+
 def write_cache(entries, k_index, dst_row, n_rows):
     """The write path into a decode cache: [CSA2 column] "890 字节是怎么来的" stores each
     main-KV entry in 4 bits (E2M1 codes, one E4M3 scale per 16 channels) and the indexer
@@ -382,6 +406,7 @@ def grouped_out_proj(o, w1, w2):
 __all__ = [
     "grouped_out_proj",
     "gated_pool", "gated_pool_weights", "rms_norm", "rope_angles", "rope", "compress", "write_cache",
+    "compress_packed",
     "dense_attn",
     "n_visible", "indexer_scores", "topk_indices", "index_topk_full", "block_max",
     "hier_candidates", "reindex_topk", "reindex_topk_masked", "reuse", "window_rows",

@@ -573,3 +573,34 @@ def test_grouped_out_proj_is_a_block_diagonal_then_dense_product():
     w1b = r.standard_normal((1, dg, n_h * c))
     mid1, out1 = O.grouped_out_proj(o, w1b, w2[:, :dg])
     np.testing.assert_allclose(out1, (o.reshape(M, -1) @ w1b[0].T) @ w2[:, :dg].T, rtol=1e-12)
+
+
+# =================================================================== packed samples
+def test_packed_compressor_hand_example():
+    # two samples in one stream, m = 2, equal logits (block means): sample A = 1, 2, 3 (its
+    # tail token 3 is dropped, not paired with sample B's first token), sample B = 10, 20
+    C = np.array([[1.0], [2.0], [3.0], [10.0], [20.0]])
+    ent, _, cu_e = O.compress_packed(C, np.zeros_like(C), 2, [0, 3, 5], norm=False)
+    np.testing.assert_array_equal(ent, [[1.5], [15.0]])
+    np.testing.assert_array_equal(cu_e, [0, 1, 2])
+    # the flat stream would have paired 3 with 10
+    flat, _ = O.compress(C[:4], np.zeros((4, 1)), 2, norm=False)
+    assert flat[1, 0] == 6.5
+
+
+def test_packed_compressor_overlap_history_stops_at_sample_start():
+    # with overlap, a sample's first entry has no history even when another sample precedes
+    # it; a sample of fewer than m tokens yields no entry
+    r = _rng(61)
+    m, c = 2, 4
+    lens = [5, 1, 4]
+    n = sum(lens)
+    ca, za, cb, zb = (r.standard_normal((n, c)) for _ in range(4))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    ent, _, cu_e = O.compress_packed(ca, za, m, cu, c_b=cb, z_b=zb, norm=False)
+    np.testing.assert_array_equal(cu_e, [0, 2, 2, 4])
+    own, _ = O.compress(ca[6:10], za[6:10], m, c_b=cb[6:10], z_b=zb[6:10], overlap=True, norm=False)
+    np.testing.assert_allclose(ent[2:4], own, rtol=0, atol=0)
+    # the third sample's first entry: no history, so the same as without overlap
+    no_hist, _ = O.compress(ca[6:8], za[6:8], m, norm=False)
+    np.testing.assert_allclose(ent[2], no_hist[0], rtol=1e-15, atol=1e-15)
