@@ -29,7 +29,8 @@ class CompressDesc(C.Structure):
                 ("out", _vp), ("out_batch_stride", _i64), ("w_ik", _vp), ("d_index", _i),
                 ("out_ik", _vp), ("out_ik_batch_stride", _i64), ("dst_row", _vp),
                 ("out_codes", _vp), ("out_scales", _vp), ("ik_codes", _vp), ("ik_scales", _vp),
-                ("q_rows", _i64), ("cb0", _vp), ("zb0", _vp)]
+                ("q_rows", _i64), ("cb0", _vp), ("zb0", _vp), ("cu_seqlens", _vp), ("n_samples", _i),
+                ("out_cu_entries", _vp)]
 
 
 class IndexDesc(C.Structure):
@@ -139,13 +140,15 @@ def version() -> int:
 def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, norm=True,
                   eps=1e-6, rope_dims=0, rope_theta=10000.0, out=None, w_ik=None, out_ik=None,
                   dst_row=None, out_codes=None, out_scales=None, ik_codes=None, ik_scales=None,
-                  cb0=None, zb0=None, plain_out=True, stream=None):
+                  cb0=None, zb0=None, cu_seqlens=None, out_cu_entries=None, plain_out=True, stream=None):
     """ca, za (cb, zb): [B, n, c] fp32/bf16 -> (out [B, n//m, c], out_ik [B, n//m, d_I] or None).
 
     Write path: out_codes / out_scales [B, rows, c/2] / [B, rows, c/16] (FP4 entries) and
     ik_codes / ik_scales [B, rows, d_I/2] / [B, rows, d_I/32] (MXFP4 K_I), entry i of
     sequence b at row dst_row[b] + i; cb0 / zb0 [B, m, c]: with overlap, the history rows of
-    entry 0 (the block before it).  With plain_out=False and quantised planes given, the
+    entry 0 (the block before it).  cu_seqlens [S+1] (int32, B = 1): packed samples, each
+    compressed on its own; out gets n//m rows (an upper bound), out_cu_entries [S+1] the
+    samples' entry offsets.  With plain_out=False and quantised planes given, the
     plain outputs are not allocated (returned as None) unless passed."""
     B, n, c = ca.shape
     ne = n // m
@@ -168,7 +171,9 @@ def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, n
                      out_ik_batch_stride=out_ik.stride(0) if out_ik is not None else 0,
                      dst_row=_p(dst_row), out_codes=_p(out_codes), out_scales=_p(out_scales),
                      ik_codes=_p(ik_codes), ik_scales=_p(ik_scales), q_rows=q_rows, cb0=_p(cb0),
-                     zb0=_p(zb0))
+                     zb0=_p(zb0), cu_seqlens=_p(cu_seqlens),
+                     n_samples=cu_seqlens.numel() - 1 if cu_seqlens is not None else 0,
+                     out_cu_entries=_p(out_cu_entries))
     _check(lib().csa2_compress(C.byref(d), _stream(stream)))
     return out, out_ik
 

@@ -126,7 +126,7 @@ static int check_compress(const csa2_compress_desc* d) {
   if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return fail(CSA2_ERR_INVALID, "compress: rope_theta must be > 0");
   if (d->norm && !(d->eps >= 0.f)) return fail(CSA2_ERR_INVALID, "compress: eps must be >= 0");
   const long long n_ent = (long long)d->B * (d->n / d->m);
-  if (n_ent == 0) return CSA2_OK;
+  if (n_ent == 0 && !(d->cu_seqlens && d->out_cu_entries)) return CSA2_OK;
   if (!d->ca || !d->za) return fail(CSA2_ERR_INVALID, "compress: ca and za are required");
   if (!d->out && !d->out_codes) return fail(CSA2_ERR_INVALID, "compress: out or out_codes is required");
   if (!d->out_codes != !d->out_scales)
@@ -138,6 +138,12 @@ static int check_compress(const csa2_compress_desc* d) {
   if (d->q_rows < 0) return fail(CSA2_ERR_INVALID, "compress: q_rows must be >= 0");
   if (d->overlap && (!d->cb || !d->zb)) return fail(CSA2_ERR_INVALID, "compress: overlap needs cb and zb");
   if (!d->cb0 != !d->zb0) return fail(CSA2_ERR_INVALID, "compress: cb0 and zb0 go together");
+  if (d->cu_seqlens) {
+    if (d->B != 1) return fail(CSA2_ERR_INVALID, "compress: packed samples (cu_seqlens) need B == 1");
+    if (d->n_samples < 1 || d->n_samples > CSA2_MAX_PACKED_SAMPLES)
+      return fail(CSA2_ERR_INVALID, "compress: n_samples must be in [1, %d]", CSA2_MAX_PACKED_SAMPLES);
+    if (d->cb0) return fail(CSA2_ERR_INVALID, "compress: cb0 / zb0 do not combine with cu_seqlens");
+  }
   if (d->cb0 && !d->overlap) return fail(CSA2_ERR_INVALID, "compress: cb0 and zb0 need overlap");
   if (d->w_ik) {
     if (!d->out_ik && !d->ik_codes) return fail(CSA2_ERR_INVALID, "compress: w_ik needs out_ik or ik_codes");
@@ -161,7 +167,7 @@ static int check_compress(const csa2_compress_desc* d) {
 int csa2_compress(const csa2_compress_desc* d, void* stream) {
   int rc = check_compress(d);
   if (rc != CSA2_OK) return rc;
-  if ((long long)d->B * (d->n / d->m) == 0) return ok();
+  if ((long long)d->B * (d->n / d->m) == 0 && !(d->cu_seqlens && d->out_cu_entries)) return ok();
   return hip_status(launch_compress(*d, (hipStream_t)stream), "compress");
 }
 

@@ -20,6 +20,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kRowsPerWG = 32;
+constexpr int kMaxSamples = CSA2_MAX_PACKED_SAMPLES;  // packed samples per call (LDS offsets)
 
 template <typename T>
 struct Ld;
@@ -107,6 +108,63 @@ __device__ __forceinline__ float max32(float v) {
   return fmaxf(a, b);
 }
 
+// Packed samples: E[s] = number of entries of the samples before s (each sample of len
+// tokens gives floor(len / m) entries), E[ns] the total; an exclusive scan over the
+// workgroup (each thread a contiguous run of samples), written to LDS.
+// sample s's tokens [lo, lo + len) of an n-token stream: its bounds clamped into [0, n] and
+// made non-decreasing, so no access leaves the stream whatever the caller's offsets hold
+__device__ __forceinline__ void sample_span(const int32_t* __restrict__ cu, int s, int n, int* lo, int* len) {
+  const int a = min(max(cu[s], 0), n);
+  const int e = min(max(cu[s + 1], a), n);
+  *lo = a;
+  *len = e - a;
+}
+__device__ __forceinline__ int sample_entries(const int32_t* __restrict__ cu, int s, int n, int m) {
+  int lo, len;
+  sample_span(cu, s, n, &lo, &len);
+  return len / m;
+}
+__device__ __forceinline__ void sample_entry_offsets(const int32_t* __restrict__ cu, int ns, int n, int m, int* E,
+                                                     int* tmp) {
+  const int t = threadIdx.x;
+  const int per = (ns + kThreads - 1) / kThreads;
+  const int s0 = t * per;
+  int local = 0;
+  for (int u = 0; u < per; ++u) {
+    const int s = s0 + u;
+    if (s < ns) local += sample_entries(cu, s, n, m);
+  }
+  tmp[t] = local;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off *= 2) {  // inclusive scan
+    const int v = tmp[t] + (t >= off ? tmp[t - off] : 0);
+    __syncthreads();
+    tmp[t] = v;
+    __syncthreads();
+  }
+  int run = tmp[t] - local;
+  for (int u = 0; u < per; ++u) {
+    const int s = s0 + u;
+    if (s < ns) {
+      E[s] = run;
+      run += sample_entries(cu, s, n, m);
+    }
+  }
+  if (t == kThreads - 1) E[ns] = tmp[t];
+  __syncthreads();
+}
+// the sample holding packed entry e: the last s with E[s] <= e (a sample without entries
+// shares its E with the next one and is skipped)
+__device__ __forceinline__ int sample_of(const int* E, int ns, int e) {
+  int lo = 0, hi = ns;  // E[lo] <= e < E[hi] once e < E[ns]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (E[mid] <= e) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // online per-channel softmax accumulation of one token row (8 channels)
 __device__ __forceinline__ void accum8(float* mx, float* den, float* acc, const float* z, const float* cv) {
 #pragma unroll
@@ -170,11 +228,20 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
     const T* __restrict__ w_ik, int d_index, T* __restrict__ out_ik, int64_t out_ik_bstride,
     int64_t ik_cap, const int32_t* __restrict__ dst_row, uint8_t* __restrict__ out_codes,
     uint8_t* __restrict__ out_scales, uint8_t* __restrict__ ik_codes, uint8_t* __restrict__ ik_scales,
-    int64_t q_rows) {
+    int64_t q_rows, const int32_t* __restrict__ cu_seqlens, int n_samples, int e_off,
+    int32_t* __restrict__ out_cu_entries) {
   constexpr bool kProj = kDI > 0;
   extern __shared__ float xs[];  // [kRowsPerWG][c] pre-RoPE normalised entries (kProj only)
-  const int n_ent = n / m;
   const int b = blockIdx.y;
+  // packed samples (B = 1): per-sample entry offsets in LDS after the projection's space
+  int* E = reinterpret_cast<int*>(xs + e_off);
+  int n_ent = n / m;
+  if (cu_seqlens) {
+    sample_entry_offsets(cu_seqlens, n_samples, n, m, E, E + n_samples + 1);
+    n_ent = E[n_samples];
+    if (out_cu_entries && blockIdx.x == 0)
+      for (int s = threadIdx.x; s <= n_samples; s += kThreads) out_cu_entries[s] = E[s];
+  }
   const int row0 = blockIdx.x * kRowsPerWG;
   const int lane_in_row = threadIdx.x % G;
   const int row_slot = threadIdx.x / G;
@@ -186,11 +253,22 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
   for (int lr = row_slot; lr < kRowsPerWG; lr += kRowsPerPass) {
     const int i = row0 + lr;
     if (i >= n_ent) break;
+    // entry i pools tokens tok0 .. tok0 + m - 1 of the stream; il is its block within its
+    // sequence (a sample of a packed stream restarts at block 0: positions from 0, no history)
+    int il = i, sidx = b;
+    int64_t tok0 = (int64_t)m * i;
+    if (cu_seqlens) {
+      sidx = sample_of(E, n_samples, i);
+      il = i - E[sidx];
+      int lo, len;
+      sample_span(cu_seqlens, sidx, n, &lo, &len);
+      tok0 = (int64_t)lo + (int64_t)m * il;
+    }
     float mx[8], den[8], acc[8], z[8], cv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { mx[e] = -INFINITY; den[e] = 0.f; acc[e] = 0.f; }
     for (int j = 0; j < m; ++j) {
-      const size_t off = seq_off + (size_t)(m * i + j) * c + ch;
+      const size_t off = seq_off + (size_t)(tok0 + j) * c + ch;
       Ld<T>::load8(za + off, z);
       Ld<T>::load8(ca + off, cv);
       if (ba) {
@@ -201,9 +279,9 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
     }
     // history: the previous block's b-branch rows; entry 0 takes them from cb0 / zb0 when
     // given, else it has none (its -inf logits carry zero weight)
-    if (overlap && (i > 0 || cb0)) {
-      const T* hc = i > 0 ? cb + seq_off + (size_t)m * (i - 1) * c : cb0 + (size_t)b * m * c;
-      const T* hz = i > 0 ? zb + seq_off + (size_t)m * (i - 1) * c : zb0 + (size_t)b * m * c;
+    if (overlap && (il > 0 || cb0)) {
+      const T* hc = il > 0 ? cb + seq_off + (size_t)(tok0 - m) * c : cb0 + (size_t)b * m * c;
+      const T* hz = il > 0 ? zb + seq_off + (size_t)(tok0 - m) * c : zb0 + (size_t)b * m * c;
       for (int j = 0; j < m; ++j) {
         const size_t off = (size_t)j * c + ch;
         Ld<T>::load8(hz + off, z);
@@ -232,7 +310,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
       for (int e = 0; e < 8; ++e) xs[lr * c + ch + e] = y[e];
     }
     if (rope_dims > 0 && ch + 8 > c - rope_dims) {
-      const double pos = (double)((pos0 ? pos0[b] : 0)) + (double)m * (double)i;
+      const double pos = (double)((pos0 ? pos0[sidx] : 0)) + (double)m * (double)il;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const int cc = ch + e;
@@ -323,14 +401,16 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(
 
 template <typename T, int G, int kDI>
 hipError_t launch_t(const csa2_compress_desc& d, hipStream_t s) {
-  const int n_ent = d.n / d.m;
-  dim3 grid((n_ent + kRowsPerWG - 1) / kRowsPerWG, d.B);
+  const int n_ent = d.n / d.m;  // packed samples: an upper bound of their entries
+  dim3 grid(std::max((n_ent + kRowsPerWG - 1) / kRowsPerWG, d.cu_seqlens ? 1 : 0), d.B);
   const int64_t ob = d.out_batch_stride ? d.out_batch_stride : (int64_t)n_ent * d.c;
   const int64_t oib = d.out_ik_batch_stride ? d.out_ik_batch_stride : (int64_t)n_ent * d.d_index;
   const int64_t out_cap = ob / d.c, ik_cap = d.d_index ? oib / d.d_index : 0;
   const int64_t q_rows = d.q_rows ? d.q_rows : (int64_t)n_ent;
-  // pre-RoPE entries, then (same space) the partial sums of the projection
-  const size_t lds = kDI > 0 ? std::max((size_t)kRowsPerWG * d.c, (size_t)kThreads * kRowsPerWG) * sizeof(float) : 0;
+  // pre-RoPE entries, then (same space) the partial sums of the projection; packed samples
+  // add their entry offsets and a scan buffer after it
+  const size_t proj_floats = kDI > 0 ? std::max((size_t)kRowsPerWG * d.c, (size_t)kThreads * kRowsPerWG) : 0;
+  const size_t lds = (proj_floats + (d.cu_seqlens ? (size_t)d.n_samples + 1 + kThreads : 0)) * sizeof(float);
   RopeFreq rope;
   rope_freq_host(&rope, d.rope_dims, d.rope_theta);
   hipLaunchKernelGGL((compress_kernel<T, G, kDI>), grid, dim3(kThreads), lds, s, d.n, d.c, d.m,
@@ -338,7 +418,8 @@ hipError_t launch_t(const csa2_compress_desc& d, hipStream_t s) {
                      (const T*)d.cb0, (const T*)d.zb0, d.ba,
                      d.bb, d.pos0, d.norm, d.eps, d.rope_dims, rope, (T*)d.out, ob, out_cap,
                      (const T*)d.w_ik, d.d_index, (T*)d.out_ik, oib, ik_cap, d.dst_row,
-                     d.out_codes, d.out_scales, d.w_ik ? d.ik_codes : nullptr, d.ik_scales, q_rows);
+                     d.out_codes, d.out_scales, d.w_ik ? d.ik_codes : nullptr, d.ik_scales, q_rows,
+                     d.cu_seqlens, d.n_samples, (int)proj_floats, d.out_cu_entries);
   return hipGetLastError();
 }
 
@@ -370,11 +451,12 @@ hipError_t launch_dt(const csa2_compress_desc& d, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_compress(const csa2_compress_desc& d, hipStream_t s) {
-  if (d.n / d.m == 0) return hipSuccess;
+  if (d.n / d.m == 0 && !(d.cu_seqlens && d.out_cu_entries)) return hipSuccess;
   // every pointer a kernel dereferences must be set
   if (!d.ca || !d.za || (!d.out && !d.out_codes) || (d.overlap && (!d.cb || !d.zb)) ||
       (d.w_ik && !d.out_ik && !d.ik_codes) || (!d.out_codes != !d.out_scales) ||
-      (!d.ik_codes != !d.ik_scales) || (d.out_codes && d.c % 16 != 0) || (!d.cb0 != !d.zb0))
+      (!d.ik_codes != !d.ik_scales) || (d.out_codes && d.c % 16 != 0) || (!d.cb0 != !d.zb0) ||
+      (d.cu_seqlens && (d.B != 1 || d.n_samples < 1 || d.n_samples > kMaxSamples || d.cb0)))
     return hipErrorInvalidValue;
   ScopedProf p(s, "compress");
   return d.dtype == CSA2_F32 ? launch_dt<float>(d, s) : launch_dt<uint16_t>(d, s);

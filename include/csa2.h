@@ -32,6 +32,7 @@ extern "C" {
 #endif
 
 #define CSA2_VERSION 1
+#define CSA2_MAX_PACKED_SAMPLES 4096
 
 #if defined(__GNUC__) || defined(__clang__)
 #define CSA2_API __attribute__((visibility("default")))
@@ -112,6 +113,16 @@ typedef enum {
  *   Rows outside an output's capacity (out_batch_stride / c, out_ik_batch_stride / d_index,
  *   q_rows) or below 0 are not written.  Every rounding decision is exact: the same fp32
  *   entry values always give the same bytes.
+ * Packed samples ([DSA-to-CSA notes]: samples packed into one token stream must not share a
+ * compression window, and a tail shorter than m is not completed by the next sample):
+ *   cu_seqlens: NULL, or int32 [n_samples + 1] device offsets: sample s holds tokens
+ *     [cu_seqlens[s], cu_seqlens[s+1]) of the stream (B must be 1).  Each sample is
+ *     compressed on its own: its floor(len/m) entries follow those of the samples before it,
+ *     its positions start at pos0[s] (pos0 is then per sample; NULL = 0), and its first entry
+ *     has no history.  Offsets are clamped into [0, n] and made non-decreasing.
+ *   n_samples: 1 .. CSA2_MAX_PACKED_SAMPLES.  cb0 / zb0 are not accepted with cu_seqlens.
+ *   out_cu_entries: NULL or int32 [n_samples + 1]: receives the samples' entry offsets (the
+ *     last one is the number of entries written).
  * Supported: c/8 a power of two, 8 <= c <= 512 (c % 16 == 0 for FP4 planes); rope_dims even
  * and <= c; with w_ik, d_index in {32, 64, 128} and c * d_index >= 1024.
  */
@@ -136,6 +147,9 @@ typedef struct {
   uint8_t *ik_codes, *ik_scales;
   int64_t q_rows;
   const void *cb0, *zb0;
+  const int32_t *cu_seqlens;
+  int n_samples;
+  int32_t *out_cu_entries;
 } csa2_compress_desc;
 
 CSA2_API int csa2_compress(const csa2_compress_desc *d, void *stream);

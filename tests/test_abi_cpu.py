@@ -213,3 +213,13 @@ def test_out_proj_validation(L):
         assert L.csa2_out_proj(C.byref(d), None) == code, (over, csa2.last_error())
     d = csa2.OutProjDesc(**{**base, "M": 0, "o": None})
     assert L.csa2_out_proj(C.byref(d), None) == csa2.CSA2_OK
+
+
+def test_compress_packed_validation(L):
+    base = dict(B=1, n=8, c=64, m=2, dtype=csa2.CSA2_F32, ca=FAKE, za=FAKE, out=FAKE, eps=1e-6,
+                cu_seqlens=FAKE, n_samples=2)
+    for over, code in [(dict(B=2), csa2.CSA2_ERR_INVALID), (dict(n_samples=0), csa2.CSA2_ERR_INVALID),
+                       (dict(n_samples=csa2.lib() and 4097), csa2.CSA2_ERR_INVALID),
+                       (dict(overlap=1, cb=FAKE, zb=FAKE, cb0=FAKE, zb0=FAKE), csa2.CSA2_ERR_INVALID)]:
+        d = csa2.CompressDesc(**{**base, **over})
+        assert L.csa2_compress(C.byref(d), None) == code, (over, csa2.last_error())
