@@ -178,6 +178,22 @@ __device__ __forceinline__ void accum8(float* mx, float* den, float* acc, const 
   }
 }
 
+// x_hat[row, cc0 .. cc0 + kCB) . W[cc0 .. cc0 + kCB, d] added to acc (4 channels per LDS read)
+template <int kCB>
+__device__ __forceinline__ void project_row(const float* xs, int c, int row, int cc0, const float (&w)[kCB],
+                                            float& acc) {
+  float a = acc;
+#pragma unroll
+  for (int q = 0; q < kCB; q += 4) {
+    const float4 x4 = *reinterpret_cast<const float4*>(&xs[row * c + cc0 + q]);
+    a += x4.x * w[q];
+    a += x4.y * w[q + 1];
+    a += x4.z * w[q + 2];
+    a += x4.w * w[q + 3];
+  }
+  acc = a;
+}
+
 // One thread's share of the indexer-K projection: sum over channels [c_lo, c_lo + span) of
 // x_hat[row, ch] * W_ik[ch, d] for the rows below nrows (in chunks of 8; a chunk is uniform
 // over the workgroup).  W is read kCB channels at a time, the next block's loads issued
@@ -197,20 +213,15 @@ __device__ __forceinline__ void project_part(const float* xs, const T* __restric
     for (int u = 0; u < kCB; ++u) wnxt[u] = Ld<T>::scalar(w_ik + (size_t)(cn + u) * kDIc + d);
 #pragma unroll
     for (int rc = 0; rc < kRowsPerWG; rc += 8) {
-      if (rc < nrows) {
+      // a full chunk of 8 rows runs unguarded; a partial one (a decode append has a single
+      // row) skips its missing rows.  Both conditions are uniform over the workgroup.
+      if (rc + 8 <= nrows) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          float acc = part_sum[rc + r];
+        for (int r = 0; r < 8; ++r) project_row(xs, c, rc + r, cc0, wcur, part_sum[rc + r]);
+      } else if (rc < nrows) {
 #pragma unroll
-          for (int q = 0; q < kCB; q += 4) {
-            const float4 x4 = *reinterpret_cast<const float4*>(&xs[(rc + r) * c + cc0 + q]);
-            acc += x4.x * wcur[q];
-            acc += x4.y * wcur[q + 1];
-            acc += x4.z * wcur[q + 2];
-            acc += x4.w * wcur[q + 3];
-          }
-          part_sum[rc + r] = acc;
-        }
+        for (int r = 0; r < 8; ++r)
+          if (rc + r < nrows) project_row(xs, c, rc + r, cc0, wcur, part_sum[rc + r]);
       }
     }
 #pragma unroll
