@@ -187,6 +187,8 @@ def test_attn_validation(L):
         (dict(kv=None), csa2.CSA2_ERR_INVALID),
         (dict(win=FAKE), csa2.CSA2_ERR_INVALID),  # no win_pos0
         (dict(num_splits=-1), csa2.CSA2_ERR_INVALID),
+        (dict(dense_m=-1), csa2.CSA2_ERR_INVALID),
+        (dict(dense_m=128), csa2.CSA2_ERR_INVALID),  # dense attention takes no index list
     ]
     for over, code in cases:
         d = csa2.AttnDesc(**{**base, **over})
@@ -223,3 +225,14 @@ def test_compress_packed_validation(L):
                        (dict(overlap=1, cb=FAKE, zb=FAKE, cb0=FAKE, zb0=FAKE), csa2.CSA2_ERR_INVALID)]:
         d = csa2.CompressDesc(**{**base, **over})
         assert L.csa2_compress(C.byref(d), None) == code, (over, csa2.last_error())
+
+
+def test_attn_dense_workspace_counts_every_entry(L):
+    # dense mode sizes its split partials over all N entries (k is ignored)
+    base = dict(B=2, T=1, H=64, c=512, k=0, N=8192, rope_dims=64, rope_theta=1e4, eps=1e-6, q_norm=1,
+                q_dtype=csa2.CSA2_BF16, q=FAKE, q_pos=FAKE, kv_dtype=csa2.CSA2_BF16, kv=FAKE, out=FAKE,
+                dense_m=128)
+    d = csa2.AttnDesc(**base)
+    dense = L.csa2_attn_workspace_bytes(C.byref(d))
+    d = csa2.AttnDesc(**{**base, "dense_m": 0, "k": 8192, "idx": FAKE})
+    assert dense == L.csa2_attn_workspace_bytes(C.byref(d)) > 0
