@@ -5,21 +5,24 @@
 // per head in the softmax denominator; [CSA2 column] "保留了 CSA 的骨架": the selected
 // entries are joined by the latest 128 uncompressed rows of the layer).
 //
-// attn_mfma (bf16 queries, groups of 32 heads, c = 512, bf16 or FP4 rows):
-//   One workgroup = one query x 32 heads x a contiguous range of row slots (a split).
-//   Rows are gathered 32 at a time into LDS (FP4 rows dequantised on the way: E2M1 x E4M3
-//   is exact in bf16), double-buffered through registers; the workgroup barriers order
-//   LDS only, so the next tile's loads stay in flight across them.  Wave (hq, mr) computes
-//   the S^T block rows 16*mr.. x heads 16*hq.. on v_mfma_f32_16x16x32_bf16 (q_hat in
-//   registers); the C layout of S^T gives each lane one head and 4 rows, written to LDS in
-//   the A-operand order of P for the PV product.  For PV each wave owns 128 output
-//   channels of all 32 heads; the V operand (rows along K) is read with the gfx950 LDS
-//   transpose read ds_read_b64_tr_b16 from the same row-major tile that fed S^T (shared
+// attn_mfma (bf16 queries, 64 heads per workgroup, c = 512, bf16 or FP4 rows):
+//   One workgroup = one query x 64 heads x a contiguous range of row slots (a split): 8
+//   waves in two halves of 32 heads that share every row tile in LDS, so each selected row
+//   is read once per query.  Rows are gathered a tile at a time into LDS (64 rows for bf16,
+//   32 for FP4, whose larger register set spills at 64; FP4 rows are dequantised on the way:
+//   E2M1 x E4M3 is exact in bf16), one tile in flight in registers; the workgroup barriers
+//   order LDS only, so the next tile's loads stay in flight across them.  Wave (half, hq,
+//   mr) computes the S^T blocks of rows 32*kk + 16*mr.. x heads 32*half + 16*hq.. on
+//   v_mfma_f32_16x16x32_bf16 (q_hat in registers; two independent accumulators in a 64-row
+//   tile); the C layout of S^T gives each lane one head and 4 rows per block, written to LDS
+//   in the A-operand order of P for the PV product.  For PV each wave owns 128 output
+//   channels of its half's 32 heads; the V operand (rows along K) is read with the gfx950
+//   LDS transpose read ds_read_b64_tr_b16 from the same row-major tile that fed S^T (shared
 //   K = V, one copy in LDS).  The row pitch is padded by 16 bytes so both read patterns
 //   avoid bank conflicts.  Softmax in fp32 with exp2 (scale folded into q_hat) against a
-//   fixed per-head reference (see kOverflow).  With several splits per query the
-//   unnormalised partial output and (max, sum) go to a workspace and attn_combine merges
-//   them in a fixed order.
+//   fixed per-head reference (see kOverflow).  With several splits per query each split's
+//   output (normalised by its own sum, bf16) and (max, sum) go to a workspace in 32-head
+//   units and attn_combine merges them in a fixed order.
 //
 // attn_simple: any head count / width / dtype; one wave per (query, head), fp32 math.
 
@@ -202,13 +205,18 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 // ------------------------------------------------------------------ attn_mfma
 constexpr int kC = 512;           // channels
 constexpr int kHG = 32;           // heads per split-partial unit (one half of a workgroup)
-constexpr int kTile = 32;         // rows per tile
+// rows per tile: 64 for bf16 rows (fewer barriers and exchanges per row); 32 for FP4 rows,
+// whose larger register prefetch set (codes, scales and bf16 window rows) spills at 64
+template <bool kFP4>
+constexpr int kTileOf = kFP4 ? 32 : 64;
 constexpr int kRowBytes = kC * 2;
 constexpr int kThreadsM = 512;    // 8 waves: two halves of 4, one per 32 heads
 constexpr int kHW = 2 * kHG;       // heads per workgroup
 constexpr int kWaves = kThreadsM / 64;
-constexpr int kPrefRows = kTile / kWaves;          // bf16 rows each wave loads per tile
-constexpr int kFp4Per = kTile * 16 / kThreadsM;    // FP4 16-byte code chunks per thread per tile
+template <int kT>
+constexpr int kPrefRows = kT / kWaves;          // bf16 rows each wave loads per tile
+template <int kT>
+constexpr int kFp4Per = kT * 16 / kThreadsM;    // FP4 16-byte code chunks per thread per tile
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -217,8 +225,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // MFMA A operand (16 B each) fall in different banks, and every offset inside a tile is
 // a compile-time immediate.
 constexpr int kPitch = kRowBytes + 16;
-constexpr int kPPitch = kTile + 8;    // P rows (bf16), padded likewise
-constexpr int kMaxSplitTiles = 32;    // row tiles per split (slots staged in LDS)
+constexpr int kMaxSplitRows = 1024;   // row slots per split (staged in LDS)
 // Softmax reference: each head fixes the max of its first valid tile as the reference m
 // and keeps it; the final normalisation divides by a sum taken with the same reference,
 // so the result is the exact softmax for any m, and the accumulators are never rescaled.
@@ -227,10 +234,12 @@ constexpr int kMaxSplitTiles = 32;    // row tiles per split (slots staged in LD
 // |z| <= sqrt(c) * log2(e)).
 constexpr float kOverflow = 60.0f;
 
+template <int kT>
 struct MfmaSmem {
+  static constexpr int kPPitch = kT + 8;  // P rows (bf16), padded likewise
   // two row tiles; the same bytes also stage q_hat ([32 heads][kPitch]) before the loop
   // and the bf16 output tile ([32][512]) after it
-  alignas(16) uint8_t tile[2][kTile * kPitch];
+  alignas(16) uint8_t tile[2][kT * kPitch];
   alignas(16) uint16_t pbuf[kHW][kPPitch];  // P in PV A-operand order (bf16)
   float wmax[2][kHW];                       // per row half: tile max per head (first valid tile)
   float omax[2][kHW];                       // per row half: tile max per head (overflow check)
@@ -238,27 +247,27 @@ struct MfmaSmem {
   float mfin[kHW];
   float rope_c[64], rope_s[64];             // cos/sin of the query position, per frequency
   alignas(16) int ovf[kWaves];              // per wave: a head overflowed its reference
-  int src[kMaxSplitTiles * kTile];          // per slot: >= 0 kv entry id, -2-w window row w, -1 empty
+  int src[kMaxSplitRows];                   // per slot: >= 0 kv entry id, -2-w window row w, -1 empty
 };
-static_assert(sizeof(MfmaSmem) <= 80 * 1024, "LDS of one workgroup");
-static_assert(2 * kTile * kPitch >= kHW * kPitch, "q_hat of the workgroup's heads fits the two row tiles");
+static_assert(sizeof(MfmaSmem<64>) <= 160 * 1024, "LDS of one workgroup (one per CU)");
+static_assert(2 * 32 * kPitch >= kHW * kPitch, "q_hat of the workgroup's heads fits the two row tiles");
 
 // registers for one tile in flight.  bf16 rows: wave w owns rows w, w+8, .., w+24 and
 // lane l carries their 16-byte chunk l.  FP4 rows: thread q carries code chunk q%16 of row
 // q/16 and the two E4M3 scales of its 32 channels.
-template <bool kFP4>
+template <bool kFP4, int kT = kTileOf<kFP4>>
 struct Prefetch {
-  uint4 v[kPrefRows];
-  uint4 fc[kFP4 ? kFp4Per : 1];
-  uint32_t fs[kFP4 ? kFp4Per : 1];
+  uint4 v[kPrefRows<kT>];
+  uint4 fc[kFP4 ? kFp4Per<kT> : 1];
+  uint32_t fs[kFP4 ? kFp4Per<kT> : 1];
 };
 
 // Slot -> row source for this split's slots [slot0, slot0 + n): index slot s < k holds its
 // entry id (-1 if empty or out of range), slot k + w window row lo_row + w as -2 - row,
 // slots past R are empty.  The index slots do not depend on the query position, so their
 // ids are loaded first (ids_of_split) and only combined with the window here.
-constexpr int kSlotsPerThread = kMaxSplitTiles * kTile / kThreadsM;
-static_assert(kMaxSplitTiles * kTile == kSlotsPerThread * kThreadsM, "slot ids per thread");
+constexpr int kSlotsPerThread = kMaxSplitRows / kThreadsM;
+static_assert(kMaxSplitRows == kSlotsPerThread * kThreadsM, "slot ids per thread");
 __device__ __forceinline__ void ids_of_split(const AttnDev& a, int row, int slot0, int n,
                                              int (&ids)[kSlotsPerThread]) {
 #pragma unroll
@@ -304,11 +313,12 @@ __device__ __forceinline__ RowBases row_bases(const AttnDev& a, int b) {
 template <bool kFP4>
 __device__ __forceinline__ void fetch_tile(const RowBases& rb, const int* src, Prefetch<kFP4>& pf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int srow[kPrefRows];
+  constexpr int kPR = kPrefRows<kTileOf<kFP4>>;
+  int srow[kPR];
 #pragma unroll
-  for (int i = 0; i < kPrefRows; ++i) srow[i] = src[wave + kWaves * i];  // all slot reads first, one wait
+  for (int i = 0; i < kPR; ++i) srow[i] = src[wave + kWaves * i];  // all slot reads first, one wait
 #pragma unroll
-  for (int i = 0; i < kPrefRows; ++i) {
+  for (int i = 0; i < kPR; ++i) {
     const int sr = __builtin_amdgcn_readfirstlane(srow[i]);  // uniform per wave
     const uint16_t* base = nullptr;
     if (sr <= -2) base = rb.win + (size_t)(-2 - sr) * kC;
@@ -317,7 +327,7 @@ __device__ __forceinline__ void fetch_tile(const RowBases& rb, const int* src, P
   }
   if constexpr (kFP4) {
 #pragma unroll
-    for (int i = 0; i < kFp4Per; ++i) {
+    for (int i = 0; i < kFp4Per<kTileOf<kFP4>>; ++i) {
       const int q = threadIdx.x + kThreadsM * i;
       const int r = q >> 4, part = q & 15;
       const int sr = src[r];
@@ -336,14 +346,14 @@ template <bool kFP4>
 __device__ __forceinline__ void commit_tile(const int* src, const Prefetch<kFP4>& pf, uint8_t* tile) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < kPrefRows; ++i) {
+  for (int i = 0; i < kPrefRows<kTileOf<kFP4>>; ++i) {
     const int r = wave + kWaves * i;
     const int sr = __builtin_amdgcn_readfirstlane(src[r]);
     if (!kFP4 || sr < 0) *reinterpret_cast<uint4*>(tile + r * kPitch + 16 * lane) = pf.v[i];
   }
   if constexpr (kFP4) {
 #pragma unroll
-    for (int i = 0; i < kFp4Per; ++i) {
+    for (int i = 0; i < kFp4Per<kTileOf<kFP4>>; ++i) {
       const int q = threadIdx.x + kThreadsM * i;
       const int r = q >> 4, part = q & 15;
       if (src[r] >= 0) {
@@ -383,8 +393,10 @@ __device__ __forceinline__ void stage_rope(const AttnDev& a, int t_pos, float* r
 // PV, wave (half, w4) owns output channels 128*w4 .. 128*w4+127 of its half's 32 heads.
 template <bool kFP4>
 __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
+  constexpr int kTile = kTileOf<kFP4>;
+  constexpr int kKK = kTile / 32;  // 32-row blocks per tile (k steps of PV)
   extern __shared__ __align__(16) uint8_t smem_raw[];
-  MfmaSmem& sm = *reinterpret_cast<MfmaSmem*>(smem_raw);
+  MfmaSmem<kTile>& sm = *reinterpret_cast<MfmaSmem<kTile>*>(smem_raw);
   const int split = blockIdx.y;
   const int hg = blockIdx.z;
   const int row = blockIdx.x;
@@ -461,8 +473,9 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
     qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(qs + (32 * half + 16 * hq + li) * kPitch + 64 * ks + 16 * g));
   lds_barrier();
 
-  // per-lane LDS byte offsets (tile-relative): A operand row 16*mr + li at chunk g;
-  // transpose-read source rows 4g + li/4 (and +16) at channel 128*wave + 4*(li%4)
+  // per-lane LDS byte offsets (tile-relative): A operand row 32*kk + 16*mr + li at chunk g
+  // (this wave's two 16-row blocks kk = 0, 1); transpose-read source rows 32*kk + 4g + li/4
+  // (and +16) at channel 128*w4 + 4*(li%4)
   const int a_off = (16 * mr + li) * kPitch + 16 * g;
   const int t_off0 = (4 * g + (li >> 2)) * kPitch + 8 * (li & 3) + 256 * w4;
   const int t_off1 = t_off0 + 16 * kPitch;
@@ -487,31 +500,39 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
       commit_tile<kFP4>(src, pf, sm.tile[buf]);
       lds_barrier();
       if (ti + 1 < tile1) fetch_tile<kFP4>(rb, src + kTile, pf);
-      // valid rows of this wave's half: row 16*mr + r <-> bit r
-      const uint32_t vm = (uint32_t)__ballot(lane < 16 && src[16 * mr + (lane & 15)] != -1);
+      // valid rows of this wave's blocks: row 32*kk + 16*mr + r <-> bit 16*kk + r
+      const uint32_t vm = (uint32_t)__ballot(lane < 16 * kKK && src[32 * (lane >> 4) + 16 * mr + (lane & 15)] != -1);
 
       const uint8_t* tl = sm.tile[buf];
       const lds_u8* tl3 = (const lds_u8*)tl;
-      // ---- S^T tile: rows 16*mr.. x heads 16*hq..; A reads issued ahead of the MFMAs
-      bf16x8 av[16];
+      // ---- S^T tile: rows 32*kk + 16*mr.. x heads 16*hq.., two independent accumulators;
+      // each block's A reads issued ahead of its MFMAs
+      f32x4 sacc[kKK];
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tl + a_off + 64 * ks));
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < kKK; ++kk) {
+        bf16x8 av[16];
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], qreg[ks], sacc, 0, 0, 0);
-      // lane holds head my_head, rows 16*mr + 4*g + j
-      bool valid[4];
+        for (int ks = 0; ks < 16; ++ks)
+          av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(tl + a_off + 32 * kk * kPitch + 64 * ks));
+        sacc[kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) sacc[kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], qreg[ks], sacc[kk], 0, 0, 0);
+      }
+      // lane holds head my_head, rows 32*kk + 16*mr + 4*g + j
+      bool valid[kKK][4];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        valid[j] = (vm >> (4 * g + j)) & 1u;
-        if (valid[j]) tmax = fmaxf(tmax, sacc[j]);
-      }
-      tmax = rows_max(tmax);  // this wave's 16 rows
-      // The reference is fixed by the first tile holding a valid row, the max over all 32
-      // of its rows (exchanged between the two row halves).  Validity is per row, the same
-      // for every head, so the branch is uniform over the workgroup.  Later tiles only
-      // check their own half against it; the overflow flag is exchanged with P below.
+      for (int kk = 0; kk < kKK; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          valid[kk][j] = (vm >> (16 * kk + 4 * g + j)) & 1u;
+          if (valid[kk][j]) tmax = fmaxf(tmax, sacc[kk][j]);
+        }
+      tmax = rows_max(tmax);  // this wave's rows
+      // The reference is fixed by the first tile holding a valid row, the max over all
+      // of its rows (exchanged between the two waves of a head block).  Validity is per row,
+      // the same for every head, so the branch is uniform over the workgroup.  Later tiles
+      // only check their own rows against it; the overflow flag is exchanged with P below.
       if (m_use == -INFINITY) {
         if (g == 0) sm.wmax[mr][my_head] = tmax;
         lds_barrier();
@@ -520,17 +541,20 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
       }
       const bool ovf = tmax > m_use + kOverflow;
       if (g == 0) sm.omax[mr][my_head] = tmax;
-      float p[4];
       float psum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        p[j] = valid[j] ? exp2f(sacc[j] - m_use) : 0.f;
-        psum += p[j];
+      for (int kk = 0; kk < kKK; ++kk) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[j] = valid[kk][j] ? exp2f(sacc[kk][j] - m_use) : 0.f;
+          psum += p[j];
+        }
+        // P for head my_head, k-slot 32*kk + 8g + 4*mr + j = row 32*kk + 16*mr + 4g + j
+        *reinterpret_cast<uint2*>(&sm.pbuf[my_head][32 * kk + 8 * g + 4 * mr]) =
+            make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       }
       l_part += rows_sum(psum);
-      // P for head my_head, k-slots 8g + 4*mr + j = row 16*mr + 4g + j
-      *reinterpret_cast<uint2*>(&sm.pbuf[my_head][8 * g + 4 * mr]) =
-          make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       if (lane == 0) sm.ovf[wave] = __ballot(ovf) != 0;
       lds_barrier();
       const int4 ov0 = *reinterpret_cast<const int4*>(sm.ovf);
@@ -541,20 +565,26 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
         break;
       }
 
-      // ---- O[half's heads, 128*w4 .. +128] += P x V
-      bf16x8 pa[2];
+      // ---- O[half's heads, 128*w4 .. +128] += P x V, the tile's rows in two k steps of 32
+      bf16x8 pa[kKK][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        pa[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.pbuf[32 * half + 16 * mt + li][8 * g]));
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        // channels 128*w4 + 16*nt + (0..15); rows 4g..4g+3 and 16+4g..16+4g+3
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off0 + 32 * nt));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off1 + 32 * nt));
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int kk = 0; kk < kKK; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], bv, oacc[mt][nt], 0, 0, 0);
+          pa[kk][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.pbuf[32 * half + 16 * mt + li][32 * kk + 8 * g]));
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+        for (int kk = 0; kk < kKK; ++kk) {
+          // channels 128*w4 + 16*nt + (0..15); rows 32kk + 4g..+3 and 32kk + 16 + 4g..+3
+          const int ko = 32 * kk * kPitch + 32 * nt;
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off0 + ko));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tl3 + t_off1 + ko));
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[kk][mt], bv, oacc[mt][nt], 0, 0, 0);
+        }
       }
       buf ^= 1;
     }
@@ -726,8 +756,12 @@ bool mfma_ok(const csa2_attn_desc& d) {
 
 int max_rows(const csa2_attn_desc& d) { return d.k + ((d.win && d.n_win > 0) ? d.n_win : 0); }
 
+int tile_rows(const csa2_attn_desc& d) { return d.kv_dtype == CSA2_FP4_E4M3 ? kTileOf<true> : kTileOf<false>; }
+
 void pick_splits(const csa2_attn_desc& d, int* splits, int* tps) {
   const int rows = d.B * d.T;
+  const int kTile = tile_rows(d);
+  const int kMaxSplitTiles = kMaxSplitRows / kTile;
   const int n_tiles = (max_rows(d) + kTile - 1) / kTile;
   const int n_wg = d.H / kHW;  // workgroups per (query, split)
   int s = d.num_splits > 0 ? d.num_splits : (256 + rows * n_wg - 1) / (rows * n_wg);
@@ -814,22 +848,22 @@ hipError_t launch_attn(const csa2_attn_desc& d0, void* ws, size_t ws_bytes, hipS
     a.part_o = (uint16_t*)ws;
     a.part_ml = (float*)((char*)ws + units * plan.splits * kHG * kC * sizeof(uint16_t));
   }
-  const size_t lds = sizeof(MfmaSmem);
+  const size_t lds_bf16 = sizeof(MfmaSmem<kTileOf<false>>), lds_fp4 = sizeof(MfmaSmem<kTileOf<true>>);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_mfma<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bf16);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)attn_mfma<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      e = hipFuncSetAttribute((const void*)attn_mfma<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_fp4);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int splits = plan.splits;
   if (d.kv_dtype == CSA2_FP4_E4M3) {
     ScopedProf p(s, "attn_mfma_fp4");
-    hipLaunchKernelGGL(attn_mfma<true>, dim3(rows, splits, d.H / kHW), dim3(kThreadsM), lds, s, a);
+    hipLaunchKernelGGL(attn_mfma<true>, dim3(rows, splits, d.H / kHW), dim3(kThreadsM), lds_fp4, s, a);
   } else {
     ScopedProf p(s, "attn_mfma");
-    hipLaunchKernelGGL(attn_mfma<false>, dim3(rows, splits, d.H / kHW), dim3(kThreadsM), lds, s, a);
+    hipLaunchKernelGGL(attn_mfma<false>, dim3(rows, splits, d.H / kHW), dim3(kThreadsM), lds_bf16, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits <= 1) return e;
