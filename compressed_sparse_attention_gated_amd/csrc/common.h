@@ -138,6 +138,12 @@ __device__ __forceinline__ void pair_xor32(float v, float* a, float* b) {
   *a = __uint_as_float(r[0]);
   *b = __uint_as_float(r[1]);
 }
+// v of lane l plus v of lane l ^ 32 (the same sum, bit for bit, as an exchange through LDS)
+__device__ __forceinline__ float sum_xor32(float v) {
+  float a, b;
+  pair_xor32(v, &a, &b);
+  return a + b;
+}
 // sum / max over the 4 lanes l, l^16, l^32, l^48 (the four 16-lane rows); every lane active
 __device__ __forceinline__ float rows_sum(float v) {
   float a, b;

@@ -176,7 +176,7 @@ __device__ __forceinline__ float tile_score(const bf16x8 (*areg)[DI / 16], const
     for (int r = 0; r < 16; ++r) s += wreg[mt][r] * relu_bits(acc[r]);
   }
   // lanes l and l^32 hold the two halves of the head rows of the same entry
-  s += xor32(s);
+  s = sum_xor32(s);
   return s;
 }
 
@@ -209,8 +209,8 @@ __device__ __forceinline__ void epi2(const f32x16* acc0, const f32x16* acc1, con
       x0 += wreg[mt][r] * relu_bits(acc0[mt][r]);
       x1 += wreg[mt][r] * relu_bits(acc1[mt][r]);
     }
-  *s0 = x0 + xor32(x0);
-  *s1 = x1 + xor32(x1);
+  *s0 = sum_xor32(x0);
+  *s1 = sum_xor32(x1);
 }
 
 // One 32-entry tile split the same way: MFMAs into acc, then the epilogue.  A wave that
@@ -233,7 +233,7 @@ __device__ __forceinline__ float epi1(const f32x16* acc, const float (*wreg)[16]
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) x += wreg[mt][r] * relu_bits(acc[mt][r]);
-  return x + xor32(x);
+  return sum_xor32(x);
 }
 
 __device__ __forceinline__ int n_visible(const Dev& a, int row) {
