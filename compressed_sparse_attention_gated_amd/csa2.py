@@ -70,6 +70,8 @@ EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk",
            "csa2_profile_collect"]
 
 _lib = None
+# the descriptor layouts below are those of this version of include/csa2.h
+ABI_VERSION = 2
 
 
 def lib():
@@ -93,6 +95,9 @@ def lib():
     L.csa2_attn_workspace_bytes.restype = C.c_size_t
     L.csa2_sparse_attn.argtypes = [C.POINTER(AttnDesc), _vp, C.c_size_t, _vp]
     L.csa2_out_proj.argtypes = [C.POINTER(OutProjDesc), _vp]
+    if L.csa2_version() != ABI_VERSION:  # a library built from other sources: layouts differ
+        raise RuntimeError(f"libcsa2.so reports ABI version {L.csa2_version()}, this binding expects "
+                           f"{ABI_VERSION}; rebuild it with `python -m compressed_sparse_attention_gated_amd.build`")
     L.csa2_last_error.restype = C.c_char_p
     L.csa2_profile_enable.argtypes = [_i]
     L.csa2_profile_collect.argtypes = [C.POINTER(KernelTime), _i]

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 1
+#define CSA2_VERSION 2 /* 2: write-path, packed-sample, dense-attention and projection fields */
 #define CSA2_MAX_PACKED_SAMPLES 4096
 
 #if defined(__GNUC__) || defined(__clang__)
