@@ -555,7 +555,9 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
             make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
       }
       l_part += rows_sum(psum);
-      if (lane == 0) sm.ovf[wave] = __ballot(ovf) != 0;
+      // the vote is taken with every lane active (inside `lane == 0` it would see one head)
+      const bool wave_ovf = __ballot(ovf) != 0;
+      if (lane == 0) sm.ovf[wave] = wave_ovf;
       lds_barrier();
       const int4 ov0 = *reinterpret_cast<const int4*>(sm.ovf);
       const int4 ov1 = *reinterpret_cast<const int4*>(sm.ovf + 4);

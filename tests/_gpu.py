@@ -4,6 +4,8 @@ import sys
 import numpy as np
 import torch
 
+from oracle import formats as F
+
 DEV = "cuda"
 
 
@@ -56,3 +58,24 @@ def assert_close(got, want, atol, rtol, what=""):
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside atol={atol} rtol={rtol}; "
                              f"first at {tuple(i)}: got {got[tuple(i)]} want {want[tuple(i)]}; "
                              f"max abs err {np.abs(got - want).max():.3g}")
+
+
+def plant_high_scores(g, q, kv, ids_gammas, aligned=256, fp4=False):
+    """Give every head of each query one sign pattern s on the first `aligned` channels
+    (|q| kept), and set each listed key row to gamma * s there and N(0, 1) elsewhere: its
+    score is then about 0.82 * gamma * aligned * scale * log2(e) for every head, a sum of
+    like-signed terms (small relative rounding), while the N(0, 1) part decides how rows
+    of one level share the softmax.  With fp4 the planted rows are replaced by their
+    decoded FP4 quantisation.  q [B, 1, H, c] and kv [B, N, c] (fp64) are changed in
+    place; ids_gammas[b] lists (entry id, gamma)."""
+    B, c = q.shape[0], q.shape[-1]
+    for b in range(B):
+        s = np.where(g.normal((aligned,), dtype="f32") >= 0, 1.0, -1.0)
+        q[b, 0, :, :aligned] = np.abs(q[b, 0, :, :aligned]) * s
+        for e, gamma in ids_gammas[b]:
+            row = np.asarray(g.normal((c,), dtype="bf16"), np.float64)
+            row[:aligned] = gamma * s
+            if fp4:
+                row = F.fp4_main_decode(*F.quantize_fp4_main(row[None]))[0]
+            kv[b, e] = row
+

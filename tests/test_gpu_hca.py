@@ -8,7 +8,7 @@ import torch
 import oracle as O
 from oracle import formats as F
 from compressed_sparse_attention_gated_amd import workloads as W
-from tests._gpu import assert_close, banner, bf16, f32, host, i32, u8
+from tests._gpu import assert_close, banner, bf16, f32, host, i32, plant_high_scores, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +44,28 @@ def test_hca_dense_decode_mfma(C, kv_format):
                             sink=a["sink"], rope_dims=64)
     assert_close(host(out), want, **BF16_TOL, what=f"hca {kv_format}")
     assert_close(host(mass), wm, atol=1e-2, rtol=1e-2, what="mass")
+
+
+def test_hca_dense_reference_restart(C):
+    # entry 100 scores ~100 log2 units above the first tile, entries 250 and 280 ~390 (and
+    # share the softmax): the dense split restarts twice and must still be exact
+    banner("hca dense decode reference restart B=1 N=300 m'=128 H=64 c=512 bf16")
+    g = W.rng(64)
+    N, mp, c, r = 300, 128, 512, 64
+    a = W.attn_inputs(g, 1, 1, N, 64, c, Lw=128)
+    q = np.array(a["q"], np.float64)
+    kv = np.array(a["kv"], np.float64)
+    plant_high_scores(g, q, kv, [[(100, 8.0), (250, 30.0), (280, 30.0)]])
+    q_pos = np.array([[mp * N + 5]], np.int32)
+    win_pos0 = (q_pos[:, 0] - 127).astype(np.int32)
+    out = C.csa2_sparse_attn(bf16(q), i32(q_pos), None, kv=bf16(kv), win=bf16(a["win"]),
+                             win_pos0=i32(win_pos0), n_win=128, sink=f32(a["sink"]), dense_m=mp,
+                             num_splits=1)
+    torch.cuda.synchronize()
+    want, _ = O.dense_attn(q, q_pos, kv, mp, win=a["win"], win_pos0=win_pos0, window=128,
+                           sink=a["sink"], rope_dims=r)
+    assert np.abs(want[0, 0, :, 0]).min() > 20
+    assert_close(host(out), want, **BF16_TOL, what="hca restart")
 
 
 def test_hca_dense_prefill_f32(C):

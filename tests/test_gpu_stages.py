@@ -8,7 +8,7 @@ import torch
 import oracle as O
 from oracle import formats as F
 from compressed_sparse_attention_gated_amd import workloads as W
-from tests._gpu import assert_close, banner, bf16, dev, f32, host, i32, u8
+from tests._gpu import assert_close, banner, bf16, dev, f32, host, i32, plant_high_scores, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -306,3 +306,45 @@ def test_attn_splits_agree(C):
     o5b = host(C.csa2_sparse_attn(*args, num_splits=5, **kw))
     np.testing.assert_array_equal(o5, o5b)  # deterministic
     assert_close(o5, o1, atol=8e-3, rtol=8e-3, what="splits")
+
+
+
+@pytest.mark.parametrize("kv_format", ["bf16", "fp4"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_attn_reference_restart(C, kv_format, splits):
+    """Selected rows scoring hundreds of log2 units above the first tile's maximum, far
+    beyond what the kernel's fixed softmax reference allows: the kernel must raise its
+    reference and start the split again, and still give the exact softmax.  Query 0: a row
+    at ~100 (slot 100), then two rows at ~390 (slots 300 and 500) that share the softmax,
+    so a single split restarts twice.  Query 1: a ~390 row in the first tile (slot 20, no
+    restart) and another at slot 511."""
+    banner(f"attn reference restart B=2 N=3000 H=64 c=512 k=512 kv={kv_format} splits={splits}")
+    g = W.rng(23)
+    B, N, L, H, c, r = 2, 3000, 3000, 64, 512, 64
+    a = W.attn_inputs(g, B, 1, N, H, c, Lw=128, kv_format=kv_format)
+    idx = W.random_topk_lists(g, B, 1, N, 512)
+    q = np.array(a["q"], np.float64)
+    kvd = (np.array(a["kv"], np.float64) if kv_format == "bf16"
+           else F.fp4_main_decode(a["kv_codes"], a["kv_scales"]))
+    plants = [[(idx[0, 0, 100], 8.0), (idx[0, 0, 300], 30.0), (idx[0, 0, 500], 30.0)],
+              [(idx[1, 0, 20], 30.0), (idx[1, 0, 511], 30.0)]]
+    plant_high_scores(g, q, kvd, plants, fp4=kv_format == "fp4")
+    if kv_format == "fp4":  # re-encode only the planted rows; the random rows keep their planes
+        codes, scales = np.array(a["kv_codes"]), np.array(a["kv_scales"])
+        for b in range(B):
+            ids = [e for e, _ in plants[b]]
+            codes[b, ids], scales[b, ids] = F.quantize_fp4_main(kvd[b, ids])
+        assert np.array_equal(F.fp4_main_decode(codes, scales), kvd)
+        kvkw = dict(kv_codes=u8(codes), kv_scales=u8(scales))
+    else:
+        kvkw = dict(kv=bf16(kvd))
+    q_pos = np.full((B, 1), L, np.int32)
+    win_pos0 = np.full(B, L - 127, np.int32)
+    mass = torch.empty((B, 1, H), device="cuda")
+    out = C.csa2_sparse_attn(bf16(q), i32(q_pos), i32(idx), win=bf16(a["win"]), win_pos0=i32(win_pos0),
+                             n_win=128, sink=f32(a["sink"]), out_mass=mass, num_splits=splits, **kvkw)
+    torch.cuda.synchronize()
+    want, wm = _oracle_attn(q, q_pos, kvd, idx, a["win"], win_pos0, 128, a["sink"], r)
+    assert np.abs(want[:, 0, :, 0]).min() > 20  # every head is dominated by the planted rows
+    assert_close(host(out), want, **BF16_TOL, what=f"attn restart {kv_format}")
+    assert_close(host(mass), wm, atol=1e-2, rtol=1e-2, what="mass restart")
