@@ -1,10 +1,10 @@
-"""Whole-step GPU parity on the five workloads at their full sizes, through the same call
+"""Whole-step GPU parity on the six workloads at their full sizes, through the same call
 chains (and so the same kernels and launch shapes) that the benchmark times.
 
 The tiny prefill is checked whole against the oracle.  At full size, the oracle computes
 sampled outputs one by one:
   - decode: every query's top-k indices (bit-exact) and attention output;
-  - FP4 decode and the hierarchical group: a sample of the sequences;
+  - FP4 decode, the hierarchical group and HCA decode: a sample of the sequences;
   - the 32K-token prefill: every compressed entry, indexer-K row and window row, plus a
     sample of the query positions (the earliest ones, block boundaries, the last ones and
     random ones).
@@ -20,7 +20,7 @@ import torch
 import oracle as O
 from oracle import formats as F
 from compressed_sparse_attention_gated_amd import workloads as W
-from compressed_sparse_attention_gated_amd.steps import DecodeStep, HierStep, PrefillStep
+from compressed_sparse_attention_gated_amd.steps import DecodeStep, HcaDecodeStep, HierStep, PrefillStep
 from tests._gpu import assert_close, banner, dev, f32, host, i32
 
 pytestmark = pytest.mark.gpu
@@ -172,6 +172,29 @@ def test_full_hier_group_b8_l1m(C):
             o_ref, _ = _oracle_attn_query(_np(e["q"][b, 0]), L, rows, _np(e["win"][b]), L - W_ + 1, W_,
                                           _np(e["sink"]), wl.rope_dims)
             assert_close(g_outs[layer][b, 0], o_ref, **BF16_TOL, what=f"attention layer {layer} b={b}")
+
+
+# =================================================================== HCA decode
+def test_full_hca_decode_b32_l1m(C):
+    wl = W.WORKLOADS[6]
+    banner("full HCA decode: B=32 L=1048576 m'=128 -> 8192 entries + 128 window, dense, 4 sequences checked")
+    d = W.hca_inputs(wl, 3006)
+    step = HcaDecodeStep(wl, d)
+    win_before = d["win"].clone()
+    _, out = step.run(d)
+    torch.cuda.synchronize()
+    go, gw = _np(out), _np(d["win"])
+    L, W_ = wl.L, wl.window
+    sink = _np(d["sink"])
+    for b in (0, 11, 22, 31):
+        new_row, _ = O.compress(_np(d["c_new"][b]), _np(d["z_new"][b]), 1, rope_dims=wl.rope_dims, pos0=L)
+        assert_close(gw[b, W_ - 1], new_row[0], **BF16_TOL, what=f"new window row b={b}")
+        win_ref = _np(win_before[b])
+        win_ref[W_ - 1] = new_row[0]
+        want, _ = O.dense_attn(_np(d["q"][b:b + 1]), np.array([[L]]), _np(d["kv"][b:b + 1]), wl.m,
+                               win=win_ref[None], win_pos0=[L - W_ + 1], window=W_, sink=sink,
+                               rope_dims=wl.rope_dims)
+        assert_close(go[b, 0], want[0, 0], **BF16_TOL, what=f"HCA attention b={b}")
 
 
 # =================================================================== 32K-token prefill

@@ -275,19 +275,23 @@ def test_attn_decode_mfma(C, kv_format, splits):
     assert_close(host(mass), wm, atol=1e-2, rtol=1e-2, what="mass")
 
 
-def test_attn_prefill_mfma_varied_windows_and_heads(C):
-    banner("attn prefill MFMA B=1 T=40 H=128 k=64, windows clipped by position, empty rows")
+@pytest.mark.parametrize("kv_format", ["bf16", "fp4"])
+def test_attn_prefill_mfma_varied_windows_and_heads(C, kv_format):
+    banner(f"attn prefill MFMA B=1 T=40 H=128 k=64 kv={kv_format}, windows clipped by position, empty rows")
     g = W.rng(21)
     T, N = 40, 500
-    a = W.attn_inputs(g, 1, T, N, 128, 512, Lw=201)
+    a = W.attn_inputs(g, 1, T, N, 128, 512, Lw=201, kv_format=kv_format)
     q_pos = (np.arange(T, dtype=np.int32) * 5)[None]  # 0 .. 195
     nv = np.minimum(q_pos // 2, N)
     idx = W.random_topk_lists(g, 1, T, nv, 64)
     win_pos0 = np.array([3], np.int32)  # queries before position 3 have no window rows
-    out = C.csa2_sparse_attn(bf16(a["q"]), i32(q_pos), i32(idx), kv=bf16(a["kv"]), win=bf16(a["win"]),
-                             win_pos0=i32(win_pos0), n_win=128, sink=f32(a["sink"]))
+    kvkw = (dict(kv=bf16(a["kv"])) if kv_format == "bf16"
+            else dict(kv_codes=u8(a["kv_codes"]), kv_scales=u8(a["kv_scales"])))
+    out = C.csa2_sparse_attn(bf16(a["q"]), i32(q_pos), i32(idx), win=bf16(a["win"]),
+                             win_pos0=i32(win_pos0), n_win=128, sink=f32(a["sink"]), **kvkw)
     torch.cuda.synchronize()
-    want, _ = _oracle_attn(a["q"], q_pos, a["kv"], idx, a["win"], win_pos0, 128, a["sink"], 64)
+    kvd = a["kv"] if kv_format == "bf16" else F.fp4_main_decode(a["kv_codes"], a["kv_scales"])
+    want, _ = _oracle_attn(a["q"], q_pos, kvd, idx, a["win"], win_pos0, 128, a["sink"], 64)
     got = host(out)
     assert np.all(got[0, 0] == 0)  # position 0: no visible entry, no window row
     assert_close(got, want, **BF16_TOL, what="attn prefill")
