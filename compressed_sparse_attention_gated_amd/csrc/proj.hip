@@ -108,41 +108,51 @@ __global__ void __launch_bounds__(kPT) gemm_nt(GemmArgs p) {
 }
 
 // Few rows (decode: one token per sequence): the product is a stream over the weights.  A
-// workgroup of kSplit waves owns one 32 x 32 tile of C; wave w takes the w-th 1/kSplit of
-// the contraction through the same register ring, and the partial tiles meet in LDS, added
-// in wave order (deterministic).  N/32 x batch workgroups, each reading its 32 weight rows
-// once.
+// workgroup of kSplit waves owns a 32 x 16NB tile of C as 2 x NB 16 x 16 accumulators; wave
+// w takes the w-th 1/kSplit of the contraction through the same register ring, and the
+// partial tiles meet in LDS, added in wave order (deterministic).  The 16 x 16 x 32 layout
+// gives each load 64 contiguous bytes of 16 rows (the 32 x 32 x 16 one gives 32 bytes of 32
+// rows), which streams the weights faster.  NB = 2 when N/32 x batch workgroups still fill
+// the 256 compute units, else NB = 1; each workgroup reads its weight rows once.
 constexpr int kSplit = 8;
+template <int NB>  // 16-column blocks per workgroup (1 or 2)
 __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
-  __shared__ float part[kSplit][16][64];
+  __shared__ float part[kSplit][8 * NB][64];
   const int z = blockIdx.z;
   const uint16_t* A = p.A + z * p.sa;
   const uint16_t* W = p.W + z * p.sw;
   uint16_t* Cz = p.C + z * p.sc;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 32;
-  const int r = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * 16 * NB;
+  // 16 x 16 x 32 operand layout: lane l reads row l % 16 of a 16-row block, the 8 k values
+  // at 8 * (l / 16) of every 32-wide k step, so one load covers 64 contiguous bytes of 16 rows
+  const int r = lane & 15, c = lane >> 4;
   const int kspan = p.K / kSplit;
-  const uint16_t* pa = A + (size_t)min(r, p.M - 1) * p.lda + wave * kspan + 8 * h;
-  const uint16_t* pw = W + (size_t)min(n0 + r, p.N - 1) * p.K + wave * kspan + 8 * h;
+  const size_t k0 = (size_t)wave * kspan + 8 * c;
+  const uint16_t* pa0 = A + (size_t)min(r, p.M - 1) * p.lda + k0;
+  const uint16_t* pa1 = A + (size_t)min(16 + r, p.M - 1) * p.lda + k0;
+  const uint16_t* pw0 = W + (size_t)min(n0 + r, p.N - 1) * p.K + k0;
+  const uint16_t* pw1 = W + (size_t)min(n0 + 16 * (NB - 1) + r, p.N - 1) * p.K + k0;
   const int nk = kspan / kKStep;
-  f32x16 acc = {};
+  f32x4 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};  // [row block][column block]
   struct Raw {
-    uint4 a[2], w[2];
+    uint4 a0, a1, w0, w1;
   };
   auto load = [&](int t, Raw& q) {
     const int k = min(t, nk - 1) * kKStep;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      q.a[s] = *reinterpret_cast<const uint4*>(pa + k + 16 * s);
-      q.w[s] = *reinterpret_cast<const uint4*>(pw + k + 16 * s);
-    }
+    q.a0 = *reinterpret_cast<const uint4*>(pa0 + k);
+    q.a1 = *reinterpret_cast<const uint4*>(pa1 + k);
+    q.w0 = *reinterpret_cast<const uint4*>(pw0 + k);
+    if (NB == 2) q.w1 = *reinterpret_cast<const uint4*>(pw1 + k);
   };
   auto use = [&](const Raw& q) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(q.a[s]), as_bf16x8(q.w[s]), acc, 0, 0, 0);
+    acc00 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a0), as_bf16x8(q.w0), acc00, 0, 0, 0);
+    acc10 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a1), as_bf16x8(q.w0), acc10, 0, 0, 0);
+    if (NB == 2) {
+      acc01 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a0), as_bf16x8(q.w1), acc01, 0, 0, 0);
+      acc11 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a1), as_bf16x8(q.w1), acc11, 0, 0, 0);
+    }
   };
   Raw ring[kDepth];
 #pragma unroll
@@ -163,16 +173,26 @@ __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
     if (t + i >= nk) break;
     use(ring[i]);
   }
+  // C layout of a 16 x 16 accumulator: lane l holds column l % 16, register i row
+  // 4 * (l / 16) + i; partial slot 4 * (NB * row block + column block) + i
 #pragma unroll
-  for (int i = 0; i < 16; ++i) part[wave][i][lane] = acc[i];
+  for (int i = 0; i < 4; ++i) {
+    part[wave][i][lane] = acc00[i];
+    part[wave][4 * NB + i][lane] = acc10[i];
+    if (NB == 2) {
+      part[wave][4 + i][lane] = acc01[i];
+      part[wave][12 + i][lane] = acc11[i];
+    }
+  }
   __syncthreads();
-  // thread (i, l) of the first 16 x 64 adds the waves' register i of lane l, in wave order
-  for (int e = threadIdx.x; e < 16 * 64; e += 64 * kSplit) {
-    const int i = e / 64, l = e % 64;
+  // thread (j, l) of the first 8NB x 64 adds the waves' slot j of lane l, in wave order
+  for (int e = threadIdx.x; e < 8 * NB * 64; e += 64 * kSplit) {
+    const int j = e / 64, l = e % 64;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kSplit; ++w) v += part[w][i][l];
-    const int m = 8 * (i / 4) + 4 * (l / 32) + (i % 4), n = n0 + (l & 31);
+    for (int w = 0; w < kSplit; ++w) v += part[w][j][l];
+    const int mb = j / (4 * NB), nb = (j / 4) % NB, i = j % 4;
+    const int m = 16 * mb + 4 * (l / 16) + i, n = n0 + 16 * nb + (l % 16);
     if (m < p.M && n < p.N) Cz[(size_t)m * p.ldc + n] = f32_to_bf16_bits(v);
   }
 }
@@ -279,8 +299,12 @@ __global__ void __launch_bounds__(256, 2) gemm_nt_lds(GemmArgs p) {
 hipError_t launch_gemm(const GemmArgs& p, int batch, hipStream_t s, const char* name) {
   ScopedProf prof(s, name);
   if (p.M <= 32 && p.K % (kSplit * kKStep) == 0) {
-    dim3 grid((p.N + 31) / 32, 1, batch);
-    hipLaunchKernelGGL(gemm_nt_splitk, grid, dim3(64 * kSplit), 0, s, p);
+    // 32 columns per workgroup when that still gives one per compute unit, else 16
+    if ((size_t)((p.N + 31) / 32) * batch >= 256) {
+      hipLaunchKernelGGL(gemm_nt_splitk<2>, dim3((p.N + 31) / 32, 1, batch), dim3(64 * kSplit), 0, s, p);
+    } else {
+      hipLaunchKernelGGL(gemm_nt_splitk<1>, dim3((p.N + 15) / 16, 1, batch), dim3(64 * kSplit), 0, s, p);
+    }
   } else if (p.M > 32 && p.K % kTK == 0) {
     dim3 grid((p.N + kTN - 1) / kTN, (p.M + kTM - 1) / kTM, batch);
     hipLaunchKernelGGL(gemm_nt_lds, grid, dim3(256), 0, s, p);

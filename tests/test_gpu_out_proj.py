@@ -23,6 +23,8 @@ def C():
 
 @pytest.mark.parametrize("M,n_h,c,g,d_g,d", [
     (5, 8, 64, 2, 64, 96),          # tiny, d not a multiple of the 64-column wave tile
+    (17, 16, 128, 4, 2032, 200),    # few rows: 32-column split-K tiles, last one half full
+    (17, 16, 128, 8, 504, 200),     # few rows: 16-column split-K tiles, last one half full
     (32, 64, 512, 8, 1024, 4096),   # V4-Flash shape at decode (one token per sequence)
     (300, 64, 512, 8, 1024, 4096),  # many tokens, ragged last row tile
 ])
