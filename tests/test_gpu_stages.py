@@ -352,3 +352,27 @@ def test_attn_reference_restart(C, kv_format, splits):
     assert np.abs(want[:, 0, :, 0]).min() > 20  # every head is dominated by the planted rows
     assert_close(host(out), want, **BF16_TOL, what=f"attn restart {kv_format}")
     assert_close(host(mass), wm, atol=1e-2, rtol=1e-2, what="mass restart")
+
+
+def test_attn_f32_large_score_jumps(C):
+    """The generic kernel's running softmax under the same planted rows: scores ~100 and
+    ~410 log2 units above the first rows' (fp32 I/O, c = 64, RoPE on the last 16)."""
+    banner("attn f32 large score jumps B=3 N=300 H=4 c=64 k=64 window 16")
+    g = W.rng(24)
+    B, N, H, c, r = 3, 300, 4, 64, 16
+    a = W.attn_inputs(g, B, 1, N, H, c, Lw=64, io_dtype="f32")
+    idx = W.random_topk_lists(g, B, 1, N, 64)
+    q = np.array(a["q"], np.float64)
+    kv = np.array(a["kv"], np.float64)
+    plant_high_scores(g, q, kv, [[(idx[b, 0, 5], 15.0), (idx[b, 0, 30], 60.0), (idx[b, 0, 60], 60.0)]
+                                 for b in range(B)], aligned=c - r)
+    q_pos = np.full((B, 1), 400, np.int32)
+    win_pos0 = np.full(B, 400 - 63, np.int32)
+    mass = torch.empty((B, 1, H), device="cuda")
+    out = C.csa2_sparse_attn(f32(q), i32(q_pos), i32(idx), kv=f32(kv), win=f32(a["win"]), win_pos0=i32(win_pos0),
+                             n_win=16, sink=f32(a["sink"]), rope_dims=r, out_mass=mass)
+    torch.cuda.synchronize()
+    want, wm = _oracle_attn(q, q_pos, kv, idx, a["win"], win_pos0, 16, a["sink"], r)
+    assert np.abs(want[:, 0, :, 0]).min() > 50
+    assert_close(host(out), want, **F32_TOL, what="attn f32 jumps")
+    assert_close(host(mass), wm, **F32_TOL, what="mass f32 jumps")
