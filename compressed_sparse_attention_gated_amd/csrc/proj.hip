@@ -108,16 +108,18 @@ __global__ void __launch_bounds__(kPT) gemm_nt(GemmArgs p) {
 }
 
 // Few rows (decode: one token per sequence): the product is a stream over the weights.  A
-// workgroup of kSplit waves owns a 32 x 16NB tile of C as 2 x NB 16 x 16 accumulators; wave
-// w takes the w-th 1/kSplit of the contraction through the same register ring, and the
-// partial tiles meet in LDS, added in wave order (deterministic).  The 16 x 16 x 32 layout
-// gives each load 64 contiguous bytes of 16 rows (the 32 x 32 x 16 one gives 32 bytes of 32
-// rows), which streams the weights faster.  NB = 2 when N/32 x batch workgroups still fill
-// the 256 compute units, else NB = 1; each workgroup reads its weight rows once.
+// workgroup of kSplit waves owns a 16MB x 16NB tile of C as MB x NB 16 x 16 accumulators
+// (MB = 2 for up to 32 rows, 4 for up to 64); wave w takes the w-th 1/kSplit of the
+// contraction through the same register ring, and the partial tiles meet in LDS, added in
+// wave order (deterministic).  The 16 x 16 x 32 layout gives each load 64 contiguous bytes
+// of 16 rows (the 32 x 32 x 16 one gives 32 bytes of 32 rows), which streams the weights
+// faster.  NB = 2 when N/32 x batch workgroups still fill the 256 compute units, else NB = 1;
+// each workgroup reads its weight rows once.
 constexpr int kSplit = 8;
-template <int NB>  // 16-column blocks per workgroup (1 or 2)
+constexpr int kSplitRows = 64;  // most rows the split-K kernel takes
+template <int MB, int NB>  // 16-row blocks (2 or 4), 16-column blocks (1 or 2) per workgroup
 __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
-  __shared__ float part[kSplit][8 * NB][64];
+  __shared__ float part[kSplit][4 * MB * NB][64];
   const int z = blockIdx.z;
   const uint16_t* A = p.A + z * p.sa;
   const uint16_t* W = p.W + z * p.sw;
@@ -130,29 +132,34 @@ __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
   const int r = lane & 15, c = lane >> 4;
   const int kspan = p.K / kSplit;
   const size_t k0 = (size_t)wave * kspan + 8 * c;
-  const uint16_t* pa0 = A + (size_t)min(r, p.M - 1) * p.lda + k0;
-  const uint16_t* pa1 = A + (size_t)min(16 + r, p.M - 1) * p.lda + k0;
-  const uint16_t* pw0 = W + (size_t)min(n0 + r, p.N - 1) * p.K + k0;
-  const uint16_t* pw1 = W + (size_t)min(n0 + 16 * (NB - 1) + r, p.N - 1) * p.K + k0;
+  const uint16_t* pa[MB];
+  const uint16_t* pw[NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) pa[mb] = A + (size_t)min(16 * mb + r, p.M - 1) * p.lda + k0;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) pw[nb] = W + (size_t)min(n0 + 16 * nb + r, p.N - 1) * p.K + k0;
   const int nk = kspan / kKStep;
-  f32x4 acc00 = {}, acc01 = {}, acc10 = {}, acc11 = {};  // [row block][column block]
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   struct Raw {
-    uint4 a0, a1, w0, w1;
+    uint4 a[MB], w[NB];
   };
   auto load = [&](int t, Raw& q) {
     const int k = min(t, nk - 1) * kKStep;
-    q.a0 = *reinterpret_cast<const uint4*>(pa0 + k);
-    q.a1 = *reinterpret_cast<const uint4*>(pa1 + k);
-    q.w0 = *reinterpret_cast<const uint4*>(pw0 + k);
-    if (NB == 2) q.w1 = *reinterpret_cast<const uint4*>(pw1 + k);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) q.a[mb] = *reinterpret_cast<const uint4*>(pa[mb] + k);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) q.w[nb] = *reinterpret_cast<const uint4*>(pw[nb] + k);
   };
   auto use = [&](const Raw& q) {
-    acc00 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a0), as_bf16x8(q.w0), acc00, 0, 0, 0);
-    acc10 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a1), as_bf16x8(q.w0), acc10, 0, 0, 0);
-    if (NB == 2) {
-      acc01 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a0), as_bf16x8(q.w1), acc01, 0, 0, 0);
-      acc11 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a1), as_bf16x8(q.w1), acc11, 0, 0, 0);
-    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(q.a[mb]), as_bf16x8(q.w[nb]), acc[mb][nb], 0, 0, 0);
   };
   Raw ring[kDepth];
 #pragma unroll
@@ -176,17 +183,14 @@ __global__ void __launch_bounds__(64 * kSplit) gemm_nt_splitk(GemmArgs p) {
   // C layout of a 16 x 16 accumulator: lane l holds column l % 16, register i row
   // 4 * (l / 16) + i; partial slot 4 * (NB * row block + column block) + i
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    part[wave][i][lane] = acc00[i];
-    part[wave][4 * NB + i][lane] = acc10[i];
-    if (NB == 2) {
-      part[wave][4 + i][lane] = acc01[i];
-      part[wave][12 + i][lane] = acc11[i];
-    }
-  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave][4 * (NB * mb + nb) + i][lane] = acc[mb][nb][i];
   __syncthreads();
-  // thread (j, l) of the first 8NB x 64 adds the waves' slot j of lane l, in wave order
-  for (int e = threadIdx.x; e < 8 * NB * 64; e += 64 * kSplit) {
+  // thread (j, l) of the first 4MB*NB x 64 adds the waves' slot j of lane l, in wave order
+  for (int e = threadIdx.x; e < 4 * MB * NB * 64; e += 64 * kSplit) {
     const int j = e / 64, l = e % 64;
     float v = 0.f;
 #pragma unroll
@@ -298,12 +302,16 @@ __global__ void __launch_bounds__(256, 2) gemm_nt_lds(GemmArgs p) {
 
 hipError_t launch_gemm(const GemmArgs& p, int batch, hipStream_t s, const char* name) {
   ScopedProf prof(s, name);
-  if (p.M <= 32 && p.K % (kSplit * kKStep) == 0) {
+  if (p.M <= kSplitRows && p.K % (kSplit * kKStep) == 0) {
     // 32 columns per workgroup when that still gives one per compute unit, else 16
-    if ((size_t)((p.N + 31) / 32) * batch >= 256) {
-      hipLaunchKernelGGL(gemm_nt_splitk<2>, dim3((p.N + 31) / 32, 1, batch), dim3(64 * kSplit), 0, s, p);
+    const bool wide = (size_t)((p.N + 31) / 32) * batch >= 256;
+    const dim3 grid(wide ? (p.N + 31) / 32 : (p.N + 15) / 16, 1, batch), block(64 * kSplit);
+    if (p.M <= 32) {
+      if (wide) hipLaunchKernelGGL((gemm_nt_splitk<2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((gemm_nt_splitk<2, 1>), grid, block, 0, s, p);
     } else {
-      hipLaunchKernelGGL(gemm_nt_splitk<1>, dim3((p.N + 15) / 16, 1, batch), dim3(64 * kSplit), 0, s, p);
+      if (wide) hipLaunchKernelGGL((gemm_nt_splitk<4, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((gemm_nt_splitk<4, 1>), grid, block, 0, s, p);
     }
   } else if (p.M > 32 && p.K % kTK == 0) {
     dim3 grid((p.N + kTN - 1) / kTN, (p.M + kTM - 1) / kTM, batch);

@@ -26,6 +26,9 @@ def C():
     (17, 16, 128, 4, 2032, 200),    # few rows: 32-column split-K tiles, last one half full
     (17, 16, 128, 8, 504, 200),     # few rows: 16-column split-K tiles, last one half full
     (32, 64, 512, 8, 1024, 4096),   # V4-Flash shape at decode (one token per sequence)
+    (64, 64, 512, 8, 1024, 4096),   # V4-Flash shape, 64 sequences (four 16-row blocks)
+    (40, 16, 128, 4, 2032, 200),    # 33..64 rows: 32-column split-K tiles, last one half full
+    (33, 16, 128, 8, 504, 200),     # 33..64 rows: 16-column split-K tiles, one row in block 2
     (300, 64, 512, 8, 1024, 4096),  # many tokens, ragged last row tile
 ])
 def test_out_proj(C, M, n_h, c, g, d_g, d):
