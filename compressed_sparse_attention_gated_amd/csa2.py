@@ -120,6 +120,33 @@ def _p(t):
     return None if t is None else C.c_void_p(t.data_ptr())
 
 
+_I32, _U8, _F32 = (torch.int32,), (torch.uint8,), (torch.float32,)
+_DATA = (torch.float32, torch.bfloat16)
+
+
+def _arg(name, t, dtypes, device, shape=None, rows_view=False):
+    """Check one tensor argument before its pointer goes to the library, which reads every
+    buffer as dense row-major memory of the stated dtype: it must be on the call's device,
+    of one of `dtypes`, contiguous (with rows_view: the last two dims contiguous, any batch
+    stride) and, if given, of `shape` (None entries are free).  Raises ValueError."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if rows_view:
+        if t.dim() != 3 or t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+            raise ValueError(f"{name}: [B, rows, c] with contiguous rows required (strides {t.stride()})")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (strides {tuple(t.stride())})")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple('*' if s is None else s for s in shape)}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -155,12 +182,40 @@ def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, n
     compressed on its own; out gets n//m rows (an upper bound), out_cu_entries [S+1] the
     samples' entry offsets.  With plain_out=False and quantised planes given, the
     plain outputs are not allocated (returned as None) unless passed."""
+    if not isinstance(ca, torch.Tensor) or ca.dim() != 3:
+        raise ValueError("ca: a [B, n, c] tensor is required")
     B, n, c = ca.shape
     ne = n // m
+    dv, dt = ca.device, (ca.dtype,)
+    _arg("ca", ca, _DATA, dv)
+    for name, t in (("za", za), ("cb", cb), ("zb", zb)):
+        _arg(name, t, dt, dv, (B, n, c))
+    for name, t in (("ba", ba), ("bb", bb)):
+        _arg(name, t, _F32, dv, (m, c))
+    for name, t in (("cb0", cb0), ("zb0", zb0)):
+        _arg(name, t, dt, dv, (B, m, c))
+    S = None if cu_seqlens is None else cu_seqlens.numel() - 1
+    _arg("pos0", pos0, _I32, dv, (B if S is None else S,))
+    _arg("dst_row", dst_row, _I32, dv, (B,))
+    _arg("cu_seqlens", cu_seqlens, _I32, dv, (None,))
+    _arg("out_cu_entries", out_cu_entries, _I32, dv, (None if S is None else S + 1,))
+    _arg("out", out, dt, dv, (B, None, c), rows_view=True)
+    d_w = None
+    if w_ik is not None:
+        _arg("w_ik", w_ik, dt, dv, (c, None))
+        d_w = w_ik.shape[1]
+    _arg("out_ik", out_ik, dt, dv, (B, None, d_w), rows_view=True)
+    # the FP4 and MXFP4 planes share one row count (q_rows bounds both)
     q_rows = 0
     for t in (out_codes, ik_codes):
         if t is not None:
             q_rows = t.shape[1]
+    _arg("out_codes", out_codes, _U8, dv, (B, q_rows, c // 2))
+    _arg("out_scales", out_scales, _U8, dv, (B, q_rows, c // 16))
+    if (ik_codes is not None or ik_scales is not None) and d_w is None:
+        raise ValueError("ik_codes / ik_scales need w_ik")
+    _arg("ik_codes", ik_codes, _U8, dv, (B, q_rows, None if d_w is None else d_w // 2))
+    _arg("ik_scales", ik_scales, _U8, dv, (B, q_rows, None if d_w is None else d_w // 32))
     if out is None and (plain_out or out_codes is None):
         out = torch.empty((B, ne, c), dtype=ca.dtype, device=ca.device)
     d_index = 0
@@ -187,10 +242,25 @@ def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, n
 def _index_desc(q_idx, w, q_pos, k, m, *, k_idx=None, k_codes=None, k_scales=None, N=None,
                 cand=None, n_cand=None, src_idx=None, out_idx=None, out_block_max=None, block=8,
                 out_scores=None):
+    if not isinstance(q_pos, torch.Tensor) or q_pos.dim() != 2:
+        raise ValueError("q_pos: a [B, T] int32 tensor is required")
     B, T = q_pos.shape
+    dv = q_pos.device
+    _arg("q_pos", q_pos, _I32, dv, (B, T))
+    _arg("q_idx", q_idx, (torch.bfloat16,), dv, (B, T, None, None))
     H_I, d_I = (q_idx.shape[2], q_idx.shape[3]) if q_idx is not None else (1, 32)
+    _arg("w", w, _F32, dv, (B, T, H_I))
     if N is None:
         N = (k_idx.shape[1] if k_idx is not None else (k_codes.shape[1] if k_codes is not None else 0))
+    _arg("k_idx", k_idx, (torch.bfloat16,), dv, (B, N, d_I))
+    _arg("k_codes", k_codes, _U8, dv, (B, N, d_I // 2))
+    _arg("k_scales", k_scales, _U8, dv, (B, N, d_I // 32))
+    _arg("cand", cand, _I32, dv, (B, T, None))
+    _arg("n_cand", n_cand, _I32, dv, (B, T))
+    _arg("src_idx", src_idx, _I32, dv, (B, T, k))
+    _arg("out_idx", out_idx, _I32, dv, (B, T, k))
+    _arg("out_block_max", out_block_max, _F32, dv, (B, T, -(-N // block)))
+    _arg("out_scores", out_scores, _F32, dv, (B, T, N if cand is None else cand.shape[-1]))
     return IndexDesc(B=B, T=T, H_I=H_I, d_I=d_I, N=N, m=m, k=k, q_idx=_p(q_idx), w=_p(w),
                      q_pos=_p(q_pos), k_dtype=CSA2_MXFP4 if k_codes is not None else CSA2_BF16,
                      k_idx=_p(k_idx), k_codes=_p(k_codes), k_scales=_p(k_scales), cand=_p(cand),
@@ -232,6 +302,10 @@ def csa2_hier_candidates(block_max, q_pos, N, *, m=1, block=8, n_keep=2048, out_
     """block_max [B, T, ceil(N/block)] -> (cand [B, T, n_keep*block], count [B, T])."""
     B, T = q_pos.shape
     dev = q_pos.device
+    _arg("q_pos", q_pos, _I32, dev, (B, T))
+    _arg("block_max", block_max, _F32, dev, (B, T, -(-N // block)))
+    _arg("out_cand", out_cand, _I32, dev, (B, T, n_keep * block))
+    _arg("out_count", out_count, _I32, dev, (B, T))
     if out_cand is None:
         out_cand = torch.empty((B, T, n_keep * block), dtype=torch.int32, device=dev)
     if out_count is None:
@@ -256,9 +330,23 @@ def csa2_hier_workspace_bytes(block_max, q_pos, N, *, m=1, block=8, n_keep=2048)
 def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
                win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0, eps=1e-6,
                scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0, dense_m=0):
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q: a [B, T, H, c] tensor is required")
     B, T, H, c = q.shape
+    dv, dt = q.device, (q.dtype,)
+    _arg("q", q, _DATA, dv)
+    _arg("q_pos", q_pos, _I32, dv, (B, T))
+    _arg("idx", idx, _I32, dv, (B, T, None))
     if N is None:
         N = kv.shape[1] if kv is not None else (kv_codes.shape[1] if kv_codes is not None else 0)
+    _arg("kv", kv, dt, dv, (B, N, c))
+    _arg("kv_codes", kv_codes, _U8, dv, (B, N, c // 2))
+    _arg("kv_scales", kv_scales, _U8, dv, (B, N, c // 16))
+    _arg("win", win, dt, dv, (B, None, c))
+    _arg("win_pos0", win_pos0, _I32, dv, (B,))
+    _arg("sink", sink, _F32, dv, (H,))
+    _arg("out", out, dt, dv, (B, T, H, c))
+    _arg("out_mass", out_mass, _F32, dv, (B, T, H))
     kvdt = CSA2_FP4_E4M3 if kv_codes is not None else _DT[q.dtype]
     return AttnDesc(B=B, T=T, H=H, c=c, k=idx.shape[-1] if idx is not None else 0, N=N,
                     rope_dims=rope_dims, rope_theta=rope_theta, eps=eps, scale=scale,
@@ -300,6 +388,12 @@ def csa2_out_proj(o, w1, w2, *, mid=None, out=None, stream=None):
     M = o.numel() // (n_h * c)
     g, d_g = w1.shape[0], w1.shape[1]
     dd = w2.shape[0]
+    bf, dv = (torch.bfloat16,), o.device
+    _arg("o", o, bf, dv)
+    _arg("w1", w1, bf, dv, (g, d_g, c * n_h // g))
+    _arg("w2", w2, bf, dv, (dd, g * d_g))
+    _arg("mid", mid, bf, dv, (M, g * d_g))
+    _arg("out", out, bf, dv, (M, dd))
     if mid is None:
         mid = torch.empty((M, g * d_g), dtype=torch.bfloat16, device=o.device)
     if out is None:

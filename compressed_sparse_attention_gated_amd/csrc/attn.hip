@@ -482,6 +482,10 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
   const int my_head = 32 * half + 16 * hq + li;  // WG-local head of this lane's S^T column
 
   float m_use = -INFINITY, l_part = 0.f;  // head my_head, rows of half mr (replicated over g)
+  // Set once the reference is fixed.  It is decided from the tile's row validity, which is
+  // the same for every wave, so the barrier inside that branch is reached by all waves even
+  // when a head's scores are NaN (fmaxf drops NaN, which would leave its max at -inf).
+  bool ref_set = false;
   f32x4 oacc[2][8];
   for (int pass = 0;; ++pass) {
     if (pass > 0) {  // restart with a larger reference: every wave left the loop together
@@ -502,6 +506,8 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
       if (ti + 1 < tile1) fetch_tile<kFP4>(rb, src + kTile, pf);
       // valid rows of this wave's blocks: row 32*kk + 16*mr + r <-> bit 16*kk + r
       const uint32_t vm = (uint32_t)__ballot(lane < 16 * kKK && src[32 * (lane >> 4) + 16 * mr + (lane & 15)] != -1);
+      // any valid row in the whole tile: identical in every wave
+      const bool tile_any = __ballot(lane < kTile && src[lane] != -1) != 0;
 
       const uint8_t* tl = sm.tile[buf];
       const lds_u8* tl3 = (const lds_u8*)tl;
@@ -533,11 +539,13 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
       // of its rows (exchanged between the two waves of a head block).  Validity is per row,
       // the same for every head, so the branch is uniform over the workgroup.  Later tiles
       // only check their own rows against it; the overflow flag is exchanged with P below.
-      if (m_use == -INFINITY) {
+      // A head whose scores are all NaN has no max: it takes 0 (its output is NaN anyway).
+      if (!ref_set && tile_any) {
         if (g == 0) sm.wmax[mr][my_head] = tmax;
         lds_barrier();
         tmax = fmaxf(sm.wmax[0][my_head], sm.wmax[1][my_head]);
-        m_use = tmax;  // O is still 0
+        m_use = tmax == -INFINITY ? 0.f : tmax;  // O is still 0
+        ref_set = true;
       }
       const bool ovf = tmax > m_use + kOverflow;
       if (g == 0) sm.omax[mr][my_head] = tmax;

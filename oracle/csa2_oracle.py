@@ -42,17 +42,30 @@ import math
 import numpy as np
 
 # ============================================================ compressor
+def _logsumexp(terms):
+    """log(sum_j exp(terms[j])) over axis 0, per channel; -inf terms contribute nothing."""
+    t = np.asarray(terms, np.float64)
+    top = t.max(axis=0)
+    safe = np.where(np.isfinite(top), top, 0.0)
+    with np.errstate(divide="ignore"):  # all terms -inf: log 0 = -inf
+        return safe + np.log(np.exp(t - safe).sum(axis=0))
+
+
 def gated_pool(c_a, z_a, m, *, b_a=None, c_b=None, z_b=None, b_b=None, overlap=False):
     """Gated per-channel softmax pooling over blocks of m tokens.
 
     Non-overlap (CSA2, [Evolution blog] §4.1, and HCA eq. (22)-(23) of
-    [DSA-to-CSA notes]): entry i pools tokens [m*i, m*i+m); for every channel the
-    weights are a softmax over the m gate logits (Z + optional position bias B).
+    [DSA-to-CSA notes]): entry i pools tokens [m*i, m*i+m).  For channel ch the gate
+    logit of token j is Z[j,ch] + B[j-m*i, ch], and entry i is the weighted sum of
+    C[j,ch] with weights exp(logit_j - LSE), where LSE = log sum_j exp(logit_j): a
+    softmax over the block's positions, separately for every channel.
 
-    Overlap (CSA, [DSA-to-CSA notes] eq. (11)-(12)): entry i takes a per-channel
-    softmax over 2m candidates, the current block through (C^a, Z^a + B^a) and the
-    previous block through (C^b, Z^b + B^b).  Block 0 has no previous block: its
-    history logits are -inf and its history values 0, so they get zero weight.
+    Overlap (CSA, [DSA-to-CSA notes] eq. (11)-(12)): the candidates of entry i are the
+    current block (values C^a, logits Z^a + B^a) and the previous block (values C^b,
+    logits Z^b + B^b).  Both sets share one normaliser LSE over all 2m logits, and the
+    entry is the current-block sum plus the history sum.  Block 0 has no previous block:
+    the pages give its history logits -inf (and values 0), so its history weights are 0
+    and only the current block enters its normaliser and its sum.
 
     Only complete blocks are pooled; a ragged tail of n % m tokens is ignored.
     Inputs are [n, c]; biases are [m, c] or None (= 0).  Returns [n // m, c] fp64.
@@ -61,28 +74,22 @@ def gated_pool(c_a, z_a, m, *, b_a=None, c_b=None, z_b=None, b_b=None, overlap=F
     z_a = np.asarray(z_a, np.float64)
     n, c = c_a.shape
     ba = np.zeros((m, c)) if b_a is None else np.asarray(b_a, np.float64)
-    if overlap:
-        c_b = np.asarray(c_b, np.float64)
-        z_b = np.asarray(z_b, np.float64)
-        bb = np.zeros((m, c)) if b_b is None else np.asarray(b_b, np.float64)
+    bb = np.zeros((m, c)) if b_b is None else np.asarray(b_b, np.float64)
     out = np.zeros((n // m, c))
     for i in range(n // m):
-        cur = slice(m * i, m * i + m)
-        logits = [z_a[cur] + ba]
-        values = [c_a[cur]]
-        if overlap:
-            if i == 0:
-                logits.append(np.full((m, c), -np.inf))
-                values.append(np.zeros((m, c)))
-            else:
-                prev = slice(m * (i - 1), m * i)
-                logits.append(z_b[prev] + bb)
-                values.append(c_b[prev])
-        lg = np.concatenate(logits, axis=0)
-        vals = np.concatenate(values, axis=0)
-        p = np.exp(lg - lg.max(axis=0))
-        p = p / p.sum(axis=0)
-        out[i] = (p * vals).sum(axis=0)
+        cur_logit = z_a[m * i:m * i + m] + ba          # [m, c]
+        cur_value = c_a[m * i:m * i + m]
+        has_history = overlap and i > 0
+        if has_history:
+            hist_logit = np.asarray(z_b, np.float64)[m * (i - 1):m * i] + bb
+            hist_value = np.asarray(c_b, np.float64)[m * (i - 1):m * i]
+            lse = _logsumexp(np.concatenate([_logsumexp(cur_logit)[None], _logsumexp(hist_logit)[None]]))
+        else:
+            lse = _logsumexp(cur_logit)
+        y = (np.exp(cur_logit - lse) * cur_value).sum(axis=0)
+        if has_history:
+            y = y + (np.exp(hist_logit - lse) * hist_value).sum(axis=0)
+        out[i] = y
     return out
 
 

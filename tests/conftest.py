@@ -11,6 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload (minutes of host work)")
+    # a planted mistake in the oracle (tests/test_oracle_mutations.py runs the pins against
+    # each one in a child process; CPU only)
+    mutant = os.environ.get("CSA2_ORACLE_MUTANT")
+    if mutant:
+        from tests import _mutants
+
+        _mutants.apply(mutant)
 
 
 def pytest_collection_modifyitems(config, items):

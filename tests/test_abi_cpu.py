@@ -236,3 +236,36 @@ def test_attn_dense_workspace_counts_every_entry(L):
     dense = L.csa2_attn_workspace_bytes(C.byref(d))
     d = csa2.AttnDesc(**{**base, "dense_m": 0, "k": 8192, "idx": FAKE})
     assert dense == L.csa2_attn_workspace_bytes(C.byref(d)) > 0
+
+
+# ---------------------------------------------------------------- binding argument checks
+def test_binding_rejects_bad_tensors_before_any_call():
+    # the library reads every buffer as dense memory of one dtype: the binding refuses
+    # strided views, wrong dtypes and mismatched plane shapes before anything is called
+    import torch
+
+    from compressed_sparse_attention_gated_amd import csa2
+
+    B, T, H, c, N, k = 2, 1, 64, 512, 40, 8
+    q = torch.zeros((B, T, H, c), dtype=torch.bfloat16)
+    q_pos = torch.zeros((B, T), dtype=torch.int32)
+    kv = torch.zeros((B, 2 * N, c), dtype=torch.bfloat16)
+    idx64 = torch.zeros((B, T, k), dtype=torch.int64)  # torch.topk's index dtype
+    idx = torch.zeros((B, T, k), dtype=torch.int32)
+    with pytest.raises(ValueError, match="idx: dtype"):
+        csa2.csa2_sparse_attn(q, q_pos, idx64, kv=kv)
+    with pytest.raises(ValueError, match="kv: must be contiguous"):
+        csa2.csa2_sparse_attn(q, q_pos, idx, kv=kv[:, ::2])  # a strided cache view
+    with pytest.raises(ValueError, match="q_pos: dtype"):
+        csa2.csa2_sparse_attn(q, q_pos.long(), idx, kv=kv)
+    ca = torch.zeros((1, 8, 512), dtype=torch.bfloat16)
+    w_ik = torch.zeros((512, 128), dtype=torch.bfloat16)
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)  # noqa: E731
+    with pytest.raises(ValueError, match="codes: shape"):  # planes with different row counts
+        csa2.csa2_compress(ca, ca, 1, w_ik=w_ik, out_codes=u8(1, 8, 256), out_scales=u8(1, 8, 32),
+                           ik_codes=u8(1, 4, 64), ik_scales=u8(1, 4, 4))
+    with pytest.raises(ValueError, match="za: dtype"):
+        csa2.csa2_compress(ca, ca.float(), 1)
+    with pytest.raises(ValueError, match="k_idx: dtype"):
+        csa2.csa2_index_topk(csa2.CSA2_MODE_FULL, q_pos, k, q_idx=torch.zeros((B, T, 64, 128), dtype=torch.bfloat16),
+                             w=torch.zeros((B, T, 64)), k_idx=torch.zeros((B, N, 128)))

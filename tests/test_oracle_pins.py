@@ -604,3 +604,14 @@ def test_packed_compressor_overlap_history_stops_at_sample_start():
     # the third sample's first entry: no history, so the same as without overlap
     no_hist, _ = O.compress(ca[6:8], za[6:8], m, norm=False)
     np.testing.assert_allclose(ent[2], no_hist[0], rtol=1e-15, atol=1e-15)
+
+
+def test_packed_compressor_positions_restart_per_sample():
+    # m = 1 without norm writes each token rotated by its position; on c = r = 2 the
+    # rotation of (1, 0) by angle p * theta^0 is (cos p, sin p).  Every sample's tokens
+    # take positions 0, 1, .. of their own sample, not of the stream.
+    x = np.tile([[1.0, 0.0]], (5, 1))
+    ent, _, cu_e = O.compress_packed(x, np.zeros_like(x), 1, [0, 3, 5], norm=False, rope_dims=2)
+    pos = np.array([0, 1, 2, 0, 1], np.float64)
+    np.testing.assert_allclose(ent, np.stack([np.cos(pos), np.sin(pos)], axis=1), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(cu_e, [0, 3, 5])
