@@ -173,3 +173,33 @@ class PrefillStep:
                            n_win=wl.window, sink=d["sink"], rope_dims=wl.rope_dims, out=self.out,
                            workspace=self.ws_attn)
         return self.entries, self.k_index, self.win, self.idx, self.out
+
+
+def written_fp4_cache(wl, seed, pool_rows=65536):
+    """A decode cache of wl.B x wl.L entries written by the library's own write path:
+    `pool_rows` source rows ~ N(0,1) go through csa2_compress (m = 1: RMSNorm, RoPE at the
+    row's index, FP4 E2M1 codes with E4M3 scales per 16 channels), and as many indexer-K rows
+    of integers U{-3..3} through its K_I projection with an identity W_ik and no norm (MXFP4,
+    exact for these integers); the pools are tiled over the context by seeded random indices.
+    Returns (kv_codes, kv_scales, k_codes, k_scales)."""
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    c, d_I = wl.c, wl.d_I
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    src = torch.randn((1, pool_rows, c), generator=g, device=dev).to(torch.bfloat16)
+    kv_c, kv_s = u8(1, pool_rows, c // 2), u8(1, pool_rows, c // 16)
+    C.csa2_compress(src, src, 1, rope_dims=wl.rope_dims, out_codes=kv_c, out_scales=kv_s, plain_out=False)
+    ints = torch.randint(-3, 4, (1, pool_rows, c), generator=g, device=dev).to(torch.bfloat16)
+    eye = torch.zeros((c, d_I), dtype=torch.bfloat16, device=dev)
+    eye[torch.arange(d_I), torch.arange(d_I)] = 1
+    scratch_c, scratch_s = u8(1, pool_rows, c // 2), u8(1, pool_rows, c // 16)
+    k_c, k_s = u8(1, pool_rows, d_I // 2), u8(1, pool_rows, d_I // 32)
+    C.csa2_compress(ints, ints, 1, norm=False, w_ik=eye, out_codes=scratch_c, out_scales=scratch_s,
+                    ik_codes=k_c, ik_scales=k_s, plain_out=False)
+    pick_kv = torch.randint(0, pool_rows, (wl.B, wl.L), generator=g, device=dev)
+    pick_k = torch.randint(0, pool_rows, (wl.B, wl.L), generator=g, device=dev)
+    out = (kv_c[0][pick_kv].contiguous(), kv_s[0][pick_kv].contiguous(), k_c[0][pick_k].contiguous(),
+           k_s[0][pick_k].contiguous())
+    del pick_kv, pick_k
+    return out

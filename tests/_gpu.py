@@ -79,3 +79,28 @@ def plant_high_scores(g, q, kv, ids_gammas, aligned=256, fp4=False):
                 row = F.fp4_main_decode(*F.quantize_fp4_main(row[None]))[0]
             kv[b, e] = row
 
+
+def oracle_quantised_cache(B, L, seed, pool_rows=32768, c=512, d_I=128, rope_dims=64):
+    """A decode cache of B x L entries in the 4-bit formats, quantised by the oracle: main
+    KV rows are N(0,1) source rows after the write path's RMSNorm and RoPE (at the pool
+    index), stored as FP4 E2M1 with E4M3 scales per 16; indexer-K rows are integers
+    U{-3..3} stored as MXFP4 (exact).  `pool_rows` distinct rows of each are quantised on
+    the host and tiled over the cache by seeded random indices drawn on the device.
+    Returns device tensors (kv_codes, kv_scales, k_codes, k_scales)."""
+    import oracle as O
+
+    r = np.random.Generator(np.random.PCG64(seed))
+    src = r.standard_normal((pool_rows, c))
+    rows = O.rope(O.rms_norm(src), np.arange(pool_rows), rope_dims)
+    kv_codes, kv_scales = F.quantize_fp4_main(rows)
+    ki = r.integers(-3, 4, size=(pool_rows, d_I)).astype(np.float64)
+    k_codes, k_scales = F.quantize_mxfp4(ki)
+    assert np.array_equal(F.mxfp4_decode(k_codes, k_scales), ki)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    pick_kv = torch.randint(0, pool_rows, (B, L), generator=g, device=DEV)
+    pick_k = torch.randint(0, pool_rows, (B, L), generator=g, device=DEV)
+    out = []
+    for pool, pick in ((kv_codes, pick_kv), (kv_scales, pick_kv), (k_codes, pick_k), (k_scales, pick_k)):
+        out.append(u8(pool)[pick].contiguous())
+    return tuple(out)

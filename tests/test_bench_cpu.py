@@ -35,6 +35,8 @@ def test_cpu_baseline_decode_kinds(cfg, kw, build):
         d = W.decode_inputs(wl, 3, device="cpu")
     r = bench.cpu_baseline(torch, wl, d, 0.05)
     assert r["value"] > 0 and r["unit"] == "queries/s" and r["kind"] == "oracle" and r["cores"] >= 1
+    assert r["nproc"] >= 1 and r["cpu_count"] >= r["nproc"] and "cpu_model" in r
+    assert r["single_thread"]["value"] > 0 and r["single_thread"]["cores"] == 1
 
 
 def test_cpu_baseline_prefill():

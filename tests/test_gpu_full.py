@@ -21,7 +21,7 @@ import oracle as O
 from oracle import formats as F
 from compressed_sparse_attention_gated_amd import workloads as W
 from compressed_sparse_attention_gated_amd.steps import DecodeStep, HcaDecodeStep, HierStep, PrefillStep
-from tests._gpu import assert_close, banner, dev, f32, host, i32
+from tests._gpu import assert_close, banner, dev, f32, host, i32, oracle_quantised_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -96,8 +96,10 @@ def test_tiny_prefill_end_to_end(C):
 
 
 # =================================================================== decode (bf16 and FP4)
-def _check_decode(C, wl, seed, sample):
+def _check_decode(C, wl, seed, sample, cache=None):
     d = W.decode_inputs(wl, seed)
+    if cache is not None:
+        d["kv_codes"], d["kv_scales"], d["k_codes"], d["k_scales"] = cache
     step = DecodeStep(wl, d)
     win_before = d["win"].clone()
     idx, out = step.run(d)
@@ -138,9 +140,19 @@ def test_full_decode_bf16_b32_l65536(C):
 
 
 def test_full_decode_fp4_b64_l262144(C):
+    # the cache as the workload states it: N(0,1) source rows through the write path's
+    # RMSNorm and RoPE, quantised by the oracle (FP4 main KV, MXFP4 integer K_I)
     wl = W.WORKLOADS[5]
-    banner("full FP4 decode: B=64 L=262144 FP4 main KV + MXFP4 K_I, 8 queries checked")
-    _check_decode(C, wl, 3005, [0, 9, 18, 27, 36, 45, 54, 63])
+    banner("full FP4 decode: B=64 L=262144 oracle-quantised FP4 main KV + MXFP4 K_I, 8 queries checked")
+    cache = oracle_quantised_cache(wl.B, wl.L, 3015)
+    _check_decode(C, wl, 3005, [0, 9, 18, 27, 36, 45, 54, 63], cache=cache)
+
+
+def test_full_decode_fp4_random_codes(C):
+    # every FP4 / MXFP4 code value and a spread of scale bytes (random bytes), fewer queries
+    wl = W.WORKLOADS[5]
+    banner("full FP4 decode: B=64 L=262144 random code bytes, 3 queries checked")
+    _check_decode(C, wl, 3025, [1, 32, 62])
 
 
 # =================================================================== hierarchical group

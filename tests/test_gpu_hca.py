@@ -103,9 +103,8 @@ def test_hca_layer_compress_then_dense_attention(C):
     out = C.csa2_sparse_attn(bf16(a["q"]), i32(q_pos), None, kv=ent, win=win, win_pos0=i32(np.zeros(1)),
                              n_win=128, sink=f32(a["sink"]), rope_dims=64, dense_m=mp)
     torch.cuda.synchronize()
-    # the oracle reads the library's own bf16 entries and window rows (checked above against
-    # the fp64 compressor), so the attention comparison is not blurred by the write's rounding
-    want, _ = O.dense_attn(a["q"], q_pos, host(ent), mp, win=host(win), win_pos0=[0], window=128,
+    # end to end: the oracle attends over its own fp64 entries and window rows
+    want, _ = O.dense_attn(a["q"], q_pos, e_ref[None], mp, win=w_ref[None], win_pos0=[0], window=128,
                            sink=a["sink"], rope_dims=64)
     assert_close(host(out), want, **BF16_TOL, what="hca layer")
     assert_close(host(win)[0], w_ref, **BF16_TOL, what="window rows")

@@ -275,6 +275,33 @@ def test_attn_decode_mfma(C, kv_format, splits):
     assert_close(host(mass), wm, atol=1e-2, rtol=1e-2, what="mass")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_attn_nan_head_leaves_other_heads_exact(C, splits):
+    # A zero query head with eps = 0 normalises to 0/0 = NaN, so all its scores are NaN.
+    # The softmax reference of the workgroup is fixed on a condition shared by every head
+    # (a valid row in the tile), so that head's NaN stays in its own output and the other
+    # 63 heads of the workgroup (and of the query) match the oracle.
+    banner(f"attn NaN head: B=2 N=3000 H=64 c=512 k=512 eps=0, query 0 head 5 zero, splits={splits}")
+    g = W.rng(27)
+    B, N, L = 2, 3000, 3000
+    a = W.attn_inputs(g, B, 1, N, 64, 512, Lw=128)
+    idx = W.random_topk_lists(g, B, 1, N, 512)
+    q = np.array(a["q"], np.float32)
+    q[0, 0, 5] = 0.0
+    q_pos = np.full((B, 1), L, np.int32)
+    win_pos0 = np.full(B, L - 127, np.int32)
+    out = C.csa2_sparse_attn(bf16(q), i32(q_pos), i32(idx), kv=bf16(a["kv"]), win=bf16(a["win"]),
+                             win_pos0=i32(win_pos0), n_win=128, sink=f32(a["sink"]), eps=0.0, num_splits=splits)
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want, _ = O.sparse_attn(q, q_pos, a["kv"], idx, a["win"], win_pos0, 128, a["sink"], rope_dims=64, eps=0.0)
+    got = host(out)
+    assert np.isnan(want[0, 0, 5]).all()
+    keep = np.ones((B, 1, 64), bool)
+    keep[0, 0, 5] = False
+    assert_close(got[keep], want[keep], **BF16_TOL, what="heads other than the NaN head")
+
+
 @pytest.mark.parametrize("kv_format", ["bf16", "fp4"])
 def test_attn_prefill_mfma_varied_windows_and_heads(C, kv_format):
     banner(f"attn prefill MFMA B=1 T=40 H=128 k=64 kv={kv_format}, windows clipped by position, empty rows")
