@@ -64,7 +64,7 @@ class KernelTime(C.Structure):
     _fields_ = [("name", C.c_char * 48), ("ms", C.c_float)]
 
 
-EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk",
+EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk", "csa2_index_topk_noalloc",
            "csa2_hier_workspace_bytes", "csa2_hier_candidates", "csa2_attn_workspace_bytes",
            "csa2_sparse_attn", "csa2_out_proj", "csa2_version", "csa2_last_error", "csa2_profile_enable",
            "csa2_profile_collect"]
@@ -88,6 +88,7 @@ def lib():
     L.csa2_index_workspace_bytes.argtypes = [C.POINTER(IndexDesc), _i]
     L.csa2_index_workspace_bytes.restype = C.c_size_t
     L.csa2_index_topk.argtypes = [C.POINTER(IndexDesc), _i, _vp, C.c_size_t, _vp]
+    L.csa2_index_topk_noalloc.argtypes = [C.POINTER(IndexDesc), _i, _vp]
     L.csa2_hier_workspace_bytes.argtypes = [C.POINTER(HierDesc)]
     L.csa2_hier_workspace_bytes.restype = C.c_size_t
     L.csa2_hier_candidates.argtypes = [C.POINTER(HierDesc), _vp, C.c_size_t, _vp]
@@ -284,6 +285,20 @@ def csa2_index_topk(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_co
     if workspace is None or workspace.numel() < nbytes:
         workspace = _ws(nbytes, dev)
     _check(lib().csa2_index_topk(C.byref(d), mode, _p(workspace), nbytes, _stream(stream)))
+    return out_idx
+
+
+def csa2_index_topk_noalloc(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_codes=None,
+                            k_scales=None, N=None, cand=None, n_cand=None, src_idx=None, out_idx=None,
+                            out_block_max=None, block=8, out_scores=None, stream=None):
+    """csa2_index_topk with the library's static scratch instead of a workspace (for callers
+    that cannot allocate).  out_idx must be given: nothing is allocated."""
+    if out_idx is None:
+        raise ValueError("out_idx is required: the no-allocation call allocates nothing")
+    d = _index_desc(q_idx, w, q_pos, k, m, k_idx=k_idx, k_codes=k_codes, k_scales=k_scales, N=N,
+                    cand=cand, n_cand=n_cand, src_idx=src_idx, out_idx=out_idx,
+                    out_block_max=out_block_max, block=block, out_scores=out_scores)
+    _check(lib().csa2_index_topk_noalloc(C.byref(d), mode, _stream(stream)))
     return out_idx
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -305,6 +306,50 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
   t.max_len = len;
   t.ws = tk_ws; t.ws_bytes = tk_bytes;
   return hip_status(launch_topk(t, s), "index/topk");
+}
+
+// --------------------------------------------------------------- index + top-k, no allocation
+// The workspace of csa2_index_topk_noalloc lives in this file-scope device array, one copy
+// per GPU, held until the process ends.  In host code the array's name is only a stand-in:
+// its device address comes from hipGetSymbolAddress, once per device, with that device
+// current, and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch` (resolved on first use on that device)
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" int csa2_index_topk_noalloc(const csa2_index_desc* d, csa2_mode mode, void* stream) {
+  int rc = check_index(d, mode);
+  if (rc != CSA2_OK) return rc;
+  const size_t need = index_ws(d, mode);
+  if (need > CSA2_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA2_ERR_WORKSPACE, "index (no-alloc): this call needs %zu bytes of scratch, the static array holds %zu",
+                need, (size_t)CSA2_NOALLOC_SCRATCH_BYTES);
+  if (need == 0) return csa2_index_topk(d, mode, nullptr, 0, stream);
+  void* ws = nullptr;
+  hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e, "index (no-alloc): scratch address");
+  return csa2_index_topk(d, mode, ws, CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // --------------------------------------------------------------- hierarchical pool

@@ -201,6 +201,18 @@ typedef struct {
 CSA2_API size_t csa2_index_workspace_bytes(const csa2_index_desc *d, csa2_mode mode);
 CSA2_API int csa2_index_topk(const csa2_index_desc *d, csa2_mode mode, void *ws, size_t ws_bytes, void *stream);
 
+/* csa2_index_topk_noalloc: csa2_index_topk without a workspace argument, for callers that
+ *   cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc).  Same descriptor, modes, results and errors; the
+ *   workspace is a static device array of CSA2_NOALLOC_SCRATCH_BYTES held by the library on
+ *   each GPU it runs on until the process ends.  Calls needing more than that (see
+ *   csa2_index_workspace_bytes) fail with CSA2_ERR_WORKSPACE before anything is enqueued:
+ *   decode-shaped FULL calls (up to ~500 queries of 1M entries) fit, whole-prefill score
+ *   matrices do not.  The call allocates nothing.  Every call on one GPU shares that GPU's
+ *   array: calls that overlap in time on one GPU (other streams, other threads) race. */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+CSA2_API int csa2_index_topk_noalloc(const csa2_index_desc *d, csa2_mode mode, void *stream);
+
 /* ------------------------------------------------------------------ hierarchical pool
  * csa2_hier_candidates: the decoder's hierarchical candidate pool ([CSA2 column],
  *   "解码器里的分层索引"; [Evolution blog] §4.4).  For each query: blocks
