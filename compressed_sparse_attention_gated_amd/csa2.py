@@ -38,7 +38,7 @@ class IndexDesc(C.Structure):
                 ("q_idx", _vp), ("w", _vp), ("q_pos", _vp), ("k_dtype", _i), ("k_idx", _vp),
                 ("k_codes", _vp), ("k_scales", _vp), ("cand", _vp), ("n_cand", _vp),
                 ("cand_stride", _i), ("src_idx", _vp), ("out_idx", _vp), ("out_block_max", _vp),
-                ("block", _i), ("out_scores", _vp)]
+                ("block", _i), ("out_scores", _vp), ("ent_base", _vp)]
 
 
 class HierDesc(C.Structure):
@@ -52,7 +52,7 @@ class AttnDesc(C.Structure):
                 ("q_dtype", _i), ("q", _vp), ("q_pos", _vp), ("kv_dtype", _i), ("kv", _vp),
                 ("kv_codes", _vp), ("kv_scales", _vp), ("idx", _vp), ("win", _vp), ("Lw", _i),
                 ("win_pos0", _vp), ("n_win", _i), ("sink", _vp), ("out", _vp), ("out_mass", _vp),
-                ("num_splits", _i), ("dense_m", _i)]
+                ("num_splits", _i), ("dense_m", _i), ("win_row0", _vp)]
 
 
 class OutProjDesc(C.Structure):
@@ -71,7 +71,7 @@ EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk", "cs
 
 _lib = None
 # the descriptor layouts below are those of this version of include/csa2.h
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def lib():
@@ -242,7 +242,7 @@ def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, n
 # ---------------------------------------------------------------------------- index + top-k
 def _index_desc(q_idx, w, q_pos, k, m, *, k_idx=None, k_codes=None, k_scales=None, N=None,
                 cand=None, n_cand=None, src_idx=None, out_idx=None, out_block_max=None, block=8,
-                out_scores=None):
+                out_scores=None, ent_base=None):
     if not isinstance(q_pos, torch.Tensor) or q_pos.dim() != 2:
         raise ValueError("q_pos: a [B, T] int32 tensor is required")
     B, T = q_pos.shape
@@ -262,25 +262,28 @@ def _index_desc(q_idx, w, q_pos, k, m, *, k_idx=None, k_codes=None, k_scales=Non
     _arg("out_idx", out_idx, _I32, dv, (B, T, k))
     _arg("out_block_max", out_block_max, _F32, dv, (B, T, -(-N // block)))
     _arg("out_scores", out_scores, _F32, dv, (B, T, N if cand is None else cand.shape[-1]))
+    _arg("ent_base", ent_base, _I32, dv, (B, T))
     return IndexDesc(B=B, T=T, H_I=H_I, d_I=d_I, N=N, m=m, k=k, q_idx=_p(q_idx), w=_p(w),
                      q_pos=_p(q_pos), k_dtype=CSA2_MXFP4 if k_codes is not None else CSA2_BF16,
                      k_idx=_p(k_idx), k_codes=_p(k_codes), k_scales=_p(k_scales), cand=_p(cand),
                      n_cand=_p(n_cand), cand_stride=cand.shape[-1] if cand is not None else 0,
                      src_idx=_p(src_idx), out_idx=_p(out_idx), out_block_max=_p(out_block_max),
-                     block=block, out_scores=_p(out_scores))
+                     block=block, out_scores=_p(out_scores), ent_base=_p(ent_base))
 
 
 def csa2_index_topk(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_codes=None,
                     k_scales=None, N=None, cand=None, n_cand=None, src_idx=None, out_idx=None,
-                    out_block_max=None, block=8, out_scores=None, workspace=None, stream=None):
-    """FULL / REINDEX / REUSE.  Returns out_idx [B, T, k] int32."""
+                    out_block_max=None, block=8, out_scores=None, ent_base=None, workspace=None,
+                    stream=None):
+    """FULL / REINDEX / REUSE.  Returns out_idx [B, T, k] int32.  ent_base [B, T] (FULL):
+    packed samples, the first entry id of each query's sample (q_pos is sample-local)."""
     B, T = q_pos.shape
     dev = q_pos.device
     if out_idx is None:
         out_idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
     d = _index_desc(q_idx, w, q_pos, k, m, k_idx=k_idx, k_codes=k_codes, k_scales=k_scales, N=N,
                     cand=cand, n_cand=n_cand, src_idx=src_idx, out_idx=out_idx,
-                    out_block_max=out_block_max, block=block, out_scores=out_scores)
+                    out_block_max=out_block_max, block=block, out_scores=out_scores, ent_base=ent_base)
     nbytes = lib().csa2_index_workspace_bytes(C.byref(d), mode)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _ws(nbytes, dev)
@@ -290,14 +293,14 @@ def csa2_index_topk(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_co
 
 def csa2_index_topk_noalloc(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_codes=None,
                             k_scales=None, N=None, cand=None, n_cand=None, src_idx=None, out_idx=None,
-                            out_block_max=None, block=8, out_scores=None, stream=None):
+                            out_block_max=None, block=8, out_scores=None, ent_base=None, stream=None):
     """csa2_index_topk with the library's static scratch instead of a workspace (for callers
     that cannot allocate).  out_idx must be given: nothing is allocated."""
     if out_idx is None:
         raise ValueError("out_idx is required: the no-allocation call allocates nothing")
     d = _index_desc(q_idx, w, q_pos, k, m, k_idx=k_idx, k_codes=k_codes, k_scales=k_scales, N=N,
                     cand=cand, n_cand=n_cand, src_idx=src_idx, out_idx=out_idx,
-                    out_block_max=out_block_max, block=block, out_scores=out_scores)
+                    out_block_max=out_block_max, block=block, out_scores=out_scores, ent_base=ent_base)
     _check(lib().csa2_index_topk_noalloc(C.byref(d), mode, _stream(stream)))
     return out_idx
 
@@ -307,7 +310,7 @@ def csa2_index_workspace_bytes(mode, q_pos, k, **kw):
                     k_codes=kw.get("k_codes"), k_scales=kw.get("k_scales"), N=kw.get("N"),
                     cand=kw.get("cand"), n_cand=kw.get("n_cand"), src_idx=kw.get("src_idx"),
                     out_idx=kw.get("out_idx"), out_block_max=kw.get("out_block_max"),
-                    block=kw.get("block", 8), out_scores=kw.get("out_scores"))
+                    block=kw.get("block", 8), out_scores=kw.get("out_scores"), ent_base=kw.get("ent_base"))
     return lib().csa2_index_workspace_bytes(C.byref(d), mode)
 
 
@@ -344,7 +347,7 @@ def csa2_hier_workspace_bytes(block_max, q_pos, N, *, m=1, block=8, n_keep=2048)
 # ---------------------------------------------------------------------------- attention
 def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
                win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0, eps=1e-6,
-               scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0, dense_m=0):
+               scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0, dense_m=0, win_row0=None):
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q: a [B, T, H, c] tensor is required")
     B, T, H, c = q.shape
@@ -362,6 +365,7 @@ def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None,
     _arg("sink", sink, _F32, dv, (H,))
     _arg("out", out, dt, dv, (B, T, H, c))
     _arg("out_mass", out_mass, _F32, dv, (B, T, H))
+    _arg("win_row0", win_row0, _I32, dv, (B, T))
     kvdt = CSA2_FP4_E4M3 if kv_codes is not None else _DT[q.dtype]
     return AttnDesc(B=B, T=T, H=H, c=c, k=idx.shape[-1] if idx is not None else 0, N=N,
                     rope_dims=rope_dims, rope_theta=rope_theta, eps=eps, scale=scale,
@@ -369,21 +373,23 @@ def _attn_desc(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None,
                     kv_dtype=kvdt, kv=_p(kv), kv_codes=_p(kv_codes), kv_scales=_p(kv_scales),
                     idx=_p(idx), win=_p(win), Lw=win.shape[1] if win is not None else 0,
                     win_pos0=_p(win_pos0), n_win=n_win if win is not None else 0, sink=_p(sink),
-                    out=_p(out), out_mass=_p(out_mass), num_splits=num_splits, dense_m=dense_m)
+                    out=_p(out), out_mass=_p(out_mass), num_splits=num_splits, dense_m=dense_m,
+                    win_row0=_p(win_row0))
 
 
 def csa2_sparse_attn(q, q_pos, idx, *, kv=None, kv_codes=None, kv_scales=None, N=None, win=None,
                      win_pos0=None, n_win=128, sink=None, rope_dims=64, rope_theta=10000.0,
                      eps=1e-6, scale=0.0, q_norm=True, out=None, out_mass=None, num_splits=0,
-                     dense_m=0, workspace=None, stream=None):
+                     dense_m=0, win_row0=None, workspace=None, stream=None):
     """q [B, T, H, c] -> out [B, T, H, c] (dtype of q).  dense_m > 0 (idx None): dense
-    attention over every entry visible at the query's position (entries of dense_m tokens)."""
+    attention over every entry visible at the query's position (entries of dense_m tokens).
+    win_row0 [B, T]: packed samples, the window row of position 0 of each query's sample."""
     if out is None:
         out = torch.empty_like(q)
     d = _attn_desc(q, q_pos, idx, kv=kv, kv_codes=kv_codes, kv_scales=kv_scales, N=N, win=win,
                    win_pos0=win_pos0, n_win=n_win, sink=sink, rope_dims=rope_dims,
                    rope_theta=rope_theta, eps=eps, scale=scale, q_norm=q_norm, out=out,
-                   out_mass=out_mass, num_splits=num_splits, dense_m=dense_m)
+                   out_mass=out_mass, num_splits=num_splits, dense_m=dense_m, win_row0=win_row0)
     nbytes = lib().csa2_attn_workspace_bytes(C.byref(d))
     if workspace is None or workspace.numel() < nbytes:
         workspace = _ws(nbytes, q.device)

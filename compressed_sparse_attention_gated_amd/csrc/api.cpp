@@ -199,6 +199,8 @@ static int check_index(const csa2_index_desc* d, csa2_mode mode) {
   }
   if (mode == CSA2_MODE_FULL && d->out_block_max && !pow2_upto(d->block, 32))
     return fail(CSA2_ERR_UNSUPPORTED, "index: block must be a power of two <= 32");
+  if (d->ent_base && mode != CSA2_MODE_FULL)
+    return fail(CSA2_ERR_INVALID, "index: ent_base (packed samples) is for FULL mode only");
   if (mode == CSA2_MODE_REINDEX) {
     if (!d->cand || !d->n_cand || d->cand_stride < 1) return fail(CSA2_ERR_INVALID, "index: REINDEX needs cand, n_cand, cand_stride >= 1");
     if (d->N == 0) return fail(CSA2_ERR_INVALID, "index: REINDEX with N == 0");
@@ -210,7 +212,7 @@ static int check_index(const csa2_index_desc* d, csa2_mode mode) {
 // decode-style FULL calls (few queries per sequence, long rows) fuse the chunk-local
 // top-k into the scan; the workspace then holds (key, slot) pairs instead of scores
 static bool use_fused(const csa2_index_desc* d, csa2_mode mode) {
-  return mode == CSA2_MODE_FULL && d->T < 8 && d->N > 8192 &&
+  return mode == CSA2_MODE_FULL && !d->ent_base && d->T < 8 && d->N > 8192 &&
          scan_select_chunk((int)(d->B * d->T), d->N, d->k) <= kMaxSelectChunk;
 }
 
@@ -291,6 +293,7 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
     a.scores = scores; a.row_stride = len;
     a.block_max = mode == CSA2_MODE_FULL ? d->out_block_max : nullptr;
     a.nblk = (d->N + a.block - 1) / a.block;
+    a.ent_base = mode == CSA2_MODE_FULL ? d->ent_base : nullptr;
     hipError_t e = launch_index_scan(a, s);
     if (e != hipSuccess) return hip_status(e, "index/scan");
   }
@@ -298,7 +301,7 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
   t.rows = (int)rows; t.k = d->k; t.scores = scores; t.row_stride = len;
   t.out_idx = d->out_idx;
   if (mode == CSA2_MODE_FULL) {
-    t.q_pos = d->q_pos; t.N = d->N; t.m = d->m;
+    t.q_pos = d->q_pos; t.N = d->N; t.m = d->m; t.id_base = d->ent_base;
   } else {
     t.counts = d->n_cand; t.idx_map = d->cand; t.idx_map_stride = d->cand_stride;
   }
@@ -423,8 +426,10 @@ static int check_attn(const csa2_attn_desc* d) {
     if (d->kv_dtype != CSA2_FP4_E4M3 && !d->kv) return fail(CSA2_ERR_INVALID, "attn: kv required");
   }
   if (d->win) {
-    if (!d->win_pos0 || d->Lw < 0 || d->n_win < 0) return fail(CSA2_ERR_INVALID, "attn: window needs win_pos0, Lw >= 0, n_win >= 0");
+    if ((!d->win_pos0 && !d->win_row0) || d->Lw < 0 || d->n_win < 0)
+      return fail(CSA2_ERR_INVALID, "attn: window needs win_pos0 (or win_row0), Lw >= 0, n_win >= 0");
   }
+  if (d->win_row0 && !d->win) return fail(CSA2_ERR_INVALID, "attn: win_row0 without a window");
   return CSA2_OK;
 }
 

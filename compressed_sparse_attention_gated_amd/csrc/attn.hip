@@ -46,6 +46,7 @@ struct AttnDev {
   const int32_t* idx;
   const void* win;
   const int32_t* win_pos0;
+  const int32_t* win_row0;  // [rows] or null: packed samples, the window row of the sample's position 0
   const float* sink;
   void* out;
   float* out_mass;
@@ -70,7 +71,17 @@ __device__ __forceinline__ WinRange window_of_p0(const AttnDev& a, int p0, int t
   if (hi >= lo) { w.lo_row = lo - p0; w.cnt = hi - lo + 1; }
   return w;
 }
-__device__ __forceinline__ WinRange window_of(const AttnDev& a, int b, int t_pos) {
+// The window rows of query `row` (sequence b, position t_pos).  Packed samples: positions
+// [max(0, t - W + 1), t] of the query's own sample, at rows win_row0 + position.
+__device__ __forceinline__ WinRange window_of(const AttnDev& a, int b, int row, int t_pos) {
+  if (a.win && a.n_win > 0 && a.win_row0) {
+    WinRange w{0, 0};
+    const int r0 = a.win_row0[row];
+    const int lo = max(r0 + max(t_pos - a.n_win + 1, 0), 0);
+    const int hi = min(r0 + t_pos, a.Lw - 1);
+    if (t_pos >= 0 && hi >= lo) { w.lo_row = lo; w.cnt = hi - lo + 1; }
+    return w;
+  }
   return window_of_p0(a, (a.win && a.n_win > 0) ? a.win_pos0[b] : 0, t_pos);
 }
 
@@ -127,7 +138,7 @@ __global__ void __launch_bounds__(64) attn_simple(AttnDev a) {
 #pragma unroll
   for (int j = 0; j < kSimpleMaxPerLane; ++j) qv[j] *= a.scale_log2;
 
-  const WinRange wr = window_of(a, b, t_pos);
+  const WinRange wr = window_of(a, b, row, t_pos);
   const int R = a.k + wr.cnt;
   const int lim = slot_limit(a, t_pos);
   float m_run = -INFINITY, l_run = 0.f;
@@ -419,7 +430,7 @@ __global__ void __launch_bounds__(kThreadsM, 1) attn_mfma(AttnDev a) {
   int ids[kSlotsPerThread];
   ids_of_split(a, row, tile0 * kTile, a.tiles_per_split * kTile, ids);
   const int t_pos = a.q_pos[row];
-  const WinRange wr = window_of(a, b, t_pos);
+  const WinRange wr = window_of(a, b, row, t_pos);
   const int R = a.k + wr.cnt;
   const int n_tiles = (R + kTile - 1) / kTile;
   const int tile1 = min(tile0 + a.tiles_per_split, n_tiles);
@@ -802,7 +813,7 @@ AttnDev make_dev(const csa2_attn_desc& d) {
   a.q_f32 = d.q_dtype == CSA2_F32;
   a.kv_kind = d.kv_dtype == CSA2_FP4_E4M3 ? 1 : 0;
   a.q = d.q; a.q_pos = d.q_pos; a.kv = d.kv; a.kv_codes = d.kv_codes; a.kv_scales = d.kv_scales;
-  a.idx = d.idx; a.win = d.win; a.win_pos0 = d.win_pos0; a.sink = d.sink; a.out = d.out;
+  a.idx = d.idx; a.win = d.win; a.win_pos0 = d.win_pos0; a.win_row0 = d.win_row0; a.sink = d.sink; a.out = d.out;
   a.out_mass = d.out_mass;
   a.dense_m = d.dense_m;
   a.n_hg = d.H / kHG;
@@ -838,7 +849,7 @@ hipError_t launch_attn(const csa2_attn_desc& d0, void* ws, size_t ws_bytes, hipS
   const bool rows_needed = d.k > 0 && d.N > 0;
   if (!d.q || !d.q_pos || !d.out || (d.k > 0 && !d.idx && d.dense_m == 0) ||
       (rows_needed && d.kv_dtype == CSA2_FP4_E4M3 && (!d.kv_codes || !d.kv_scales)) ||
-      (rows_needed && d.kv_dtype != CSA2_FP4_E4M3 && !d.kv) || (d.win && !d.win_pos0))
+      (rows_needed && d.kv_dtype != CSA2_FP4_E4M3 && !d.kv) || (d.win && !d.win_pos0 && !d.win_row0))
     return hipErrorInvalidValue;
   AttnDev a = make_dev(d);
   if (!mfma_ok(d)) {

@@ -48,6 +48,7 @@ struct Dev {
   float* scores;
   int64_t row_stride;
   float* block_max;
+  const int32_t* ent_base;  // [rows] or null: packed samples, the query's first entry
 };
 
 // Dimension order inside one 16-wide k-step.  For bf16 rows, lane half h holds dims
@@ -236,10 +237,15 @@ __device__ __forceinline__ float epi1(const f32x16* acc, const float (*wreg)[16]
   return sum_xor32(x);
 }
 
+// the first entry id a query may see: 0, or its sample's first entry (packed samples)
+__device__ __forceinline__ int entry_base(const Dev& a, int row) {
+  return a.ent_base ? min(max(a.ent_base[row], 0), a.N) : 0;
+}
 __device__ __forceinline__ int n_visible(const Dev& a, int row) {
   const int t = a.q_pos[row];
   const int nv = t >= 0 ? t / a.m : 0;
-  return nv < a.N ? nv : a.N;
+  const int cap = a.N - entry_base(a, row);
+  return nv < cap ? nv : cap;
 }
 
 // block maxima of one 32-slot tile: max over aligned groups of `block` lanes (quad swaps,
@@ -319,13 +325,14 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
   load_query<DI, KF, MT>(a, row, lane, areg, wreg);
 
   const int h = lane / 32;
+  const int eb = kCand ? 0 : entry_base(a, row);
   auto entry_of = [&](int slot) -> int {
     int s = min(slot, c1 - 1);
     if constexpr (kCand) {
       int e = a.cand[(size_t)row * a.cand_stride + s];
       return min(max(e, 0), a.N - 1);
     }
-    return s;
+    return eb + s;
   };
 
   constexpr int kStride = 32 * kWaves;
@@ -626,7 +633,9 @@ hipError_t launch3(const ScanArgs& s, const Dev& d, hipStream_t st) {
   const int rows = s.B * s.T;
   const bool cand = s.cand != nullptr;
   const bool bm = s.block_max != nullptr;
-  if (!cand && s.T >= kShWaves) {
+  // the shared-tile prefill scan gives 8 consecutive queries one entry range: packed
+  // samples (a range per query) take the private scan
+  if (!cand && s.T >= kShWaves && !s.ent_base) {
     dim3 grid(((s.T + kShWaves - 1) / kShWaves) * s.B);
     if (bm) hipLaunchKernelGGL((scan_shared<DI, KF, MT, true>), grid, dim3(kShThreads), 0, st, d);
     else hipLaunchKernelGGL((scan_shared<DI, KF, MT, false>), grid, dim3(kShThreads), 0, st, d);
@@ -696,6 +705,7 @@ Dev make_dev(const ScanArgs& s) {
   d.k_idx = (const uint16_t*)s.k_idx; d.k_codes = s.k_codes; d.k_scales = s.k_scales;
   d.cand = s.cand; d.n_cand = s.n_cand; d.scores = s.scores; d.row_stride = s.row_stride;
   d.block_max = s.block_max;
+  d.ent_base = s.ent_base;
   return d;
 }
 
@@ -717,7 +727,8 @@ int scan_select_chunk(int rows, int N, int k) {
 hipError_t launch_index_scan_select(const ScanArgs& s, int k, int chunk, int nchunks, uint32_t* keys,
                                     int32_t* slots, uint2* bounds, hipStream_t st) {
   if (s.B * s.T == 0) return hipSuccess;
-  if (!s.q_idx || !s.w || !s.q_pos || !keys || !slots || !bounds || s.cand || (s.N > 0 && s.k_dtype == CSA2_BF16 && !s.k_idx) ||
+  if (!s.q_idx || !s.w || !s.q_pos || !keys || !slots || !bounds || s.cand || s.ent_base ||
+      (s.N > 0 && s.k_dtype == CSA2_BF16 && !s.k_idx) ||
       (s.N > 0 && s.k_dtype == CSA2_MXFP4 && (!s.k_codes || !s.k_scales)) || chunk % 128 != 0 || k < 1)
     return hipErrorInvalidValue;
   const Dev d = make_dev(s);

@@ -39,6 +39,7 @@ struct ScanArgs {
   int64_t row_stride;
   float* block_max;       // [B*T, nblk] or null (FULL only)
   int nblk;
+  const int32_t* ent_base;  // [B*T] or null: a query's entries start at this id (packed samples)
 };
 hipError_t launch_index_scan(const ScanArgs& a, hipStream_t s);
 
@@ -61,6 +62,8 @@ struct TopkArgs {
   int max_len;             // upper bound of len over rows (sizes the launch)
   void* ws;                // workspace for the two-level path
   size_t ws_bytes;
+  const int32_t* id_base;  // [rows] or null: reported id = slot + id_base[row] (packed samples;
+                           // the row length is also clamped to N - id_base[row])
 };
 size_t topk_workspace_bytes(int rows, int k, int max_len);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);

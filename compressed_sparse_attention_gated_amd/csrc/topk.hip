@@ -47,6 +47,7 @@ struct Params {
   uint32_t* ws_keys;  // [rows, nchunks*k]
   int32_t* ws_slot;   // [rows, nchunks*k]
   uint2* ws_bound;    // [rows, nchunks]: (bound, count) - count keys of the chunk are >= bound
+  const int32_t* id_base;  // [rows] or null: reported id = slot + id_base[row]
 };
 
 
@@ -58,7 +59,8 @@ __device__ __forceinline__ int row_len(const Params& p, int r) {
   } else {
     const int t = p.q_pos[r];
     len = t >= 0 ? t / p.m : 0;
-    if (len > p.N) len = p.N;
+    const int cap = p.id_base ? p.N - min(max(p.id_base[r], 0), p.N) : p.N;
+    if (len > cap) len = cap;
   }
   if (p.len_div > 1) len = (len + p.len_div - 1) / p.len_div;
   if (len > p.max_len) len = p.max_len;
@@ -66,7 +68,8 @@ __device__ __forceinline__ int row_len(const Params& p, int r) {
 }
 
 __device__ __forceinline__ int32_t map_id(const Params& p, int r, int slot) {
-  return p.idx_map ? p.idx_map[(size_t)r * p.idx_map_stride + slot] : slot;
+  if (p.idx_map) return p.idx_map[(size_t)r * p.idx_map_stride + slot];
+  return p.id_base ? slot + min(max(p.id_base[r], 0), p.N) : slot;
 }
 
 // Keys of a row or chunk staged once into LDS (vector loads); all passes then run from
@@ -416,7 +419,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   p.rows = a.rows; p.k = a.k; p.scores = a.scores; p.row_stride = a.row_stride;
   p.counts = a.counts; p.q_pos = a.q_pos; p.N = a.N; p.m = a.m; p.len_div = a.len_div;
   p.force_last = a.force_last; p.idx_map = a.idx_map; p.idx_map_stride = a.idx_map_stride;
-  p.out_idx = a.out_idx;
+  p.out_idx = a.out_idx; p.id_base = a.id_base;
   p.max_len = a.max_len;
   hipError_t e;
   if (a.max_len <= kSingleMax) {
@@ -479,7 +482,7 @@ hipError_t launch_topk_merge(const TopkArgs& a, int nchunks, uint32_t* keys, int
   Params p{};
   p.rows = a.rows; p.k = a.k; p.counts = a.counts; p.q_pos = a.q_pos; p.N = a.N; p.m = a.m;
   p.len_div = a.len_div; p.force_last = a.force_last; p.idx_map = a.idx_map;
-  p.idx_map_stride = a.idx_map_stride; p.out_idx = a.out_idx; p.max_len = a.max_len;
+  p.idx_map_stride = a.idx_map_stride; p.out_idx = a.out_idx; p.max_len = a.max_len; p.id_base = a.id_base;
   p.nchunks = nchunks; p.ws_keys = keys; p.ws_slot = slots; p.ws_bound = bounds;
   int cap, defer, prune;
   const size_t lds = merge_lds(nchunks * a.k, a.k, bounds != nullptr, &cap, &defer, &prune);

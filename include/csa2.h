@@ -31,7 +31,8 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 2 /* 2: write-path, packed-sample, dense-attention and projection fields */
+#define CSA2_VERSION 3 /* 2: write-path, packed-sample, dense-attention and projection fields;
+                          3: per-query sample bounds of index and attention over packed streams */
 #define CSA2_MAX_PACKED_SAMPLES 4096
 
 #if defined(__GNUC__) || defined(__clang__)
@@ -178,6 +179,13 @@ CSA2_API int csa2_compress(const csa2_compress_desc *d, void *stream);
  *   out_scores: fp32 [B, T, N] (FULL) or [B, T, cand_stride] (REINDEX), or NULL; only
  *     visible / candidate slots are written.
  *   ws, ws_bytes: device workspace of at least csa2_index_workspace_bytes(d, mode).
+ *   ent_base: NULL, or int32 [B, T] (FULL only): packed samples.  The entries of a query's
+ *     own sample start at id ent_base[b,t] of the stream's entries (csa2_compress with
+ *     cu_seqlens reports them in out_cu_entries), q_pos is the query's position within its
+ *     sample, and it sees entries ent_base + [0, n_vis) with n_vis = min(N - ent_base,
+ *     floor(q_pos/m)): no entry of another sample ([DSA-to-CSA notes], checklist "怎样验证":
+ *     the indexer mask must not cross a sample boundary).  out_idx holds stream entry ids;
+ *     out_scores / out_block_max are indexed by the sample-local slot.
  * Supported: H_I <= 64 (heads beyond H_I are zero-padded internally), d_I in {32, 64, 128},
  *   block in {1, 2, 4, 8, 16, 32}, k <= 4096.
  */
@@ -196,6 +204,7 @@ typedef struct {
   float *out_block_max;
   int block;
   float *out_scores;
+  const int32_t *ent_base;
 } csa2_index_desc;
 
 CSA2_API size_t csa2_index_workspace_bytes(const csa2_index_desc *d, csa2_mode mode);
@@ -264,6 +273,12 @@ CSA2_API int csa2_hier_candidates(const csa2_hier_desc *d, void *ws, size_t ws_b
  *     ignored, and the rows are entries 0 .. n_vis-1 with n_vis = min(N, floor(p / dense_m))
  *     (an entry is visible once its block of dense_m tokens has ended: "因果边界与短滑窗"),
  *     then the window rows as above.
+ *   win_row0: NULL, or int32 [B, T]: packed samples.  The window buffer win[b] holds the
+ *     stream's per-token rows, and row win_row0[b,t] holds position 0 of the query's own
+ *     sample (q_pos is the position within that sample).  The window is then the rows
+ *     win_row0 + x for x in [max(0, p - window + 1), p], clipped to [0, Lw): it never
+ *     reaches into the sample before ([DSA-to-CSA notes], checklist "怎样验证": the sliding
+ *     window must not cross a sample boundary).  win_pos0 is not read.
  * Supported: c % 16 == 0, c <= 512, rope_dims even and <= c; FP4 needs bf16 q.
  *   The MFMA paths run for bf16 q, c == 512, H % 32 == 0, rope_dims <= 128; other shapes
  *   use a generic fp32 kernel with the same semantics.
@@ -290,6 +305,7 @@ typedef struct {
   int num_splits; /* row-range splits per query (0 = chosen by the library); a tuning knob
                      that does not change results beyond fp32 rounding order */
   int dense_m;
+  const int32_t *win_row0;
 } csa2_attn_desc;
 
 CSA2_API size_t csa2_attn_workspace_bytes(const csa2_attn_desc *d);

@@ -393,6 +393,69 @@ def dense_attn(q, q_pos, kv, m_prime, win=None, win_pos0=None, window=128, sink=
                        rope_dims=rope_dims, theta=theta, eps=eps, scale=scale, q_norm=q_norm)
 
 
+# ============================================================ packed samples
+def packed_sample_of(t, cu_seqlens):
+    """The sample holding stream token t: s with cu[s] <= t < cu[s+1]."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    return int(np.searchsorted(cu, t, side="right") - 1)
+
+
+def packed_visible_entries(t, cu_seqlens, cu_entries, m):
+    """Stream entry ids the indexer of stream token t may score ([DSA-to-CSA notes], checklist
+    "怎样验证": the indexer mask must not cross a sample boundary).  t is token p of its sample
+    s, which owns entries cu_e[s] .. cu_e[s+1]-1 (compress_packed's offsets); the causal rule
+    applies within the sample: cu_e[s] + [0, n_visible(p))."""
+    s = packed_sample_of(t, cu_seqlens)
+    p = int(t) - int(cu_seqlens[s])
+    n_s = int(cu_entries[s + 1]) - int(cu_entries[s])
+    return int(cu_entries[s]) + np.arange(n_visible(p, n_s, m))
+
+
+def packed_window_rows(t, cu_seqlens, window):
+    """Stream rows in the sliding window of token t: the latest `window` tokens of its own
+    sample up to and including t (the window must not cross a sample boundary either)."""
+    s = packed_sample_of(t, cu_seqlens)
+    return np.arange(max(int(cu_seqlens[s]), int(t) - window + 1), int(t) + 1)
+
+
+def index_topk_packed(q_idx, w, k_idx, cu_seqlens, cu_entries, m, k):
+    """FULL mode over a packed stream: q_idx [T, H_I, d_I], w [T, H_I] for every token,
+    k_idx [N, d_I] the stream's entries.  Each token scores only its sample's visible
+    entries; returns stream entry ids [T, k] (ascending, -1 padded)."""
+    T = np.asarray(q_idx).shape[0]
+    out = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        ids = packed_visible_entries(t, cu_seqlens, cu_entries, m)
+        s = indexer_scores(q_idx[t], w[t], np.asarray(k_idx)[ids])
+        sel = topk_indices(s, k)
+        out[t] = np.where(sel >= 0, ids[np.maximum(sel, 0)] if len(ids) else -1, -1)
+    return out
+
+
+def sparse_attn_packed(q, kv, idx, win, cu_seqlens, window=128, sink=None, rope_dims=64,
+                       theta=10000.0, eps=1e-6, scale=None, q_norm=True, tokens=None):
+    """Shared-KV sparse MQA over a packed stream: q [T, H, c] for every token, kv [N, c] the
+    stream's entries, idx [T, k] stream entry ids, win [T, c] the stream's per-token rows.
+    Token t (position p in its sample) attends to its selected entries and the window rows
+    of its own sample; RoPE and the inverse rotation use p.  `tokens` (optional) limits the
+    work to those tokens (the others stay zero).  Returns (out [T, H, c], mass [T, H])."""
+    q = np.asarray(q, np.float64)
+    T, H, c = q.shape
+    out = np.zeros((T, H, c))
+    mass = np.zeros((T, H))
+    for t in (range(T) if tokens is None else tokens):
+        s = packed_sample_of(t, cu_seqlens)
+        p = t - int(cu_seqlens[s])
+        rows = packed_window_rows(t, cu_seqlens, window)
+        # the window buffer of the query is its own sample's rows, position 0 at row cu[s]
+        o, ms = sparse_attn(q[t][None, None], np.array([[p]]), np.asarray(kv, np.float64)[None],
+                            np.asarray(idx)[t][None, None], np.asarray(win, np.float64)[rows][None],
+                            [p - len(rows) + 1], window, sink, rope_dims=rope_dims, theta=theta,
+                            eps=eps, scale=scale, q_norm=q_norm)
+        out[t], mass[t] = o[0, 0], ms[0, 0]
+    return out, mass
+
+
 def grouped_out_proj(o, w1, w2):
     """Grouped output projection after the core attention ([DSA-to-CSA notes] section
     "Grouped output projection"): the n_h heads' outputs are split into g groups of n_h/g
@@ -418,4 +481,6 @@ __all__ = [
     "n_visible", "indexer_scores", "topk_indices", "index_topk_full", "block_max",
     "hier_candidates", "reindex_topk", "reindex_topk_masked", "reuse", "window_rows",
     "attend_one", "sparse_attn",
+    "packed_sample_of", "packed_visible_entries", "packed_window_rows", "index_topk_packed",
+    "sparse_attn_packed",
 ]

@@ -239,6 +239,18 @@ def out_proj_interleaved_groups():
     _set("grouped_out_proj", g)
 
 
+def packed_window_crosses_samples():
+    _set("packed_window_rows", lambda t, cu_seqlens, window: np.arange(max(0, int(t) - window + 1), int(t) + 1))
+
+
+def packed_visibility_stream_position():
+    def g(t, cu_seqlens, cu_entries, m):
+        s = _orig("packed_sample_of")(t, cu_seqlens)
+        n_s = int(cu_entries[s + 1]) - int(cu_entries[s])
+        return int(cu_entries[s]) + np.arange(_orig("n_visible")(int(t), n_s, m))  # t, not t - cu[s]
+    _set("packed_visible_entries", g)
+
+
 # ------------------------------------------------------------------ cache formats
 def fp4_ties_away_from_zero():
     import oracle.formats as F
@@ -279,6 +291,7 @@ MUTANTS = {f.__name__: f for f in [
     topk_ties_to_higher_index, topk_score_order, block_mean_not_max, hier_latest_not_forced,
     reindex_returns_slots, attn_drop_sink, attn_scale_one_over_c, attn_no_inverse_rotation,
     window_excludes_current_token, out_proj_interleaved_groups, fp4_ties_away_from_zero,
+    packed_window_crosses_samples, packed_visibility_stream_position,
     mxfp4_exponent_off_by_one, e4m3_bias_eight,
 ]}
 

@@ -77,7 +77,7 @@ FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails before any lau
 
 
 def test_version_and_errors(L):
-    assert L.csa2_version() == csa2.ABI_VERSION == 2
+    assert L.csa2_version() == csa2.ABI_VERSION == 3
     assert L.csa2_compress(None, None) == csa2.CSA2_ERR_INVALID
     assert "null" in csa2.last_error()
 

@@ -1,6 +1,8 @@
-"""GPU parity of the compressor over packed samples (csa2_compress with cu_seqlens): each
-sample compressed on its own inside one token stream, against the fp64 oracle; and the
-packed call against separate per-sample calls, byte for byte (entries, K_I, cache planes)."""
+"""GPU parity over packed samples (several samples in one token stream): the compressor
+(csa2_compress with cu_seqlens) compresses each sample on its own, against the fp64 oracle
+and against separate per-sample calls byte for byte; the indexer (ent_base) and the
+attention window (win_row0) of a token stay inside its own sample, against the oracle's
+packed index and attention."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +14,8 @@ from tests._gpu import assert_close, banner, bf16, f32, host, i32
 pytestmark = pytest.mark.gpu
 
 F32_TOL = dict(atol=1e-4, rtol=1e-4)
+BF16_TOL = dict(atol=2e-2, rtol=2e-2)
+W_ = W  # the module, where W names a window size below
 
 
 @pytest.fixture(scope="module")
@@ -79,3 +83,71 @@ def test_packed_equals_per_sample_calls(C):
         for name in p1:
             np.testing.assert_array_equal(host(planes[name])[0, row:row + k], host(p1[name])[0], err_msg=name)
         row += k
+
+
+# ------------------------------------------------------------------ index + attention over a packed stream
+def _packed_meta(lens, m):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu_e = np.concatenate([[0], np.cumsum([L // m for L in lens])]).astype(np.int32)
+    n = int(cu[-1])
+    sample = np.searchsorted(cu, np.arange(n), side="right") - 1
+    pos = (np.arange(n) - cu[sample]).astype(np.int32)
+    return cu, cu_e, sample, pos
+
+
+@pytest.mark.parametrize("case", ["bf16_mfma", "f32_generic"])
+def test_packed_stream_compress_index_attention(C, case):
+    # Six samples in one token stream (one shorter than m): the compressor writes each
+    # sample's entries (positions restarting), the per-token window rows likewise (m = 1);
+    # the indexer of a token scores only its sample's visible entries (ent_base), and its
+    # window holds only its sample's latest tokens (win_row0).  Indices bit-exact against the
+    # oracle's packed top-k; attention against the oracle's own entries and window rows.
+    bf = case == "bf16_mfma"
+    lens = [300, 1, 257, 130, 64, 181] if bf else [40, 1, 23, 17, 9, 30]
+    m = 2
+    c, H, HI, dI, k, W, r = (512, 64, 64, 128, 64, 128, 64) if bf else (64, 4, 4, 32, 8, 16, 16)
+    banner(f"packed stream {case}: samples {lens} m=2 c={c} H={H} k={k} window {W}")
+    g = W_.rng(5301 if bf else 5302)
+    cu, cu_e, sample, pos = _packed_meta(lens, m)
+    n, ne = int(cu[-1]), int(cu_e[-1])
+    dt = "bf16" if bf else "f32"
+    cin = W_.compress_inputs(g, n, c, m, dtype=dt, d_I=dI if bf else 0)
+    wsrc = g.normal((1, n, c), dtype=dt)
+    ind = W_.indexer_inputs(g, 1, n, 1, HI, dI, W_.WORKLOADS[4].w_values)
+    att = W_.attn_inputs(g, 1, n, 1, H, c, Lw=1, io_dtype=dt)
+    cast = bf16 if bf else f32
+    # compressor: entries per sample and the per-token window rows (m = 1), packed
+    ent, k_lib = C.csa2_compress(cast(cin["ca"]), cast(cin["za"]), m, rope_dims=r, cu_seqlens=i32(cu),
+                                 w_ik=cast(cin["w_ik"]) if bf else None)
+    win, _ = C.csa2_compress(cast(wsrc), cast(wsrc), 1, rope_dims=r, cu_seqlens=i32(cu))
+    e_ref, k_ref, cu_e_ref = O.compress_packed(cin["ca"][0], cin["za"][0], m, cu, rope_dims=r,
+                                               w_ik=cin["w_ik"].astype(np.float64) if bf else None)
+    w_ref, _, _ = O.compress_packed(wsrc[0], wsrc[0], 1, cu, rope_dims=r)
+    np.testing.assert_array_equal(cu_e_ref, cu_e)
+    tol = BF16_TOL if bf else F32_TOL
+    assert_close(host(ent)[0, :ne], e_ref, **tol, what="packed entries")
+    assert_close(host(win)[0], w_ref, **tol, what="packed window rows")
+    # indexer K: integers (bit-exact scores), from the oracle's projection when there is one
+    k_int = np.clip(np.rint(2.0 * k_ref), -3, 3) if bf else g.ints((ne, dI), -3, 3, dtype="f32").astype(np.float64)
+    qp = i32(pos[None])
+    ent_base = i32(cu_e[sample][None])
+    idx = C.csa2_index_topk(C.CSA2_MODE_FULL, qp, k, q_idx=bf16(ind["q_idx"]), w=f32(ind["w"]), m=m,
+                            k_idx=bf16(k_int[None].astype(np.float32)), ent_base=ent_base)
+    win_row0 = i32(cu[sample][None])
+    out = C.csa2_sparse_attn(cast(att["q"]), qp, idx, kv=ent[:, :ne].contiguous(), win=win, win_row0=win_row0,
+                             n_win=W, sink=f32(att["sink"]), rope_dims=r)
+    torch.cuda.synchronize()
+    i_ref = O.index_topk_packed(ind["q_idx"][0].astype(np.float64), ind["w"][0], k_int, cu, cu_e, m, k)
+    np.testing.assert_array_equal(host(idx)[0], i_ref)
+    # every selected id lies in the query's own sample
+    gi = host(idx)[0]
+    own_lo, own_hi = cu_e[sample][:, None], cu_e[sample + 1][:, None]
+    assert np.all((gi == -1) | ((gi >= own_lo) & (gi < own_hi)))
+    # attention: the tokens at and around every sample boundary and a random sample of the rest
+    rs = np.random.default_rng(3)
+    toks = sorted({int(t) for b in cu[:-1] for t in (b, b + 1, b + 2, b + 3) if t < n} |
+                  {int(t) for t in (cu[1:] - 1)} | set(rs.integers(0, n, 24 if bf else n).tolist()))
+    want, _ = O.sparse_attn_packed(att["q"][0], e_ref, i_ref, w_ref, cu, window=W, sink=att["sink"],
+                                   rope_dims=r, tokens=toks)
+    got = host(out)[0]
+    assert_close(got[toks], want[toks], **tol, what="packed attention")

@@ -615,3 +615,38 @@ def test_packed_compressor_positions_restart_per_sample():
     pos = np.array([0, 1, 2, 0, 1], np.float64)
     np.testing.assert_allclose(ent, np.stack([np.cos(pos), np.sin(pos)], axis=1), rtol=0, atol=1e-15)
     np.testing.assert_array_equal(cu_e, [0, 3, 5])
+
+
+def test_packed_index_and_window_masks_hand_example():
+    # a stream of three samples (5, 1 and 4 tokens), m = 2: the samples own entries [0, 2),
+    # none (one token is shorter than m) and [2, 4).  Worked by hand: token p of a sample sees
+    # the entries of its own sample whose block has ended (p >= 2(j+1)), and a 3-token window
+    # of its own sample.
+    cu, cu_e, m, W = [0, 5, 6, 10], [0, 2, 2, 4], 2, 3
+    want_entries = {0: [], 1: [], 2: [0], 3: [0], 4: [0, 1], 5: [], 6: [], 7: [], 8: [2], 9: [2]}
+    want_window = {0: [0], 1: [0, 1], 2: [0, 1, 2], 3: [1, 2, 3], 4: [2, 3, 4], 5: [5], 6: [6],
+                   7: [6, 7], 8: [6, 7, 8], 9: [7, 8, 9]}
+    for t in range(10):
+        assert list(O.packed_visible_entries(t, cu, cu_e, m)) == want_entries[t], t
+        assert list(O.packed_window_rows(t, cu, W)) == want_window[t], t
+    # the packed top-k keeps every visible entry (k = 4) and nothing of another sample: with
+    # scores equal to the entry id + 1 the order is plain, and entry 3 (not yet visible at
+    # token 9) must not appear
+    q_idx = np.ones((10, 1, 1))
+    k_idx = np.arange(1.0, 5.0)[:, None]
+    got = O.index_topk_packed(q_idx, np.ones((10, 1)), k_idx, cu, cu_e, m, 4)
+    for t in range(10):
+        e = want_entries[t]
+        assert list(got[t]) == e + [-1] * (4 - len(e)), t
+    # attention of token 8 (sample 3, position 2) over its entry 2 and window rows 6, 7, 8:
+    # without norm, rope or sink, a softmax over those four rows with scale 1
+    r = _rng(71)
+    q, kv, win = r.standard_normal((10, 1, 4)), r.standard_normal((4, 4)), r.standard_normal((10, 4))
+    idx = np.full((10, 4), -1)
+    idx[8, 0] = 2
+    out, mass = O.sparse_attn_packed(q, kv, idx, win, cu, window=W, rope_dims=0, q_norm=False, scale=1.0)
+    rows = np.stack([kv[2], win[6], win[7], win[8]])
+    p = softmax(rows @ q[8, 0])
+    np.testing.assert_allclose(out[8, 0], p @ rows, rtol=1e-13)
+    assert mass[8, 0] == pytest.approx(1.0)
+
