@@ -154,6 +154,19 @@ def test_index_full_decode_two_level(C):
     _check_full(C, d, q_pos, 1, 512, what="two-level")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("HI,dI", [(64, 64), (32, 128), (48, 32), (16, 64)])
+def test_index_full_decode_shapes(C, HI, dI, fmt):
+    banner(f"index FULL decode {fmt} K_I B=3 N=9000 H_I={HI} d_I={dI} k=256 (fused scan + chunk top-k)")
+    g = W.rng(40 + HI + dI + (fmt == "mxfp4"))
+    mx = fmt == "mxfp4"
+    d = W.indexer_inputs(g, 3, 1, 9000, HI, dI, W.WORKLOADS[5 if mx else 2].w_values,
+                         k_format="mxfp4" if mx else "bf16")
+    kd = F.mxfp4_decode(d["k_codes"], d["k_scales"]) if mx else None
+    q_pos = np.array([[9000], [8191], [300]], np.int32)  # full, ragged tail, mostly empty chunks
+    _check_full(C, d, q_pos, 1, 256, k_dense=kd, mx=mx, what=f"decode {fmt} {HI}x{dI}")
+
+
 def test_index_full_mxfp4(C):
     banner("index FULL MXFP4 K_I decode B=2 N=3000 k=128 and prefill T=64")
     g = W.rng(13)
