@@ -311,6 +311,39 @@ def attn_bytes(wl):
     return queries * (wl.k * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2 + wl.k * 4)
 
 
+def mxfp4_query_stage(torch, C, wl, d, idx_ref, reps=20):
+    """The Full layer's index call with q_I in MXFP4 as well (the indexer QK path in FP4 on
+    both sides, scaled FP4 x FP4 MFMA).  The step's integer q_I values are exact in E2M1 (scale
+    byte 127), so the call must return the step's own indices; its scan and merge are timed per
+    launch like the step's."""
+    q = d["q_idx"].float()
+    if not bool(((q == q.round()) & (q.abs() <= 3)).all()):
+        return {"skipped": "q_I is not exactly representable in E2M1"}
+    lut = torch.tensor([0, 2, 4, 5], dtype=torch.uint8, device=q.device)  # E2M1 codes of 0, 1, 2, 3
+    code = lut[q.abs().long()] | ((q < 0).to(torch.uint8) << 3)
+    codes = (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous()  # dim 2i in the low nibble
+    scales = torch.full((*q.shape[:-1], q.shape[-1] // 32), 127, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(idx_ref)
+    kw = dict(q_idx=codes, q_scales=scales, w=d["w"], m=wl.m, k_codes=d["k_codes"], k_scales=d["k_scales"],
+              out_idx=out)
+    ws = torch.empty(max(1, C.csa2_index_workspace_bytes(C.CSA2_MODE_FULL, d["q_pos"], wl.k, **kw)),
+                     dtype=torch.uint8, device=q.device)
+
+    def call(_i):
+        C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, workspace=ws, **kw)
+
+    call(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, idx_ref))
+    kern = per_kernel(C, torch, call, reps)
+    scan_ms = kern["index_scan_select"]["avg_ms"]
+    merge_ms = kern.get("topk_merge", {"avg_ms": 0.0})["avg_ms"]
+    sbytes = wl.B * wl.L * (wl.d_I // 2 + wl.d_I // 32) + wl.B * wl.H_I * (wl.d_I // 2 + wl.d_I // 32 + 4)
+    return {"what": "index FULL with MXFP4 q_I and K_I (scaled FP4 x FP4 MFMA)", "same_indices": same,
+            "scan_us": scan_ms * 1e3, "merge_us": merge_ms * 1e3, "algorithmic_bytes": sbytes,
+            "frac_hbm": sbytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def write_path_stage(torch, C, wl, d, reps=20):
     """The write path into the 4-bit decode cache (csa2_compress with FP4 entry planes and
     the MXFP4 indexer-K projection), timed with HIP events per launch.  Decode workloads
@@ -475,6 +508,10 @@ def main():
         roof["target"] = {"what": "decode sparse attention (all attention launches of the step), fraction of HBM "
                                   "peak", "frac": fa, "target_frac": 0.6, "met": fa >= 0.6,
                           "us_per_attention": attn_ms * 1e3 / n_attn}
+    if wl.kind == "decode_fp4":
+        runner.run(insts[0])
+        torch.cuda.synchronize()
+        stages["mxfp4_query"] = mxfp4_query_stage(torch, C, wl, insts[0], runner.idx.clone())
     if wl.kind not in ("hier", "hca_decode"):
         stages["write_path"] = write_path_stage(torch, C, wl, insts[0])
     if wl.kind != "hier":

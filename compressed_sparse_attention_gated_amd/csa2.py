@@ -38,7 +38,8 @@ class IndexDesc(C.Structure):
                 ("q_idx", _vp), ("w", _vp), ("q_pos", _vp), ("k_dtype", _i), ("k_idx", _vp),
                 ("k_codes", _vp), ("k_scales", _vp), ("cand", _vp), ("n_cand", _vp),
                 ("cand_stride", _i), ("src_idx", _vp), ("out_idx", _vp), ("out_block_max", _vp),
-                ("block", _i), ("out_scores", _vp), ("ent_base", _vp)]
+                ("block", _i), ("out_scores", _vp), ("ent_base", _vp), ("q_dtype", _i),
+                ("q_scales", _vp)]
 
 
 class HierDesc(C.Structure):
@@ -71,7 +72,7 @@ EXPORTS = ["csa2_compress", "csa2_index_workspace_bytes", "csa2_index_topk", "cs
 
 _lib = None
 # the descriptor layouts below are those of this version of include/csa2.h
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def lib():
@@ -242,14 +243,21 @@ def csa2_compress(ca, za, m, *, cb=None, zb=None, ba=None, bb=None, pos0=None, n
 # ---------------------------------------------------------------------------- index + top-k
 def _index_desc(q_idx, w, q_pos, k, m, *, k_idx=None, k_codes=None, k_scales=None, N=None,
                 cand=None, n_cand=None, src_idx=None, out_idx=None, out_block_max=None, block=8,
-                out_scores=None, ent_base=None):
+                out_scores=None, ent_base=None, q_scales=None):
     if not isinstance(q_pos, torch.Tensor) or q_pos.dim() != 2:
         raise ValueError("q_pos: a [B, T] int32 tensor is required")
     B, T = q_pos.shape
     dv = q_pos.device
     _arg("q_pos", q_pos, _I32, dv, (B, T))
-    _arg("q_idx", q_idx, (torch.bfloat16,), dv, (B, T, None, None))
-    H_I, d_I = (q_idx.shape[2], q_idx.shape[3]) if q_idx is not None else (1, 32)
+    if q_scales is None:
+        _arg("q_idx", q_idx, (torch.bfloat16,), dv, (B, T, None, None))
+        H_I, d_I = (q_idx.shape[2], q_idx.shape[3]) if q_idx is not None else (1, 32)
+    else:  # MXFP4 q_I: codes [B, T, H_I, d_I/2] and E8M0 scales [B, T, H_I, d_I/32]
+        _arg("q_idx", q_idx, _U8, dv, (B, T, None, None))
+        if q_idx is None:
+            raise ValueError("q_idx: the MXFP4 codes are required with q_scales")
+        H_I, d_I = q_idx.shape[2], 2 * q_idx.shape[3]
+        _arg("q_scales", q_scales, _U8, dv, (B, T, H_I, d_I // 32))
     _arg("w", w, _F32, dv, (B, T, H_I))
     if N is None:
         N = (k_idx.shape[1] if k_idx is not None else (k_codes.shape[1] if k_codes is not None else 0))
@@ -268,22 +276,26 @@ def _index_desc(q_idx, w, q_pos, k, m, *, k_idx=None, k_codes=None, k_scales=Non
                      k_idx=_p(k_idx), k_codes=_p(k_codes), k_scales=_p(k_scales), cand=_p(cand),
                      n_cand=_p(n_cand), cand_stride=cand.shape[-1] if cand is not None else 0,
                      src_idx=_p(src_idx), out_idx=_p(out_idx), out_block_max=_p(out_block_max),
-                     block=block, out_scores=_p(out_scores), ent_base=_p(ent_base))
+                     block=block, out_scores=_p(out_scores), ent_base=_p(ent_base),
+                     q_dtype=CSA2_MXFP4 if q_scales is not None else CSA2_BF16, q_scales=_p(q_scales))
 
 
 def csa2_index_topk(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_codes=None,
                     k_scales=None, N=None, cand=None, n_cand=None, src_idx=None, out_idx=None,
-                    out_block_max=None, block=8, out_scores=None, ent_base=None, workspace=None,
-                    stream=None):
+                    out_block_max=None, block=8, out_scores=None, ent_base=None, q_scales=None,
+                    workspace=None, stream=None):
     """FULL / REINDEX / REUSE.  Returns out_idx [B, T, k] int32.  ent_base [B, T] (FULL):
-    packed samples, the first entry id of each query's sample (q_pos is sample-local)."""
+    packed samples, the first entry id of each query's sample (q_pos is sample-local).
+    q_scales [B, T, H_I, d_I/32] uint8: q_idx holds MXFP4 codes [B, T, H_I, d_I/2] (with an
+    MXFP4 K_I)."""
     B, T = q_pos.shape
     dev = q_pos.device
     if out_idx is None:
         out_idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
     d = _index_desc(q_idx, w, q_pos, k, m, k_idx=k_idx, k_codes=k_codes, k_scales=k_scales, N=N,
                     cand=cand, n_cand=n_cand, src_idx=src_idx, out_idx=out_idx,
-                    out_block_max=out_block_max, block=block, out_scores=out_scores, ent_base=ent_base)
+                    out_block_max=out_block_max, block=block, out_scores=out_scores, ent_base=ent_base,
+                    q_scales=q_scales)
     nbytes = lib().csa2_index_workspace_bytes(C.byref(d), mode)
     if workspace is None or workspace.numel() < nbytes:
         workspace = _ws(nbytes, dev)
@@ -293,14 +305,16 @@ def csa2_index_topk(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_co
 
 def csa2_index_topk_noalloc(mode, q_pos, k, *, q_idx=None, w=None, m=1, k_idx=None, k_codes=None,
                             k_scales=None, N=None, cand=None, n_cand=None, src_idx=None, out_idx=None,
-                            out_block_max=None, block=8, out_scores=None, ent_base=None, stream=None):
+                            out_block_max=None, block=8, out_scores=None, ent_base=None, q_scales=None,
+                            stream=None):
     """csa2_index_topk with the library's static scratch instead of a workspace (for callers
     that cannot allocate).  out_idx must be given: nothing is allocated."""
     if out_idx is None:
         raise ValueError("out_idx is required: the no-allocation call allocates nothing")
     d = _index_desc(q_idx, w, q_pos, k, m, k_idx=k_idx, k_codes=k_codes, k_scales=k_scales, N=N,
                     cand=cand, n_cand=n_cand, src_idx=src_idx, out_idx=out_idx,
-                    out_block_max=out_block_max, block=block, out_scores=out_scores, ent_base=ent_base)
+                    out_block_max=out_block_max, block=block, out_scores=out_scores, ent_base=ent_base,
+                    q_scales=q_scales)
     _check(lib().csa2_index_topk_noalloc(C.byref(d), mode, _stream(stream)))
     return out_idx
 
@@ -310,7 +324,8 @@ def csa2_index_workspace_bytes(mode, q_pos, k, **kw):
                     k_codes=kw.get("k_codes"), k_scales=kw.get("k_scales"), N=kw.get("N"),
                     cand=kw.get("cand"), n_cand=kw.get("n_cand"), src_idx=kw.get("src_idx"),
                     out_idx=kw.get("out_idx"), out_block_max=kw.get("out_block_max"),
-                    block=kw.get("block", 8), out_scores=kw.get("out_scores"), ent_base=kw.get("ent_base"))
+                    block=kw.get("block", 8), out_scores=kw.get("out_scores"), ent_base=kw.get("ent_base"),
+                    q_scales=kw.get("q_scales"))
     return lib().csa2_index_workspace_bytes(C.byref(d), mode)
 
 

@@ -173,6 +173,9 @@ int csa2_compress(const csa2_compress_desc* d, void* stream) {
 }
 
 // --------------------------------------------------------------- index + top-k
+// q_dtype 0 (a zeroed field) reads as BF16
+static bool q_is_bf16(const csa2_index_desc* d) { return d->q_dtype == CSA2_BF16 || d->q_dtype == 0; }
+
 static int check_index(const csa2_index_desc* d, csa2_mode mode) {
   if (!d) return fail(CSA2_ERR_INVALID, "index: null descriptor");
   if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
@@ -190,8 +193,13 @@ static int check_index(const csa2_index_desc* d, csa2_mode mode) {
   if (d->N < 0 || d->m < 1) return fail(CSA2_ERR_INVALID, "index: need N >= 0, m >= 1");
   if (d->k_dtype != CSA2_BF16 && d->k_dtype != CSA2_MXFP4)
     return fail(CSA2_ERR_UNSUPPORTED, "index: K_I dtype must be BF16 or MXFP4");
+  if (!q_is_bf16(d) && d->q_dtype != CSA2_MXFP4)
+    return fail(CSA2_ERR_UNSUPPORTED, "index: q_I dtype must be BF16 or MXFP4");
+  if (d->q_dtype == CSA2_MXFP4 && d->k_dtype != CSA2_MXFP4)
+    return fail(CSA2_ERR_UNSUPPORTED, "index: an MXFP4 q_I needs an MXFP4 K_I");
   if (rows == 0) return CSA2_OK;
   if (!d->q_idx || !d->w || !d->q_pos || !d->out_idx) return fail(CSA2_ERR_INVALID, "index: q_idx, w, q_pos, out_idx are required");
+  if (d->q_dtype == CSA2_MXFP4 && !d->q_scales) return fail(CSA2_ERR_INVALID, "index: q_scales required for an MXFP4 q_I");
   if (d->N > 0) {
     if (d->k_dtype == CSA2_BF16 && !d->k_idx) return fail(CSA2_ERR_INVALID, "index: k_idx required for BF16 K_I");
     if (d->k_dtype == CSA2_MXFP4 && (!d->k_codes || !d->k_scales))
@@ -261,6 +269,7 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
     a.block = d->block > 0 ? d->block : 1;
     a.q_idx = d->q_idx; a.w = d->w; a.q_pos = d->q_pos; a.k_dtype = d->k_dtype; a.k_idx = d->k_idx;
     a.k_codes = d->k_codes; a.k_scales = d->k_scales;
+    a.q_scales = d->q_dtype == CSA2_MXFP4 ? d->q_scales : nullptr;
     a.scores = d->out_scores; a.row_stride = d->N;
     a.block_max = d->out_block_max;
     a.nblk = (d->N + a.block - 1) / a.block;
@@ -287,6 +296,7 @@ int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t w
     a.block = d->block > 0 ? d->block : 1;
     a.q_idx = d->q_idx; a.w = d->w; a.q_pos = d->q_pos; a.k_dtype = d->k_dtype; a.k_idx = d->k_idx;
     a.k_codes = d->k_codes; a.k_scales = d->k_scales;
+    a.q_scales = d->q_dtype == CSA2_MXFP4 ? d->q_scales : nullptr;
     a.cand = mode == CSA2_MODE_REINDEX ? d->cand : nullptr;
     a.n_cand = mode == CSA2_MODE_REINDEX ? d->n_cand : nullptr;
     a.cand_stride = d->cand_stride;

@@ -49,6 +49,7 @@ struct Dev {
   int64_t row_stride;
   float* block_max;
   const int32_t* ent_base;  // [rows] or null: packed samples, the query's first entry
+  const uint8_t* q_scales;  // MXFP4 q_I: E8M0 bytes [rows, H_I, d_I/32] (q_idx then holds the codes)
 };
 
 // Dimension order inside one 16-wide k-step.  For bf16 rows, lane half h holds dims
@@ -308,6 +309,93 @@ constexpr int kPipeDepth = KF == 1 ? 6 : 3;
 template <int KF>
 constexpr bool kSkewEpilogue = KF == 1;
 
+// ---------------------------------------------------------------- MXFP4 q_I x MXFP4 K_I
+// Both operands in MXFP4 go to v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 codes on both
+// sides: lane (n = l % 16, g = l / 16) supplies 32 codes (16 bytes, low nibble first) of row
+// n at dims 32g .. 32g + 31 and the E8M0 byte of that 32-dim group, which the instruction
+// applies to those values; the 16 x 16 result puts rows 4g + j of column n in lane (n, g).
+// One instruction covers 128 dims; for d_I < 128 the lanes of groups g >= d_I / 32 feed
+// zero codes.  Every product of two E2M1 values and two powers of two is exact, as with
+// the bf16 operands of the other scans.  A 32-entry tile is two sub-tiles of 16 entries
+// (A: q_I, 16 heads per block; B: K_I, 16 entries).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct RawF4 {
+  uint4 c[2];      // codes of entries tb + n and tb + 16 + n at this lane's 32 dims
+  uint32_t s[2];   // their E8M0 bytes
+};
+
+// lanes of groups past d_I load group d_I/32 - 1 (in bounds) and are zeroed in f4_tile
+template <int DI>
+__device__ __forceinline__ void load_raw_f4(const Dev& a, int b, int e0, int e1, int g, RawF4& r) {
+  const int gg = min(g, DI / 32 - 1);
+  const int ent[2] = {e0, e1};
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const size_t e = (size_t)b * a.N + ent[sub];
+    r.c[sub] = *reinterpret_cast<const uint4*>(a.k_codes + e * (DI / 2) + 16 * gg);
+    r.s[sub] = a.k_scales[e * (DI / 32) + gg];
+  }
+}
+
+template <int DI, int HB>
+__device__ __forceinline__ void load_query_f4(const Dev& a, int row, int lane, i32x8* areg, int* sreg,
+                                              float (*wreg)[4]) {
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t* qc = reinterpret_cast<const uint8_t*>(a.q_idx);
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 16 * hb + n;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    int sc = 127;
+    if (head < a.H_I && g < DI / 32) {
+      const size_t q = (size_t)row * a.H_I + head;
+      v = *reinterpret_cast<const uint4*>(qc + q * (DI / 2) + 16 * g);
+      sc = a.q_scales[q * (DI / 32) + g];
+    }
+    areg[hb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    sreg[hb] = sc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hr = 16 * hb + 4 * g + j;
+      wreg[hb][j] = hr < a.H_I ? a.w[(size_t)row * a.H_I + hr] : 0.f;
+    }
+  }
+}
+
+// the MFMAs of one 32-entry tile (two sub-tiles x HB head blocks)
+template <int DI, int HB>
+__device__ __forceinline__ void f4_mfma(const i32x8* areg, const int* sreg, const RawF4& r, int g, f32x4 (*acc)[HB]) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    uint4 c = r.c[sub];
+    if (DI < 128 && g >= DI / 32) c = make_uint4(0, 0, 0, 0);
+    const i32x8 bop = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      acc[sub][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(areg[hb], bop, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                                      0, sreg[hb], 0, (int)r.s[sub]);
+  }
+}
+// the tile's scores: lane l gets slot tb + l % 32 (lanes 16..31 of each half take the second
+// sub-tile); the four lane groups of an entry are summed by two lane swaps
+template <int HB>
+__device__ __forceinline__ float f4_epilogue(const f32x4 (*acc)[HB], const float (*wreg)[4], int lane) {
+  float x[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    float v = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v += wreg[hb][j] * relu_bits(acc[sub][hb][j]);
+    x[sub] = rows_sum(v);
+  }
+  return (lane & 16) ? x[1] : x[0];
+}
+// pipeline depth of the MXFP4 x MXFP4 scans (a raw tile is 10 registers)
+constexpr int kPipeDepthF4 = 6;
+
 // ---------------------------------------------------------------- private-B scan
 template <int DI, int KF, int MT, bool kCand, bool kBlockMax>
 __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
@@ -320,11 +408,6 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
   const int c1 = min(c0 + chunk, limit);
   if (c0 >= c1) return;
 
-  bf16x8 areg[MT][DI / 16];
-  float wreg[MT][16];
-  load_query<DI, KF, MT>(a, row, lane, areg, wreg);
-
-  const int h = lane / 32;
   const int eb = kCand ? 0 : entry_base(a, row);
   auto entry_of = [&](int slot) -> int {
     int s = min(slot, c1 - 1);
@@ -338,22 +421,47 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
   constexpr int kStride = 32 * kWaves;
   const int t0 = c0 + 32 * wave;
   if (t0 >= c1) return;
-  tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(
-      t0, c1, kStride,
-      [&](int tb, RawB<DI, KF>& raw) { load_raw<DI, KF>(a, b, entry_of(tb + lane % 32), h, raw); },
-      [&](const RawB<DI, KF>& raw, int tb) {
-        bf16x8 breg[DI / 16];
-        to_b<DI, KF>(raw, h, breg);
-        float s = tile_score<DI, MT>(areg, breg, wreg);
-        if constexpr (kCand) {
-          const int slot = tb + lane % 32;
-          if (slot < c1) {
-            const int e = a.cand[(size_t)row * a.cand_stride + slot];
-            if (e < 0 || e >= a.N) s = -INFINITY;
-          }
-        }
-        emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
-      });
+  auto cand_mask = [&](float s, int tb) {
+    if constexpr (kCand) {
+      const int slot = tb + lane % 32;
+      if (slot < c1) {
+        const int e = a.cand[(size_t)row * a.cand_stride + slot];
+        if (e < 0 || e >= a.N) s = -INFINITY;
+      }
+    }
+    return s;
+  };
+  if constexpr (KF == 2) {
+    constexpr int HB = 2 * MT;
+    i32x8 areg[HB];
+    int sreg[HB];
+    float wreg[HB][4];
+    load_query_f4<DI, HB>(a, row, lane, areg, sreg, wreg);
+    const int n16 = lane & 15, g16 = lane >> 4;
+    tile_pipeline<kPipeDepthF4, RawF4>(
+        t0, c1, kStride,
+        [&](int tb, RawF4& raw) { load_raw_f4<DI>(a, b, entry_of(tb + n16), entry_of(tb + 16 + n16), g16, raw); },
+        [&](const RawF4& raw, int tb) {
+          f32x4 acc[2][HB];
+          f4_mfma<DI, HB>(areg, sreg, raw, g16, acc);
+          const float s = cand_mask(f4_epilogue<HB>(acc, wreg, lane), tb);
+          emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
+        });
+  } else {
+    bf16x8 areg[MT][DI / 16];
+    float wreg[MT][16];
+    load_query<DI, KF, MT>(a, row, lane, areg, wreg);
+    const int h = lane / 32;
+    tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(
+        t0, c1, kStride,
+        [&](int tb, RawB<DI, KF>& raw) { load_raw<DI, KF>(a, b, entry_of(tb + lane % 32), h, raw); },
+        [&](const RawB<DI, KF>& raw, int tb) {
+          bf16x8 breg[DI / 16];
+          to_b<DI, KF>(raw, h, breg);
+          const float s = cand_mask(tile_score<DI, MT>(areg, breg, wreg), tb);
+          emit<kBlockMax>(a, row, lane, tb + lane % 32, c1, s);
+        });
+  }
 }
 
 // ---------------------------------------------------------------- fused scan + chunk top-k
@@ -389,52 +497,80 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
     if (threadIdx.x == 0) *ob = make_uint2(0u, 0u);
     return;
   }
-  bf16x8 areg[MT][DI / 16];
-  float wreg[MT][16];
-  load_query<DI, KF, MT>(a, row, lane, areg, wreg);
-  const int h = lane / 32;
   constexpr int kStride = 32 * kWaves;
   const int t0 = c0 + 32 * wave;
+  // The key store needs no branch: tiles start at multiples of 32 from c0 and the chunk is a
+  // multiple of 32 entries, so every slot of a tile lies inside the chunk's key array, and
+  // keys past the visible end are never read.  With the skewed epilogue, tile t's epilogue
+  // runs after tile t+1's MFMAs are issued; before the first tile the pending epilogue is a
+  // zero tile at t0, which that tile's own epilogue overwrites.
+  auto finish = [&](float s, int tb) {  // s: the score of slot tb + lane % 32
+    const int slot = tb + lane % 32;
+    skeys[slot - c0] = float_key(s);
+    if constexpr (kScores) {
+      if (lane < 32 && slot < c1) a.scores[(size_t)row * a.row_stride + slot] = s;
+    }
+    if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, c1, s);
+  };
   if (t0 < c1) {
-    // The key store needs no branch: tiles start at multiples of 32 from c0 and the chunk
-    // is a multiple of 32 entries, so every slot of a tile lies inside the chunk's key
-    // array, and keys past the visible end are never read.  With the skewed epilogue,
-    // tile t's epilogue runs after tile t+1's MFMAs are issued; before the first tile the
-    // pending epilogue is a zero tile at t0, which that tile's own epilogue overwrites.
-    f32x16 pacc[MT];
+    if constexpr (KF == 2) {
+      constexpr int HB = 2 * MT;
+      i32x8 areg[HB];
+      int sreg[HB];
+      float wreg[HB][4];
+      load_query_f4<DI, HB>(a, row, lane, areg, sreg, wreg);
+      const int n16 = lane & 15, g16 = lane >> 4;
+      f32x4 pacc[2][HB];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) pacc[mt] = f32x16{};
-    int ptb = t0;
-    auto finish = [&](const f32x16* acc, int tb) {
-      const float s = epi1<MT>(acc, wreg);
-      const int slot = tb + lane % 32;
-      skeys[slot - c0] = float_key(s);
-      if constexpr (kScores) {
-        if (lane < 32 && slot < c1) a.scores[(size_t)row * a.row_stride + slot] = s;
-      }
-      if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, c1, s);
-    };
-    auto load = [&](int tb, RawB<DI, KF>& raw) { load_raw<DI, KF>(a, b, min(tb + lane % 32, c1 - 1), h, raw); };
-    if constexpr (kSkewEpilogue<KF>) {
-      tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(t0, c1, kStride, load, [&](const RawB<DI, KF>& raw, int tb) {
-        bf16x8 breg[DI / 16];
-        to_b<DI, KF>(raw, h, breg);
-        f32x16 cacc[MT];
-        mfma1<DI, MT>(areg, breg, cacc);
-        finish(pacc, ptb);
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) pacc[mt] = cacc[mt];
+        for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      int ptb = t0;
+      auto load = [&](int tb, RawF4& raw) {
+        load_raw_f4<DI>(a, b, min(tb + n16, c1 - 1), min(tb + 16 + n16, c1 - 1), g16, raw);
+      };
+      tile_pipeline<kPipeDepthF4, RawF4>(t0, c1, kStride, load, [&](const RawF4& raw, int tb) {
+        f32x4 cacc[2][HB];
+        f4_mfma<DI, HB>(areg, sreg, raw, g16, cacc);
+        finish(f4_epilogue<HB>(pacc, wreg, lane), ptb);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = cacc[sub][hb];
         ptb = tb;
       });
-      finish(pacc, ptb);
+      finish(f4_epilogue<HB>(pacc, wreg, lane), ptb);
     } else {
-      tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(t0, c1, kStride, load, [&](const RawB<DI, KF>& raw, int tb) {
-        bf16x8 breg[DI / 16];
-        to_b<DI, KF>(raw, h, breg);
-        f32x16 acc[MT];
-        mfma1<DI, MT>(areg, breg, acc);
-        finish(acc, tb);
-      });
+      bf16x8 areg[MT][DI / 16];
+      float wreg[MT][16];
+      load_query<DI, KF, MT>(a, row, lane, areg, wreg);
+      const int h = lane / 32;
+      auto load = [&](int tb, RawB<DI, KF>& raw) { load_raw<DI, KF>(a, b, min(tb + lane % 32, c1 - 1), h, raw); };
+      if constexpr (kSkewEpilogue<KF>) {
+        f32x16 pacc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) pacc[mt] = f32x16{};
+        int ptb = t0;
+        tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(t0, c1, kStride, load, [&](const RawB<DI, KF>& raw, int tb) {
+          bf16x8 breg[DI / 16];
+          to_b<DI, KF>(raw, h, breg);
+          f32x16 cacc[MT];
+          mfma1<DI, MT>(areg, breg, cacc);
+          finish(epi1<MT>(pacc, wreg), ptb);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) pacc[mt] = cacc[mt];
+          ptb = tb;
+        });
+        finish(epi1<MT>(pacc, wreg), ptb);
+      } else {
+        tile_pipeline<kPipeDepth<KF>, RawB<DI, KF>>(t0, c1, kStride, load, [&](const RawB<DI, KF>& raw, int tb) {
+          bf16x8 breg[DI / 16];
+          to_b<DI, KF>(raw, h, breg);
+          f32x16 acc[MT];
+          mfma1<DI, MT>(areg, breg, acc);
+          finish(epi1<MT>(acc, wreg), tb);
+        });
+      }
     }
   }
   __syncthreads();
@@ -634,8 +770,8 @@ hipError_t launch3(const ScanArgs& s, const Dev& d, hipStream_t st) {
   const bool cand = s.cand != nullptr;
   const bool bm = s.block_max != nullptr;
   // the shared-tile prefill scan gives 8 consecutive queries one entry range: packed
-  // samples (a range per query) take the private scan
-  if (!cand && s.T >= kShWaves && !s.ent_base) {
+  // samples (a range per query) take the private scan, as do MXFP4 queries
+  if constexpr (KF != 2) if (!cand && s.T >= kShWaves && !s.ent_base) {
     dim3 grid(((s.T + kShWaves - 1) / kShWaves) * s.B);
     if (bm) hipLaunchKernelGGL((scan_shared<DI, KF, MT, true>), grid, dim3(kShThreads), 0, st, d);
     else hipLaunchKernelGGL((scan_shared<DI, KF, MT, false>), grid, dim3(kShThreads), 0, st, d);
@@ -663,7 +799,8 @@ hipError_t launch2(const ScanArgs& s, const Dev& d, hipStream_t st) {
 
 template <int DI>
 hipError_t launch1(const ScanArgs& s, const Dev& d, hipStream_t st) {
-  return s.k_dtype == CSA2_MXFP4 ? launch2<DI, 1>(s, d, st) : launch2<DI, 0>(s, d, st);
+  if (s.k_dtype != CSA2_MXFP4) return launch2<DI, 0>(s, d, st);
+  return s.q_scales ? launch2<DI, 2>(s, d, st) : launch2<DI, 1>(s, d, st);
 }
 
 template <int DI, int KF, int MT, int kRows>
@@ -706,6 +843,7 @@ Dev make_dev(const ScanArgs& s) {
   d.cand = s.cand; d.n_cand = s.n_cand; d.scores = s.scores; d.row_stride = s.row_stride;
   d.block_max = s.block_max;
   d.ent_base = s.ent_base;
+  d.q_scales = s.q_scales;
   return d;
 }
 
@@ -738,11 +876,17 @@ hipError_t launch_index_scan_select(const ScanArgs& s, int k, int chunk, int nch
     return s.H_I <= 32 ? launch_sel3<DI, KF, 1>(s, d, k, chunk, nchunks, keys, slots, bounds, st)
                        : launch_sel3<DI, KF, 2>(s, d, k, chunk, nchunks, keys, slots, bounds, st);
   };
-  const bool mx = s.k_dtype == CSA2_MXFP4;
+  // KF: 0 bf16 K_I; 1 MXFP4 K_I with bf16 q_I; 2 MXFP4 K_I and q_I
+  const int kf = s.k_dtype != CSA2_MXFP4 ? 0 : (s.q_scales ? 2 : 1);
+  auto by_kf = [&](auto di) -> hipError_t {
+    if (kf == 0) return go(di, std::integral_constant<int, 0>{});
+    if (kf == 1) return go(di, std::integral_constant<int, 1>{});
+    return go(di, std::integral_constant<int, 2>{});
+  };
   switch (s.d_I) {
-    case 32: return mx ? go(std::integral_constant<int, 32>{}, std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 32>{}, std::integral_constant<int, 0>{});
-    case 64: return mx ? go(std::integral_constant<int, 64>{}, std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 64>{}, std::integral_constant<int, 0>{});
-    case 128: return mx ? go(std::integral_constant<int, 128>{}, std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 128>{}, std::integral_constant<int, 0>{});
+    case 32: return by_kf(std::integral_constant<int, 32>{});
+    case 64: return by_kf(std::integral_constant<int, 64>{});
+    case 128: return by_kf(std::integral_constant<int, 128>{});
   }
   return hipErrorInvalidValue;
 }

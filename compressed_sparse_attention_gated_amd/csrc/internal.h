@@ -40,6 +40,7 @@ struct ScanArgs {
   float* block_max;       // [B*T, nblk] or null (FULL only)
   int nblk;
   const int32_t* ent_base;  // [B*T] or null: a query's entries start at this id (packed samples)
+  const uint8_t* q_scales;  // non-null: q_I in MXFP4 (q_idx holds the codes), with an MXFP4 K_I
 };
 hipError_t launch_index_scan(const ScanArgs& a, hipStream_t s);
 

@@ -184,12 +184,18 @@ def compress_inputs(g, n, c, m, *, overlap=False, dtype="bf16", bias_std=0.0,
     return d
 
 
-def indexer_inputs(g, B, T, N, H_I, d_I, w_values, *, k_format="bf16", lo=-3, hi=3):
-    """q_I ints U{lo..hi} [B, T, H_I, d_I] (bf16), w from w_values [B, T, H_I] (f32),
-    K_I ints U{lo..hi} [B, N, d_I] (bf16), or MXFP4 planes: codes [B, N, d_I/2]
-    uniform random bytes, scales [B, N, d_I/32] in {126, 127}."""
-    d = {"q_idx": g.ints((B, T, H_I, d_I), lo, hi, dtype="bf16"),
-         "w": g.choice((B, T, H_I), w_values, dtype="f32")}
+def indexer_inputs(g, B, T, N, H_I, d_I, w_values, *, k_format="bf16", q_format="bf16", lo=-3, hi=3):
+    """q_I ints U{lo..hi} [B, T, H_I, d_I] (bf16), or with q_format "mxfp4" the planes
+    q_codes [B, T, H_I, d_I/2] (uniform random bytes) and q_scales [B, T, H_I, d_I/32] in
+    {126, 127}; w from w_values [B, T, H_I] (f32); K_I ints U{lo..hi} [B, N, d_I] (bf16),
+    or MXFP4 planes: codes [B, N, d_I/2] uniform random bytes, scales [B, N, d_I/32] in
+    {126, 127}."""
+    if q_format == "bf16":
+        d = {"q_idx": g.ints((B, T, H_I, d_I), lo, hi, dtype="bf16")}
+    else:
+        d = {"q_codes": g.bytes((B, T, H_I, d_I // 2)),
+             "q_scales": g.byte_choice((B, T, H_I, d_I // 32), MX_SCALE_BYTES)}
+    d["w"] = g.choice((B, T, H_I), w_values, dtype="f32")
     if k_format == "bf16":
         d["k_idx"] = g.ints((B, N, d_I), lo, hi, dtype="bf16")
     else:

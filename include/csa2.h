@@ -31,8 +31,9 @@
 extern "C" {
 #endif
 
-#define CSA2_VERSION 3 /* 2: write-path, packed-sample, dense-attention and projection fields;
-                          3: per-query sample bounds of index and attention over packed streams */
+#define CSA2_VERSION 4 /* 2: write-path, packed-sample, dense-attention and projection fields;
+                          3: per-query sample bounds of index and attention over packed streams;
+                          4: MXFP4 indexer queries (q_dtype, q_scales) */
 #define CSA2_MAX_PACKED_SAMPLES 4096
 
 #if defined(__GNUC__) || defined(__clang__)
@@ -186,6 +187,14 @@ CSA2_API int csa2_compress(const csa2_compress_desc *d, void *stream);
  *     floor(q_pos/m)): no entry of another sample ([DSA-to-CSA notes], checklist "怎样验证":
  *     the indexer mask must not cross a sample boundary).  out_idx holds stream entry ids;
  *     out_scores / out_block_max are indexed by the sample-local slot.
+ *   q_dtype: CSA2_BF16 (a zeroed field, 0, reads the same) for the q_idx layout above, or
+ *     CSA2_MXFP4 with an MXFP4 K_I: q_idx then holds E2M1 codes [B, T, H_I, d_I/2] (dim 2i
+ *     in the low nibble of byte i) and q_scales E8M0 bytes [B, T, H_I, d_I/32], the indexer
+ *     QK path in FP4 on both sides ([DSA-to-CSA notes], "Lightning Indexer" and "数值与
+ *     kernel": the indexer QK path is quantised to FP4).  Scores are the fp32 sums of the
+ *     exact products of the decoded values, as with a bf16 q_I.  Other values of q_dtype,
+ *     or MXFP4 with a BF16 K_I, fail with CSA2_ERR_UNSUPPORTED; a missing q_scales with
+ *     CSA2_ERR_INVALID.
  * Supported: H_I <= 64 (heads beyond H_I are zero-padded internally), d_I in {32, 64, 128},
  *   block in {1, 2, 4, 8, 16, 32}, k <= 4096.
  */
@@ -205,6 +214,8 @@ typedef struct {
   int block;
   float *out_scores;
   const int32_t *ent_base;
+  csa2_dtype q_dtype;
+  const uint8_t *q_scales;
 } csa2_index_desc;
 
 CSA2_API size_t csa2_index_workspace_bytes(const csa2_index_desc *d, csa2_mode mode);

@@ -77,7 +77,7 @@ FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails before any lau
 
 
 def test_version_and_errors(L):
-    assert L.csa2_version() == csa2.ABI_VERSION == 3
+    assert L.csa2_version() == csa2.ABI_VERSION == 4
     assert L.csa2_compress(None, None) == csa2.CSA2_ERR_INVALID
     assert "null" in csa2.last_error()
 
@@ -135,6 +135,11 @@ def test_index_validation(L):
         (dict(), R, csa2.CSA2_ERR_INVALID),  # REINDEX without candidates
         (dict(src_idx=None), U, csa2.CSA2_ERR_INVALID),
         (dict(m=0), F, csa2.CSA2_ERR_INVALID),
+        # MXFP4 q_I: only with an MXFP4 K_I, and its scales are required
+        (dict(q_dtype=csa2.CSA2_MXFP4, q_scales=FAKE), F, csa2.CSA2_ERR_UNSUPPORTED),
+        (dict(q_dtype=csa2.CSA2_MXFP4, k_dtype=csa2.CSA2_MXFP4, k_idx=None, k_codes=FAKE, k_scales=FAKE), F,
+         csa2.CSA2_ERR_INVALID),
+        (dict(q_dtype=csa2.CSA2_FP4_E4M3), F, csa2.CSA2_ERR_UNSUPPORTED),
     ]
     for over, mode, code in cases:
         d = _index(**over)

@@ -21,7 +21,7 @@ import oracle as O
 from oracle import formats as F
 from compressed_sparse_attention_gated_amd import workloads as W
 from compressed_sparse_attention_gated_amd.steps import DecodeStep, HcaDecodeStep, HierStep, PrefillStep
-from tests._gpu import assert_close, banner, dev, f32, host, i32, oracle_quantised_cache
+from tests._gpu import assert_close, banner, dev, f32, host, i32, oracle_quantised_cache, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -153,6 +153,25 @@ def test_full_decode_fp4_random_codes(C):
     wl = W.WORKLOADS[5]
     banner("full FP4 decode: B=64 L=262144 random code bytes, 3 queries checked")
     _check_decode(C, wl, 3025, [1, 32, 62])
+
+
+def test_full_index_fp4_query_b64_l262144(C):
+    # the indexer QK path in FP4 on both sides: MXFP4 q_I (random code bytes) against the
+    # FP4 workload's MXFP4 K_I, through the fused scan at full size
+    wl = W.WORKLOADS[5]
+    banner("full FP4 index: B=64 L=262144 MXFP4 q_I x MXFP4 K_I, 8 queries checked")
+    d = W.decode_inputs(wl, 3035)
+    q = W.indexer_inputs(W.rng(3036), wl.B, 1, 1, wl.H_I, wl.d_I, wl.w_values, k_format="mxfp4", q_format="mxfp4")
+    idx = C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=u8(q["q_codes"]), q_scales=u8(q["q_scales"]),
+                            w=f32(q["w"]), m=wl.m, k_codes=d["k_codes"], k_scales=d["k_scales"])
+    torch.cuda.synchronize()
+    gi = _np(idx)
+    qp = _np(d["q_pos"])
+    for b in [0, 9, 18, 27, 36, 45, 54, 63]:
+        kb = F.mxfp4_decode(_np(d["k_codes"][b]), _np(d["k_scales"][b]))
+        qb = F.mxfp4_decode(q["q_codes"][b, 0], q["q_scales"][b, 0])
+        s = O.indexer_scores(qb, q["w"][b, 0].astype(np.float64), kb, O.n_visible(int(qp[b, 0]), wl.L, wl.m))
+        np.testing.assert_array_equal(gi[b, 0], O.topk_indices(s, wl.k), err_msg=f"indices b={b}")
 
 
 # =================================================================== hierarchical group

@@ -97,6 +97,15 @@ def _oracle_scores(q_idx, w, k_idx, q_pos, m):
     return res
 
 
+def _q_args(d):
+    """The query arguments of a call and the oracle's dense q_I: bf16 q_I, or MXFP4 codes and
+    scales decoded by the oracle's own format decoder."""
+    if "q_codes" in d:
+        return (dict(q_idx=u8(d["q_codes"]), q_scales=u8(d["q_scales"])),
+                F.mxfp4_decode(d["q_codes"], d["q_scales"]))
+    return dict(q_idx=bf16(d["q_idx"])), d["q_idx"].astype(np.float64)
+
+
 def _check_full(C, d, q_pos, m, k, k_dense=None, mx=False, block=8, what=""):
     """Run FULL on the GPU and compare indices, scores and block maxima with the oracle."""
     B, T = q_pos.shape
@@ -105,11 +114,12 @@ def _check_full(C, d, q_pos, m, k, k_dense=None, mx=False, block=8, what=""):
     nblk = (N + block - 1) // block
     bmax = torch.full((B, T, nblk), float("nan"), device="cuda")
     kw = dict(k_codes=u8(d["k_codes"]), k_scales=u8(d["k_scales"])) if mx else dict(k_idx=bf16(d["k_idx"]))
-    idx = C.csa2_index_topk(C.CSA2_MODE_FULL, i32(q_pos), k, q_idx=bf16(d["q_idx"]), w=f32(d["w"]), m=m,
-                            out_scores=scores, out_block_max=bmax, block=block, **kw)
+    qa, qd = _q_args(d)
+    idx = C.csa2_index_topk(C.CSA2_MODE_FULL, i32(q_pos), k, w=f32(d["w"]), m=m,
+                            out_scores=scores, out_block_max=bmax, block=block, **qa, **kw)
     torch.cuda.synchronize()
     kd = k_dense if k_dense is not None else d["k_idx"].astype(np.float64)
-    ref = _oracle_scores(d["q_idx"].astype(np.float64), d["w"].astype(np.float64), kd, q_pos, m)
+    ref = _oracle_scores(qd, d["w"].astype(np.float64), kd, q_pos, m)
     gi, gs, gb = host(idx), host(scores), host(bmax)
     for r, s in enumerate(ref):
         b, t = divmod(r, T)
@@ -165,6 +175,47 @@ def test_index_full_decode_shapes(C, HI, dI, fmt):
     kd = F.mxfp4_decode(d["k_codes"], d["k_scales"]) if mx else None
     q_pos = np.array([[9000], [8191], [300]], np.int32)  # full, ragged tail, mostly empty chunks
     _check_full(C, d, q_pos, 1, 256, k_dense=kd, mx=mx, what=f"decode {fmt} {HI}x{dI}")
+
+
+@pytest.mark.parametrize("HI,dI", [(64, 128), (48, 64), (16, 32)])
+def test_index_mxfp4_query(C, HI, dI):
+    """FP4 on both sides of the indexer QK product (scaled FP4 x FP4 MFMA): fused decode
+    (N > 8192, ragged and mostly-empty rows), private decode, a 40-query prefill and REINDEX,
+    against the oracle's scores of the decoded q_I and K_I."""
+    banner(f"index MXFP4 q_I x MXFP4 K_I: H_I={HI} d_I={dI}")
+    g = W.rng(60 + HI + dI)
+    wv = W.WORKLOADS[5].w_values
+    d = W.indexer_inputs(g, 3, 1, 9000, HI, dI, wv, k_format="mxfp4", q_format="mxfp4")
+    kd = F.mxfp4_decode(d["k_codes"], d["k_scales"])
+    _check_full(C, d, np.array([[9000], [8191], [300]], np.int32), 1, 256, k_dense=kd, mx=True,
+                what=f"mxfp4 q fused {HI}x{dI}")
+    d = W.indexer_inputs(g, 2, 1, 3000, HI, dI, wv, k_format="mxfp4", q_format="mxfp4")
+    kd = F.mxfp4_decode(d["k_codes"], d["k_scales"])
+    _check_full(C, d, np.array([[3000], [1234]], np.int32), 1, 128, k_dense=kd, mx=True,
+                what=f"mxfp4 q private {HI}x{dI}")
+    d = W.indexer_inputs(g, 1, 40, 700, HI, dI, wv, k_format="mxfp4", q_format="mxfp4")
+    kd = F.mxfp4_decode(d["k_codes"], d["k_scales"])
+    _check_full(C, d, (np.arange(40, dtype=np.int32) * 35 + 7)[None], 2, 64, k_dense=kd, mx=True,
+                what=f"mxfp4 q prefill {HI}x{dI}")
+    # REINDEX: 300 sorted candidates of the visible entries per query
+    N, B = 5000, 2
+    d = W.indexer_inputs(g, B, 1, N, HI, dI, wv, k_format="mxfp4", q_format="mxfp4")
+    kd = F.mxfp4_decode(d["k_codes"], d["k_scales"])
+    q_pos = np.array([[N], [4000]], np.int32)
+    r = np.random.default_rng(HI + dI)
+    cands = [np.sort(r.choice(int(q_pos[b, 0]), 300, replace=False)) for b in range(B)]
+    cand = np.full((B, 1, 320), -1, np.int32)
+    for b in range(B):
+        cand[b, 0, :300] = cands[b]
+    qa, qd = _q_args(d)
+    idx = C.csa2_index_topk(C.CSA2_MODE_REINDEX, i32(q_pos), 64, w=f32(d["w"]), m=1,
+                            k_codes=u8(d["k_codes"]), k_scales=u8(d["k_scales"]), cand=i32(cand),
+                            n_cand=i32(np.full((B, 1), 300, np.int32)), **qa)
+    torch.cuda.synchronize()
+    gi = host(idx)
+    for b in range(B):
+        want = O.reindex_topk(qd[b, 0], d["w"][b, 0].astype(np.float64), kd[b], cands[b], 64)
+        np.testing.assert_array_equal(gi[b, 0], want, err_msg=f"reindex b={b}")
 
 
 def test_index_full_mxfp4(C):
