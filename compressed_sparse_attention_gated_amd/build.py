@@ -1,6 +1,6 @@
 """Build libcsa2.so (HIP kernels for gfx950 + the C-ABI host layer) in the package directory.
 
-    python -m compressed_sparse_attention_gated_amd.build [-v]
+    python -m compressed_sparse_attention_gated_amd.build [-v] [--sanitize]
 
 Every HIP translation unit is compiled with hipcc for gfx950 only; packed-fp32 VALU
 instructions are disabled at the code-generation level.
@@ -78,5 +78,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the host layer (api.cpp) for the
+# CPU checks of the C ABI: only host code is instrumented (every sanitizer flag goes to the
+# host pass alone); the kernels are the ordinary objects.  The library needs the ASan runtime
+# preloaded into the process that loads it (sanitizer_runtime()).
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libcsa2.so")
+SANITIZE_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
+SANITIZE_FLAGS = SANITIZE_HOST + ["-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_runtime() -> str | None:
+    """The clang ASan runtime of this toolchain (it also carries the UBSan handlers)."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    objs = [os.path.join(BUILD_DIR, s + ".o") for s in SOURCES if s != "api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    api_obj = os.path.join(SANITIZE_DIR, "api.cpp.o")
+    cmd = [hipcc(), "-x", "hip", *COMMON_FLAGS, *SANITIZE_FLAGS, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: api.cpp (sanitized)\n{r.stderr}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_HOST, "-shared-libsan", "-o", SANITIZE_LIB,
+           api_obj, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized)\n{r.stderr}")
+    return SANITIZE_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -13,7 +13,9 @@ import os
 import torch  # loaded first: libcsa2 then binds to the HIP runtime torch already loaded
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+# CSA2_LIBRARY names another build of the same library (the sanitized host-layer build of
+# the CPU checks); by default the in-tree build
+LIB_PATH = os.environ.get("CSA2_LIBRARY") or os.path.join(_PKG, "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID, CSA2_ERR_UNSUPPORTED, CSA2_ERR_HIP, CSA2_ERR_WORKSPACE = 0, -1, -2, -3, -4
 CSA2_F32, CSA2_BF16, CSA2_FP4_E4M3, CSA2_MXFP4 = 0, 1, 2, 3

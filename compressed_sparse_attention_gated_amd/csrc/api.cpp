@@ -66,17 +66,28 @@ namespace csa2 {
 void prof_begin(hipStream_t s, const char* name) {
   if (!g_prof_on) return;
   ProfRec r{name, take_event(), take_event(), s};
-  if (r.a) hipEventRecord(r.a, s);
+  if (r.a) (void)hipEventRecord(r.a, s);
   g_prof.push_back(r);
 }
 void prof_end(hipStream_t s) {
   if (!g_prof_on || g_prof.empty()) return;
   ProfRec& r = g_prof.back();
-  if (r.b) hipEventRecord(r.b, s);
+  if (r.b) (void)hipEventRecord(r.b, s);
 }
 }  // namespace csa2
 
 using namespace csa2;
+
+// The integer a caller stored in an enum-typed field or argument.  Reading such an object
+// as its enum type is undefined when the value is none of the enumerators, so every check
+// reads the raw integer first and rejects unknown values before the field is used.
+template <class E>
+static int raw(const E& f) {
+  static_assert(sizeof(E) == sizeof(int), "the C enums of the ABI are int-sized");
+  int v;
+  std::memcpy(&v, &f, sizeof v);
+  return v;
+}
 
 extern "C" {
 
@@ -119,7 +130,7 @@ static int check_compress(const csa2_compress_desc* d) {
   if (d->B < 0 || d->n < 0 || d->m < 1) return fail(CSA2_ERR_INVALID, "compress: need B >= 0, n >= 0, m >= 1");
   if (d->c < 8 || d->c > 512 || d->c % 8 != 0 || !pow2_upto(d->c / 8, 64))
     return fail(CSA2_ERR_UNSUPPORTED, "compress: c=%d unsupported (c/8 must be a power of two, 8 <= c <= 512)", d->c);
-  if (d->dtype != CSA2_F32 && d->dtype != CSA2_BF16)
+  if (raw(d->dtype) != CSA2_F32 && raw(d->dtype) != CSA2_BF16)
     return fail(CSA2_ERR_UNSUPPORTED, "compress: dtype must be F32 or BF16");
   if (d->overlap != 0 && d->overlap != 1) return fail(CSA2_ERR_INVALID, "compress: overlap must be 0 or 1");
   if (d->rope_dims < 0 || d->rope_dims > d->c || d->rope_dims % 2)
@@ -174,26 +185,27 @@ int csa2_compress(const csa2_compress_desc* d, void* stream) {
 
 // --------------------------------------------------------------- index + top-k
 // q_dtype 0 (a zeroed field) reads as BF16
-static bool q_is_bf16(const csa2_index_desc* d) { return d->q_dtype == CSA2_BF16 || d->q_dtype == 0; }
+static bool q_is_bf16(const csa2_index_desc* d) { return raw(d->q_dtype) == CSA2_BF16 || raw(d->q_dtype) == 0; }
 
-static int check_index(const csa2_index_desc* d, csa2_mode mode) {
+// md: the mode argument as the caller passed it (its raw integer)
+static int check_index(const csa2_index_desc* d, int md) {
   if (!d) return fail(CSA2_ERR_INVALID, "index: null descriptor");
-  if (mode != CSA2_MODE_FULL && mode != CSA2_MODE_REINDEX && mode != CSA2_MODE_REUSE)
-    return fail(CSA2_ERR_INVALID, "index: unknown mode %d", (int)mode);
+  if (md != CSA2_MODE_FULL && md != CSA2_MODE_REINDEX && md != CSA2_MODE_REUSE)
+    return fail(CSA2_ERR_INVALID, "index: unknown mode %d", md);
   if (d->B < 0 || d->T < 0) return fail(CSA2_ERR_INVALID, "index: need B, T >= 0");
   if (d->k < 1) return fail(CSA2_ERR_INVALID, "index: k must be >= 1");
   if (d->k > 4096) return fail(CSA2_ERR_UNSUPPORTED, "index: k > 4096");
   const long long rows = (long long)d->B * d->T;
-  if (mode == CSA2_MODE_REUSE) {
+  if (md == CSA2_MODE_REUSE) {
     if (rows && (!d->src_idx || !d->out_idx)) return fail(CSA2_ERR_INVALID, "index: REUSE needs src_idx and out_idx");
     return CSA2_OK;
   }
   if (d->H_I < 1 || d->H_I > 64) return fail(CSA2_ERR_UNSUPPORTED, "index: H_I must be in [1, 64]");
   if (d->d_I != 32 && d->d_I != 64 && d->d_I != 128) return fail(CSA2_ERR_UNSUPPORTED, "index: d_I must be 32, 64 or 128");
   if (d->N < 0 || d->m < 1) return fail(CSA2_ERR_INVALID, "index: need N >= 0, m >= 1");
-  if (d->k_dtype != CSA2_BF16 && d->k_dtype != CSA2_MXFP4)
+  if (raw(d->k_dtype) != CSA2_BF16 && raw(d->k_dtype) != CSA2_MXFP4)
     return fail(CSA2_ERR_UNSUPPORTED, "index: K_I dtype must be BF16 or MXFP4");
-  if (!q_is_bf16(d) && d->q_dtype != CSA2_MXFP4)
+  if (!q_is_bf16(d) && raw(d->q_dtype) != CSA2_MXFP4)
     return fail(CSA2_ERR_UNSUPPORTED, "index: q_I dtype must be BF16 or MXFP4");
   if (d->q_dtype == CSA2_MXFP4 && d->k_dtype != CSA2_MXFP4)
     return fail(CSA2_ERR_UNSUPPORTED, "index: an MXFP4 q_I needs an MXFP4 K_I");
@@ -205,11 +217,11 @@ static int check_index(const csa2_index_desc* d, csa2_mode mode) {
     if (d->k_dtype == CSA2_MXFP4 && (!d->k_codes || !d->k_scales))
       return fail(CSA2_ERR_INVALID, "index: k_codes and k_scales required for MXFP4 K_I");
   }
-  if (mode == CSA2_MODE_FULL && d->out_block_max && !pow2_upto(d->block, 32))
+  if (md == CSA2_MODE_FULL && d->out_block_max && !pow2_upto(d->block, 32))
     return fail(CSA2_ERR_UNSUPPORTED, "index: block must be a power of two <= 32");
-  if (d->ent_base && mode != CSA2_MODE_FULL)
+  if (d->ent_base && md != CSA2_MODE_FULL)
     return fail(CSA2_ERR_INVALID, "index: ent_base (packed samples) is for FULL mode only");
-  if (mode == CSA2_MODE_REINDEX) {
+  if (md == CSA2_MODE_REINDEX) {
     if (!d->cand || !d->n_cand || d->cand_stride < 1) return fail(CSA2_ERR_INVALID, "index: REINDEX needs cand, n_cand, cand_stride >= 1");
     if (d->N == 0) return fail(CSA2_ERR_INVALID, "index: REINDEX with N == 0");
   }
@@ -241,12 +253,12 @@ static size_t index_ws(const csa2_index_desc* d, csa2_mode mode) {
 }
 
 size_t csa2_index_workspace_bytes(const csa2_index_desc* d, csa2_mode mode) {
-  if (check_index(d, mode) != CSA2_OK) return 0;
+  if (check_index(d, raw(mode)) != CSA2_OK) return 0;
   return index_ws(d, mode);
 }
 
 int csa2_index_topk(const csa2_index_desc* d, csa2_mode mode, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_index(d, mode);
+  int rc = check_index(d, raw(mode));
   if (rc != CSA2_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   const long long rows = (long long)d->B * d->T;
@@ -352,7 +364,7 @@ hipError_t scratch_of_current_device(void** out) {
 }  // namespace
 
 extern "C" int csa2_index_topk_noalloc(const csa2_index_desc* d, csa2_mode mode, void* stream) {
-  int rc = check_index(d, mode);
+  int rc = check_index(d, raw(mode));
   if (rc != CSA2_OK) return rc;
   const size_t need = index_ws(d, mode);
   if (need > CSA2_NOALLOC_SCRATCH_BYTES)
@@ -421,7 +433,10 @@ static int check_attn(const csa2_attn_desc* d) {
   if (d->rope_dims < 0 || d->rope_dims > d->c || d->rope_dims % 2) return fail(CSA2_ERR_INVALID, "attn: rope_dims must be even and in [0, c]");
   if (d->rope_dims > 0 && !(d->rope_theta > 0.f)) return fail(CSA2_ERR_INVALID, "attn: rope_theta must be > 0");
   if (d->q_norm && !(d->eps >= 0.f)) return fail(CSA2_ERR_INVALID, "attn: eps must be >= 0");
-  if (d->q_dtype != CSA2_F32 && d->q_dtype != CSA2_BF16) return fail(CSA2_ERR_UNSUPPORTED, "attn: q dtype must be F32 or BF16");
+  if (raw(d->q_dtype) != CSA2_F32 && raw(d->q_dtype) != CSA2_BF16)
+    return fail(CSA2_ERR_UNSUPPORTED, "attn: q dtype must be F32 or BF16");
+  if (raw(d->kv_dtype) != CSA2_F32 && raw(d->kv_dtype) != CSA2_BF16 && raw(d->kv_dtype) != CSA2_FP4_E4M3)
+    return fail(CSA2_ERR_UNSUPPORTED, "attn: kv dtype must be F32, BF16 or FP4");
   if (d->kv_dtype != d->q_dtype && !(d->kv_dtype == CSA2_FP4_E4M3 && d->q_dtype == CSA2_BF16))
     return fail(CSA2_ERR_UNSUPPORTED, "attn: kv dtype must equal q dtype, or be FP4 with bf16 q");
   if (d->num_splits < 0) return fail(CSA2_ERR_INVALID, "attn: num_splits must be >= 0");
