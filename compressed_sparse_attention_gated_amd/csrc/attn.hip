@@ -785,7 +785,8 @@ void pick_splits(const csa2_attn_desc& d, int* splits, int* tps) {
   const int kMaxSplitTiles = kMaxSplitRows / kTile;
   const int n_tiles = (max_rows(d) + kTile - 1) / kTile;
   const int n_wg = d.H / kHW;  // workgroups per (query, split)
-  int s = d.num_splits > 0 ? d.num_splits : (256 + rows * n_wg - 1) / (rows * n_wg);
+  const int wgs = rows * n_wg;   // 0 for an empty call, which launches nothing
+  int s = d.num_splits > 0 ? d.num_splits : (wgs > 0 ? (256 + wgs - 1) / wgs : 1);
   if (s < 1) s = 1;
   if (s > n_tiles) s = n_tiles;
   const int min_s = (n_tiles + kMaxSplitTiles - 1) / kMaxSplitTiles;
@@ -834,6 +835,7 @@ AttnPlan plan_attn(const csa2_attn_desc& d) {
 }  // namespace
 
 size_t attn_workspace_bytes(const csa2_attn_desc& d0) {
+  if ((long long)d0.B * d0.T * d0.H == 0) return 0;
   const csa2_attn_desc d = effective(d0);
   const AttnPlan p = plan_attn(d);
   if (!mfma_ok(d) || p.splits <= 1) return 0;

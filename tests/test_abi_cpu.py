@@ -153,6 +153,9 @@ def test_index_validation(L):
     # REUSE needs no workspace; B*T == 0 is a no-op
     assert L.csa2_index_workspace_bytes(C.byref(_index(src_idx=FAKE)), U) == 0
     assert L.csa2_index_topk(C.byref(_index(B=0)), F, None, 0, None) == csa2.CSA2_OK
+    for over in (dict(B=0), dict(T=0), dict(B=0, N=70000), dict(T=0, N=0)):
+        for mode in (F, R):
+            assert L.csa2_index_workspace_bytes(C.byref(_index(**over)), mode) == 0, (over, mode)
     # decode rows (one query per sequence) fuse the chunk top-k into the scan: the
     # workspace holds chunk candidates, far less than a score row
     dec = L.csa2_index_workspace_bytes(C.byref(_index(N=70000)), F)
@@ -171,6 +174,10 @@ def test_hier_validation(L):
                        (dict(out_cand=None), csa2.CSA2_ERR_INVALID), (dict(m=0), csa2.CSA2_ERR_INVALID)]:
         d = csa2.HierDesc(**{**base, **over})
         assert L.csa2_hier_candidates(C.byref(d), FAKE, 1 << 30, None) == code, over
+    for over in (dict(B=0), dict(T=0)):  # empty calls: no workspace, nothing launched
+        d = csa2.HierDesc(**{**base, **over})
+        assert L.csa2_hier_workspace_bytes(C.byref(d)) == 0, over
+        assert L.csa2_hier_candidates(C.byref(d), None, 0, None) == csa2.CSA2_OK, over
     d = csa2.HierDesc(**base)
     need = L.csa2_hier_workspace_bytes(C.byref(d))
     assert need > 0
@@ -198,8 +205,12 @@ def test_attn_validation(L):
     for over, code in cases:
         d = csa2.AttnDesc(**{**base, **over})
         assert L.csa2_sparse_attn(C.byref(d), None, 0, None) == code, (over, csa2.last_error())
-    d = csa2.AttnDesc(**{**base, "B": 0})
-    assert L.csa2_sparse_attn(C.byref(d), None, 0, None) == csa2.CSA2_OK
+    # zero-sized calls size no workspace and launch nothing (B, T or H = 0; split choice
+    # must not divide by the empty workgroup count)
+    for over in (dict(B=0), dict(T=0), dict(H=0), dict(B=0, k=512), dict(T=0, num_splits=0)):
+        d = csa2.AttnDesc(**{**base, **over})
+        assert L.csa2_attn_workspace_bytes(C.byref(d)) == 0, over
+        assert L.csa2_sparse_attn(C.byref(d), None, 0, None) == csa2.CSA2_OK, over
     # a decode batch of 2 queries is split over several workgroups per query -> workspace
     d = csa2.AttnDesc(**{**base, "B": 2, "k": 512})
     need = L.csa2_attn_workspace_bytes(C.byref(d))
