@@ -232,10 +232,11 @@ constexpr int kFp4Per = kT * 16 / kThreadsM;    // FP4 16-byte code chunks per t
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// LDS row pitch: 1024 B of bf16 channels + 16 B of padding, so the 16 rows read by one
-// MFMA A operand (16 B each) fall in different banks, and every offset inside a tile is
-// a compile-time immediate.
-constexpr int kPitch = kRowBytes + 16;
+// LDS row pitch: 1024 B of bf16 channels + 32 B, a stride of 8 of the 64 banks per row, so
+// one transposing PV read (32 lanes: 8 rows x 32 B) covers the banks once.  Every offset
+// inside a tile is a compile-time immediate.  (16 B of padding keeps the S^T A-operand rows
+// apart instead, but leaves the PV reads two-way conflicted: 8-9 % slower on long rows.)
+constexpr int kPitch = kRowBytes + 32;
 constexpr int kMaxSplitRows = 1024;   // row slots per split (staged in LDS)
 // Softmax reference: each head fixes the max of its first valid tile as the reference m
 // and keeps it; the final normalisation divides by a sum taken with the same reference,
