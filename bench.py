@@ -37,6 +37,7 @@ import numpy as np
 METRIC = "decode queries/s + indexer scores/s at 64K-1M ctx; % of HBM / MFMA peak"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense FP4 (and FP6) MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -339,9 +340,11 @@ def mxfp4_query_stage(torch, C, wl, d, idx_ref, reps=20):
     scan_ms = kern["index_scan_select"]["avg_ms"]
     merge_ms = kern.get("topk_merge", {"avg_ms": 0.0})["avg_ms"]
     sbytes = wl.B * wl.L * (wl.d_I // 2 + wl.d_I // 32) + wl.B * wl.H_I * (wl.d_I // 2 + wl.d_I // 32 + 4)
+    flops = 2.0 * wl.H_I * wl.d_I * wl.B * wl.L
     return {"what": "index FULL with MXFP4 q_I and K_I (scaled FP4 x FP4 MFMA)", "same_indices": same,
             "scan_us": scan_ms * 1e3, "merge_us": merge_ms * 1e3, "algorithmic_bytes": sbytes,
-            "frac_hbm": sbytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "frac_hbm": sbytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "flops": flops,
+            "frac_fp4_mfma": flops / (scan_ms * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
 
 
 def write_path_stage(torch, C, wl, d, reps=20):
@@ -495,6 +498,11 @@ def main():
     attn_ms = sum(v["avg_ms"] * launches_per_step[k] for k, v in kern.items() if k.startswith("attn_"))
     n_attn = 5 if wl.kind == "hier" else 1
     ab = attn_bytes(wl) * n_attn
+    if wl.kind in ("decode", "decode_fp4", "hier"):
+        # the whole step against HBM: the Full layer's scan and every attention (top-k keeps
+        # its scores on chip; its index lists are counted with the attention)
+        stages["step_total"] = {"algorithmic_bytes": sb + ab, "ms_per_step": ms,
+                                "frac_hbm": (sb + ab) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     stages["attention_total"] = {"ms_per_step": attn_ms, "algorithmic_bytes": ab,
                                  "GB_per_s": ab / (attn_ms * 1e-3) / 1e9,
                                  "frac_hbm": ab / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
