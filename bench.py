@@ -312,23 +312,38 @@ def attn_bytes(wl):
     return queries * (wl.k * row_bytes + wl.window * wl.c * 2 + 2 * wl.H * wl.c * 2 + wl.k * 4)
 
 
-def mxfp4_query_stage(torch, C, wl, d, idx_ref, reps=20):
-    """The Full layer's index call with q_I in MXFP4 as well (the indexer QK path in FP4 on
-    both sides, scaled FP4 x FP4 MFMA).  The step's integer q_I values are exact in E2M1 (scale
-    byte 127), so the call must return the step's own indices; its scan and merge are timed per
-    launch like the step's."""
-    q = d["q_idx"].float()
-    if not bool(((q == q.round()) & (q.abs() <= 3)).all()):
-        return {"skipped": "q_I is not exactly representable in E2M1"}
-    lut = torch.tensor([0, 2, 4, 5], dtype=torch.uint8, device=q.device)  # E2M1 codes of 0, 1, 2, 3
-    code = lut[q.abs().long()] | ((q < 0).to(torch.uint8) << 3)
+def _mxfp4_exact(torch, x):
+    """Integer values in [-3, 3] as MXFP4 planes with scale byte 127 (exact: 0, 1, 2, 3 are
+    E2M1 codes 0, 2, 4, 5), or None if x holds anything else."""
+    x = x.float()
+    if not bool(((x == x.round()) & (x.abs() <= 3)).all()):
+        return None
+    lut = torch.tensor([0, 2, 4, 5], dtype=torch.uint8, device=x.device)
+    code = lut[x.abs().long()] | ((x < 0).to(torch.uint8) << 3)
     codes = (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous()  # dim 2i in the low nibble
-    scales = torch.full((*q.shape[:-1], q.shape[-1] // 32), 127, dtype=torch.uint8, device=q.device)
+    scales = torch.full((*x.shape[:-1], x.shape[-1] // 32), 127, dtype=torch.uint8, device=x.device)
+    return codes, scales
+
+
+def mxfp4_query_stage(torch, C, wl, d, idx_ref, reps=20, keys_too=False):
+    """The Full layer's index call with q_I in MXFP4 as well (the indexer QK path in FP4 on
+    both sides, scaled FP4 x FP4 MFMA); with keys_too the bf16 K_I is encoded as MXFP4 too.
+    The workloads' integer q_I and K_I values are exact in E2M1 (scale byte 127), so the call
+    must return the step's own indices; its scan and merge are timed per launch like the
+    step's."""
+    qe = _mxfp4_exact(torch, d["q_idx"])
+    if qe is None:
+        return {"skipped": "q_I is not exactly representable in E2M1"}
+    if keys_too:
+        ke = _mxfp4_exact(torch, d["k_idx"])
+        if ke is None:
+            return {"skipped": "K_I is not exactly representable in E2M1"}
+    else:
+        ke = (d["k_codes"], d["k_scales"])
     out = torch.empty_like(idx_ref)
-    kw = dict(q_idx=codes, q_scales=scales, w=d["w"], m=wl.m, k_codes=d["k_codes"], k_scales=d["k_scales"],
-              out_idx=out)
+    kw = dict(q_idx=qe[0], q_scales=qe[1], w=d["w"], m=wl.m, k_codes=ke[0], k_scales=ke[1], out_idx=out)
     ws = torch.empty(max(1, C.csa2_index_workspace_bytes(C.CSA2_MODE_FULL, d["q_pos"], wl.k, **kw)),
-                     dtype=torch.uint8, device=q.device)
+                     dtype=torch.uint8, device=out.device)
 
     def call(_i):
         C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, workspace=ws, **kw)
@@ -341,7 +356,9 @@ def mxfp4_query_stage(torch, C, wl, d, idx_ref, reps=20):
     merge_ms = kern.get("topk_merge", {"avg_ms": 0.0})["avg_ms"]
     sbytes = wl.B * wl.L * (wl.d_I // 2 + wl.d_I // 32) + wl.B * wl.H_I * (wl.d_I // 2 + wl.d_I // 32 + 4)
     flops = 2.0 * wl.H_I * wl.d_I * wl.B * wl.L
-    return {"what": "index FULL with MXFP4 q_I and K_I (scaled FP4 x FP4 MFMA)", "same_indices": same,
+    what = ("index FULL with the step's q_I and K_I stored as MXFP4 (exact for its integers; "
+            "scaled FP4 x FP4 MFMA)" if keys_too else "index FULL with MXFP4 q_I and K_I (scaled FP4 x FP4 MFMA)")
+    return {"what": what, "same_indices": same,
             "scan_us": scan_ms * 1e3, "merge_us": merge_ms * 1e3, "algorithmic_bytes": sbytes,
             "frac_hbm": sbytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "flops": flops,
             "frac_fp4_mfma": flops / (scan_ms * 1e-3) / 1e12 / FP4_MFMA_PEAK_TFLOPS}
@@ -516,10 +533,14 @@ def main():
         roof["target"] = {"what": "decode sparse attention (all attention launches of the step), fraction of HBM "
                                   "peak", "frac": fa, "target_frac": 0.6, "met": fa >= 0.6,
                           "us_per_attention": attn_ms * 1e3 / n_attn}
-    if wl.kind == "decode_fp4":
+    if wl.kind in ("decode", "decode_fp4"):
+        # FP4 on the indexer QK path where the inputs allow it: MXFP4 queries against the FP4
+        # cache's MXFP4 keys; for the bf16-key decode, its integer keys and queries as MXFP4
+        # (a context figure beside the step, which keeps its bf16 keys)
         runner.run(insts[0])
         torch.cuda.synchronize()
-        stages["mxfp4_query"] = mxfp4_query_stage(torch, C, wl, insts[0], runner.idx.clone())
+        name = "mxfp4_query" if wl.kind == "decode_fp4" else "mxfp4_indexer"
+        stages[name] = mxfp4_query_stage(torch, C, wl, insts[0], runner.idx.clone(), keys_too=wl.kind == "decode")
     if wl.kind not in ("hier", "hca_decode"):
         stages["write_path"] = write_path_stage(torch, C, wl, insts[0])
     if wl.kind != "hier":
