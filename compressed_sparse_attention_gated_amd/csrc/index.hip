@@ -325,7 +325,7 @@ struct RawF4 {
   uint32_t s[2];   // their E8M0 bytes
 };
 
-// lanes of groups past d_I load group d_I/32 - 1 (in bounds) and are zeroed in f4_tile
+// lanes of groups past d_I load group d_I/32 - 1 (in bounds) and are zeroed in f4_mfma
 template <int DI>
 __device__ __forceinline__ void load_raw_f4(const Dev& a, int b, int e0, int e1, int g, RawF4& r) {
   const int gg = min(g, DI / 32 - 1);
