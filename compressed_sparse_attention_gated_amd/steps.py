@@ -1,7 +1,12 @@
 """The libcsa2 call chains that make up one step of each workload.
 
 Nothing here computes: each class allocates its outputs and workspaces once, then
-`run(inputs)` enqueues the library calls of one step on the current stream.
+`run(inputs)` enqueues the library calls of one step on the current stream.  Calls that do
+not depend on each other go to a second stream of the same (default) priority and are joined
+back before the first call that reads their output, so the step ends on the current stream:
+the prefill's window rows beside its entries and index stage, the Full layer's attention
+beside the candidate pool and the Reindex scan, and the Reindex / Reuse attentions two at a
+time.
 
   DecodeStep   compress the new token into the window -> index FULL + top-k over every
                cached entry -> sparse attention (bf16 or FP4 main KV, bf16 or MXFP4 K_I).
@@ -23,6 +28,10 @@ from . import csa2 as C
 
 def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _side_stream(device):
+    return torch.cuda.Stream(device=device)  # default priority, like the current stream
 
 
 class DecodeStep:
@@ -48,7 +57,8 @@ class DecodeStep:
     def run(self, d):
         wl = self.wl
         win = d["win"]
-        # the new token's row (m = 1: RMSNorm + RoPE at position L) into the window's last slot
+        # the new token's row (m = 1: RMSNorm + RoPE at position L) into the window's last slot.
+        # (On a second stream beside the scan it gains nothing: the scan holds every CU.)
         C.csa2_compress(d["c_new"], d["z_new"], 1, pos0=d["q_pos"][:, 0], rope_dims=wl.rope_dims,
                         out=win[:, wl.window - 1:, :])
         C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"], w=d["w"], m=wl.m,
@@ -83,32 +93,42 @@ class HierStep:
                                                        rope_dims=wl.rope_dims, out=self.outs[0]), dev)
         self.ws_hier = _ws(C.csa2_hier_workspace_bytes(self.bmax, d["q_pos"], L, block=wl.block,
                                                        n_keep=wl.n_keep_blocks), dev)
+        # one attention workspace per stream: attentions on the two streams run at once
+        self.ws_attn_side = _ws(self.ws_attn.numel(), dev)
+        self.side = _side_stream(dev)
 
-    def _attn(self, d, layer, idx):
+    def _attn(self, d, layer, idx, side=False):
         e = d["layers"][layer]
         wl = self.wl
         C.csa2_sparse_attn(e["q"], d["q_pos"], idx, kv=d["kv"], win=e["win"], win_pos0=d["win_pos0"],
                            n_win=wl.window, sink=e["sink"], rope_dims=wl.rope_dims, out=self.outs[layer],
-                           workspace=self.ws_attn)
+                           workspace=self.ws_attn_side if side else self.ws_attn,
+                           stream=self.side if side else None)
 
     def run(self, d):
         wl = self.wl
         l0, l1 = d["layers"][0], d["layers"][1]
+        main = torch.cuda.current_stream()
         # Full layer: scan every entry, its own top-k, block maxima for the pool
         C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=l0["q_idx"], w=l0["w"], k_idx=d["k_idx"],
                           out_idx=self.idx_full, out_block_max=self.bmax, block=wl.block, workspace=self.ws_full)
-        self._attn(d, 0, self.idx_full)
+        # its attention on the second stream, beside the pool and the Reindex scan
+        self.side.wait_stream(main)
+        self._attn(d, 0, self.idx_full, side=True)
         # candidate pool from the block maxima
         C.csa2_hier_candidates(self.bmax, d["q_pos"], wl.L, block=wl.block, n_keep=wl.n_keep_blocks,
                                out_cand=self.cand, out_count=self.count, workspace=self.ws_hier)
         # Reindex layer: this layer's indexer over the candidates only
         C.csa2_index_topk(C.CSA2_MODE_REINDEX, d["q_pos"], wl.k, q_idx=l1["q_idx"], w=l1["w"], k_idx=d["k_idx"],
                           cand=self.cand, n_cand=self.count, out_idx=self.idx_re, workspace=self.ws_re)
-        self._attn(d, 1, self.idx_re)
-        # Reuse layers: the Reindex layer's indices, in place (no indexer work)
+        # Reuse layers: the Reindex layer's indices, in place (no indexer work, no launch)
         for layer in range(2, len(d["layers"])):
             C.csa2_index_topk(C.CSA2_MODE_REUSE, d["q_pos"], wl.k, src_idx=self.idx_re, out_idx=self.idx_re)
-            self._attn(d, layer, self.idx_re)
+        # the Reindex and Reuse attentions read the same indices: alternate the two streams
+        self.side.wait_stream(main)
+        for layer in range(1, len(d["layers"])):
+            self._attn(d, layer, self.idx_re, side=layer % 2 == 0)
+        main.wait_stream(self.side)
         return self.idx_full, self.cand, self.count, self.idx_re, self.outs
 
 
@@ -154,6 +174,7 @@ class PrefillStep:
                                                        win_pos0=self._wp0(dev), n_win=wl.window, sink=d["sink"],
                                                        rope_dims=wl.rope_dims, out=self.out), dev)
         self.wp0 = self._wp0(dev)
+        self.side = _side_stream(dev)
 
     @staticmethod
     def _wp0(dev):
@@ -162,13 +183,17 @@ class PrefillStep:
     def run(self, d, k_idx=None):
         """k_idx: the indexer K the index stage reads; default the compressor's projection."""
         wl = self.wl
+        main = torch.cuda.current_stream()
+        # window rows on the second stream: every token's own row (m = 1 keeps the row; RMSNorm
+        # + RoPE at its position); only the attention reads them
+        self.side.wait_stream(main)
+        C.csa2_compress(d["win_src"], d["win_src"], 1, rope_dims=wl.rope_dims, out=self.win, stream=self.side)
         C.csa2_compress(d["ca"], d["za"], wl.m, rope_dims=wl.rope_dims, out=self.entries, w_ik=d["w_ik"],
                         out_ik=self.k_index)
-        # window rows: every token's own row (m = 1 keeps the row; RMSNorm + RoPE at its position)
-        C.csa2_compress(d["win_src"], d["win_src"], 1, rope_dims=wl.rope_dims, out=self.win)
         C.csa2_index_topk(C.CSA2_MODE_FULL, d["q_pos"], wl.k, q_idx=d["q_idx"], w=d["w"], m=wl.m,
                           k_idx=self.k_index if k_idx is None else k_idx, out_idx=self.idx,
                           workspace=self.ws_index)
+        main.wait_stream(self.side)
         C.csa2_sparse_attn(d["q"], d["q_pos"], self.idx, kv=self.entries, win=self.win, win_pos0=self.wp0,
                            n_win=wl.window, sink=d["sink"], rope_dims=wl.rope_dims, out=self.out,
                            workspace=self.ws_attn)
