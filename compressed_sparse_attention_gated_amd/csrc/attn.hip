@@ -18,8 +18,8 @@
 //   in the A-operand order of P for the PV product.  For PV each wave owns 128 output
 //   channels of its half's 32 heads; the V operand (rows along K) is read with the gfx950
 //   LDS transpose read ds_read_b64_tr_b16 from the same row-major tile that fed S^T (shared
-//   K = V, one copy in LDS).  The row pitch is padded by 16 bytes so both read patterns
-//   avoid bank conflicts.  Softmax in fp32 with exp2 (scale folded into q_hat) against a
+//   K = V, one copy in LDS).  The row pitch is padded by 32 bytes, which keeps the
+//   transposing PV reads free of bank conflicts (see kPitch).  Softmax in fp32 with exp2 (scale folded into q_hat) against a
 //   fixed per-head reference (see kOverflow).  With several splits per query each split's
 //   output (normalised by its own sum, bf16) and (max, sum) go to a workspace in 32-head
 //   units and attn_combine merges them in a fixed order.

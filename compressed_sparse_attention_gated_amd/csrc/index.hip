@@ -12,7 +12,9 @@
 // epilogue plus one swap between the two half-waves.  The decode scans stage no K_I in
 // LDS: every K_I byte is read exactly once per query, straight into registers.  MXFP4 rows
 // (E2M1 codes + E8M0 scale per 32) are dequantised into the B registers by the hardware's
-// scaled FP4 convert (exact in bf16).
+// scaled FP4 convert (exact in bf16).  When the queries are MXFP4 as well, both operands'
+// codes and E8M0 scales go straight to the scaled FP4 MFMA v_mfma_scale_f32_16x16x128_f8f6f4
+// (16 heads x 128 dims x 16 entries per instruction; no convert).
 //
 // Three variants:
 //  * scan_select: decode FULL - workgroup (query, chunk of entries); the chunk's keys go to
