@@ -203,6 +203,16 @@ def test_full_hier_group_b8_l1m(C):
             o_ref, _ = _oracle_attn_query(_np(e["q"][b, 0]), L, rows, _np(e["win"][b]), L - W_ + 1, W_,
                                           _np(e["sink"]), wl.rope_dims)
             assert_close(g_outs[layer][b, 0], o_ref, **BF16_TOL, what=f"attention layer {layer} b={b}")
+    # the same step with its second stream folded into the current one: every output equal,
+    # bit for bit (the kernels are deterministic, so a race between the two streams would show)
+    step.side = torch.cuda.current_stream()
+    seq = step.run(d)
+    torch.cuda.synchronize()
+    for name, got, ref in (("Full indices", seq[0], g_full), ("candidates", seq[1], g_cand),
+                           ("counts", seq[2], g_cnt), ("Reindex indices", seq[3], g_re)):
+        np.testing.assert_array_equal(_np(got), ref, err_msg=f"{name}: two-stream and one-stream runs differ")
+    for layer, o in enumerate(seq[4]):
+        np.testing.assert_array_equal(_np(o), g_outs[layer], err_msg=f"attention layer {layer}: stream order")
 
 
 # =================================================================== HCA decode
@@ -242,7 +252,8 @@ def test_full_prefill_32k(C):
     # the index stage reads integer K_I derived from the oracle's projection, so that every
     # score is exact and the selection can be compared bit for bit
     k_int = np.clip(np.rint(2.0 * k_ref), -3, 3)
-    entries, k_index, win, idx, out = step.run(d, k_idx=dev(k_int[None].astype(np.float32), torch.bfloat16))
+    k_int_dev = dev(k_int[None].astype(np.float32), torch.bfloat16)
+    entries, k_index, win, idx, out = step.run(d, k_idx=k_int_dev)
     torch.cuda.synchronize()
     assert_close(_np(entries)[0], e_ref, **BF16_TOL, what="entries")
     assert_close(_np(k_index)[0], k_ref, **BF16_TOL, what="indexer K projection")
@@ -264,3 +275,11 @@ def test_full_prefill_32k(C):
         rows = e_ref[i_ref[i_ref >= 0]]
         o_ref, _ = _oracle_attn_query(qq[j], t, rows, w_ref, 0, wl.window, sink, wl.rope_dims)
         assert_close(go[j], o_ref, **BF16_TOL, what=f"attention t={t}")
+    # the same step with its second stream folded into the current one: every index and every
+    # output value equal (a race between the window-row stream and the scan would show)
+    first = [t.clone() for t in (entries, k_index, win, idx, out)]
+    step.side = torch.cuda.current_stream()
+    again = step.run(d, k_idx=k_int_dev)
+    torch.cuda.synchronize()
+    for name, a, b_ in zip(("entries", "indexer K", "window rows", "indices", "attention"), again, first):
+        assert torch.equal(a, b_), f"{name}: two-stream and one-stream runs differ"
