@@ -104,7 +104,9 @@ __host__ __device__ __forceinline__ size_t smem_keys_off(size_t smem_bytes) { re
 
 // single level: one workgroup per row
 template <int kT>
-__global__ void __launch_bounds__(kT) topk_single(Params p, int stage_cap, int defer) {
+// 512-thread rows: at most 80 VGPRs, so that three workgroups share a CU
+__global__ void __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(kT == 512 ? 6 : 1)))
+topk_single(Params p, int stage_cap, int defer) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   TopkSmem<kT>& sm = *reinterpret_cast<TopkSmem<kT>*>(smem_raw);
   uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + smem_keys_off(sizeof(TopkSmem<kT>)));

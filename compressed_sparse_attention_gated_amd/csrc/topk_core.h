@@ -2,13 +2,16 @@
 // keys of a row, ties to the lower index, reported in index order.
 //
 // Keys are order-preserving uint32 images of the scores (see float_key).  The threshold
-// T (the k-th largest key) is found by range-adaptive radix passes: the live key range
-// [lo, lo+span] starts as [min, max]; each pass histograms (key - lo) >> shift into at most
-// 2048 LDS bins (shift chosen from the span), keeps the bin holding the k-th largest key
-// and narrows the range to it, until the range is a single key.  Clustered scores (the
-// usual case once rows hold only candidates) therefore still spread over many bins, so
-// LDS atomics rarely collide.  A pass costs three barriers (the histograms are double
-// buffered).  The compaction counts the selected keys of every 256-key segment, scans the
+// T (the k-th largest key) is found in two steps.  A first pass histograms the keys into
+// 2048 LDS bins laid linearly over the scores between the smallest and the largest finite
+// one; the map is monotone (a key never lands below a smaller key's bin), so the bin that
+// holds the k-th largest key is exact.  That bin usually holds a few keys: they are
+// gathered in LDS and every wave ranks them directly.  A crowded bin (heavy ties, or
+// scores spread over many orders of magnitude) goes on with range-adaptive radix passes
+// over its own key range [lo, lo+span]: each histograms (key - lo) >> shift into at most
+// 2048 bins (shift chosen from the span), keeps the bin holding the k-th largest key and
+// narrows the range to it, until the range is a single key.  A pass costs three barriers
+// (the histograms are double buffered).  The compaction counts the selected keys of every 256-key segment, scans the
 // segment counts once across the block and then places each key at its rank in index
 // order: the output is ascending and ties resolve to the lower index.
 #pragma once
@@ -28,8 +31,59 @@ struct TopkSmem {
   uint32_t seg[kSegMax];        // per segment: (#keys > T) | (#keys == T) << 16, then their prefix
   uint32_t wsum[2][kW];
   uint32_t wlo[kW], whi[kW];
+  uint32_t wl2[kW];
   uint32_t sel_bin[2], krem[2];
   uint32_t bound_lo, bound_cnt;
+  uint32_t ncand;
+  uint32_t cand[64];  // the keys of the first pass's boundary bin, when it holds at most 64
+};
+
+// keys of finite scores lie strictly between float_key(-inf) and float_key(+inf)
+constexpr uint32_t kKeyNegInf = 0x007fffffu;
+constexpr uint32_t kKeyPosInf = 0xff800000u;
+constexpr uint32_t kCandMax = 64;
+
+// the score of a key (inverse of float_key)
+__device__ __forceinline__ float key_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Bins linear in the score: bin = (x - f0) * 2048 / (f1 - f0) for finite scores x in
+// [f0, f1], computed as one fused multiply-add and clamped to [0, 2047]; keys below every
+// finite score go to bin 0, keys above to bin 2047.  Each step is monotone (a correctly
+// rounded fma of a fixed positive slope, the clamps, truncation), so a larger key never
+// takes a lower bin, whatever the rounding.  Without two distinct finite scores (or with a
+// range too small for a finite slope) every finite key takes the middle bin.
+struct LinearBins {
+  float a = 0.f, c = 1024.f;
+  __device__ __forceinline__ void init(uint32_t flo, uint32_t fhi) {
+    if (flo < fhi) {
+      const float f0 = key_float(flo), f1 = key_float(fhi);
+      const float aa = 1024.f / (0.5f * f1 - 0.5f * f0);  // halves: no overflow of the range
+      const float cc = -f0 * aa;
+      if (__builtin_isfinite(aa) && __builtin_isfinite(cc)) {
+        a = aa;
+        c = cc;
+      }
+    }
+  }
+  // a key range that holds every key of bin t, and usually little else: the keys of the
+  // scores whose ideal bin value lies in [t - 1, t + 2) (each bin's keys are found exactly
+  // among them, and a count check catches a range that missed some)
+  __device__ __forceinline__ void key_range(uint32_t t, uint32_t* k_lo, uint32_t* k_hi) const {
+    *k_lo = t == 0 ? 0u : float_key(((float)t - 1.f - c) / a);
+    *k_hi = t >= kTopkBins - 1 ? 0xffffffffu : float_key(((float)t + 2.f - c) / a);
+    if (!(a > 0.f)) {  // every finite key in one bin
+      *k_lo = t == 0 ? 0u : kKeyNegInf;
+      *k_hi = t >= kTopkBins - 1 ? 0xffffffffu : kKeyPosInf;
+    }
+  }
+  // branch-free: -inf, the keys below it (negative NaNs) and any NaN product clamp to 0;
+  // +inf, the keys above it (positive NaNs, forced keys) are set to the last bin
+  __device__ __forceinline__ uint32_t operator()(uint32_t u) const {
+    const float v = fminf(fmaxf(__builtin_fmaf(key_float(u), a, c), 0.f), (float)(kTopkBins - 1));
+    return u >= kKeyPosInf ? (uint32_t)(kTopkBins - 1) : (uint32_t)v;
+  }
 };
 
 template <int kCtrl>
@@ -129,16 +183,19 @@ __device__ __forceinline__ void keys4(const Src& src, int i, int n, uint32_t (&k
 // Threshold T (the k-th largest key of src.key(0..n-1)) and how many keys equal to T are
 // taken.  Requires 1 <= k <= n.  Every thread of the block must call it.
 //
-// With k2 (1 <= k2 <= k) it also reports a cheap lower bound of the k2-th largest key: the
-// lower edge L2 of the first pass's bin that holds it, with g2 = the number of keys >= L2
-// (at least k2).  Chunked selection uses it to prune candidates before the merge.
+// With k2 (1 <= k2 <= k) it also reports a cheap estimate of the k2-th largest key: a key
+// L2 at the lower edge of the first pass's bin that holds it, with g2 = the exact number of
+// keys >= L2 (as a rule at least k2).  Chunked selection uses such pairs to prune candidates
+// before the merge; any pair with an exact count is safe there.
 template <int kT, class Src>
 __device__ __forceinline__ void radix_threshold(const Src& src, int n, int k, TopkSmem<kT>& sm, uint32_t* T_out,
                                 uint32_t* take_out, int k2 = 0, uint32_t* L2_out = nullptr,
                                 uint32_t* g2_out = nullptr) {
+  constexpr int kW = TopkSmem<kT>::kW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < kTopkBins; i += kT) sm.hist[0][i] = 0;
-  // live range [lo, lo + span]
+  if (threadIdx.x == 0) sm.ncand = 0;
+  // key range [lo, hi]
   uint32_t lo = 0xffffffffu, hi = 0u;
   for_keys<kT>(src, n, [&](uint32_t kk) {
     lo = min(lo, kk);
@@ -146,19 +203,179 @@ __device__ __forceinline__ void radix_threshold(const Src& src, int n, int k, To
   });
   lo = wave_umin(lo);
   hi = wave_umax(hi);
-  if (lane == 0) { sm.wlo[wave] = lo; sm.whi[wave] = hi; }
+  if (lane == 0) {
+    sm.wlo[wave] = lo;
+    sm.whi[wave] = hi;
+  }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < TopkSmem<kT>::kW; ++w) { lo = min(lo, sm.wlo[w]); hi = max(hi, sm.whi[w]); }
-  uint32_t span = hi - lo;
-  uint32_t krem = (uint32_t)k;
-  constexpr int kPer = kTopkBins / kT;
-  int cur = 0;
-  if (k2 > 0) {  // all keys equal: the bound is that key, held by every key
-    *L2_out = lo;
-    *g2_out = (uint32_t)n;
+  for (int w = 0; w < kW; ++w) {
+    lo = min(lo, sm.wlo[w]);
+    hi = max(hi, sm.whi[w]);
   }
-  bool first = true;
+  uint32_t krem = (uint32_t)k;
+  if (lo == hi) {  // all keys equal: the bound is that key, held by every key
+    if (k2 > 0) {
+      *L2_out = lo;
+      *g2_out = (uint32_t)n;
+    }
+    *T_out = lo;
+    *take_out = krem;
+    return;
+  }
+  // the range [flo, fhi] of the keys of finite scores (another pass only when some are not)
+  uint32_t flo = lo, fhi = hi;
+  if (lo <= kKeyNegInf || hi >= kKeyPosInf) {  // block-uniform
+    flo = 0xffffffffu;
+    fhi = 0u;
+    for_keys<kT>(src, n, [&](uint32_t kk) {
+      flo = min(flo, kk > kKeyNegInf ? kk : 0xffffffffu);
+      fhi = max(fhi, kk < kKeyPosInf ? kk : 0u);
+    });
+    flo = wave_umin(flo);
+    fhi = wave_umax(fhi);
+    if (lane == 0) {
+      sm.wsum[0][wave] = flo;
+      sm.wsum[1][wave] = fhi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      flo = min(flo, sm.wsum[0][w]);
+      fhi = max(fhi, sm.wsum[1][w]);
+    }
+  }
+  constexpr int kPer = kTopkBins / kT;
+  // thread t owns bins [2048 - kPer(t+1), 2048 - kPer*t): low t = high bins
+  const int hb = kTopkBins - kPer * threadIdx.x - 1;
+
+  // first pass: bins linear in the score; hist[1] is cleared for the radix passes
+  LinearBins fb;
+  fb.init(flo, fhi);
+  for (int i = threadIdx.x; i < kTopkBins; i += kT) sm.hist[1][i] = 0;
+  for_keys<kT>(src, n, [&](uint32_t kk) { atomicAdd(&sm.hist[0][fb(kk)], 1u); });
+  __syncthreads();
+  {
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) local += sm.hist[0][hb - j];
+    const uint32_t incl = wave_incl_scan(local);
+    if (lane == 63) sm.wsum[0][wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w)
+      if (w < wave) before += sm.wsum[0][w];
+    const uint32_t above = before + incl - local;
+    if (above < krem && above + local >= krem) {
+      uint32_t cum = above;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t c = sm.hist[0][hb - j];
+        if (cum + c >= krem) {
+          sm.sel_bin[0] = (uint32_t)(hb - j);
+          sm.krem[0] = krem - cum;
+          break;
+        }
+        cum += c;
+      }
+    }
+    if (k2 > 0 && above < (uint32_t)k2 && above + local >= (uint32_t)k2) {
+      uint32_t cum = above;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const uint32_t c = sm.hist[0][hb - j];
+        if (cum + c >= (uint32_t)k2) {
+          sm.bound_lo = (uint32_t)(hb - j);  // the bin
+          sm.bound_cnt = cum + c;
+          break;
+        }
+        cum += c;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t b = sm.sel_bin[0];
+  krem = sm.krem[0];
+  const uint32_t cb = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.hist[0][b]);
+  const uint32_t b2 = k2 > 0 ? sm.bound_lo : 0u;
+  const bool few = cb <= kCandMax;
+  // the boundary bin's keys (when few), found among the keys of a cheap range; the bound:
+  // a key L2 at the lower edge of bin b2 (an estimate), with the count of keys >= L2
+  uint32_t r_lo, r_hi, L2 = 0u;
+  fb.key_range(b, &r_lo, &r_hi);
+  if (k2 > 0 && b2 > 0) {  // the key of the ideal value b2: bin b2's lower edge, up to rounding
+    L2 = fb.a > 0.f ? float_key(((float)b2 - fb.c) / fb.a) : kKeyNegInf;
+  }
+  uint32_t g2c = 0;
+  if (few || k2 > 0) {
+    for_keys<kT>(src, n, [&](uint32_t kk) {
+      if (few && kk >= r_lo && kk <= r_hi) {
+        if (fb(kk) == b) sm.cand[atomicAdd(&sm.ncand, 1u)] = kk;
+      }
+      if (k2 > 0) g2c += kk >= L2 ? 1u : 0u;
+    });
+  }
+  if (k2 > 0) {
+    g2c = wave_total(wave_incl_scan(g2c));
+    if (lane == 0) sm.wl2[wave] = g2c;
+  }
+  __syncthreads();
+  if (k2 > 0) {
+    uint32_t g = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) g += sm.wl2[w];
+    *L2_out = L2;
+    *g2_out = g;
+  }
+  if (few && sm.ncand != cb) {  // the range missed keys of the bin: gather them exactly
+    __syncthreads();  // every wave has read ncand
+    if (threadIdx.x == 0) sm.ncand = 0;
+    __syncthreads();
+    for_keys<kT>(src, n, [&](uint32_t kk) {
+      if (fb(kk) == b) sm.cand[atomicAdd(&sm.ncand, 1u)] = kk;
+    });
+    __syncthreads();
+  }
+  if (few) {
+    // every wave ranks the bin's keys: T is the key with fewer than krem keys of the bin
+    // above it and at least krem at or above it
+    const uint32_t v = (uint32_t)lane < cb ? sm.cand[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < cb; ++j) {
+      const uint32_t w = sm.cand[j];
+      gt += w > v ? 1u : 0u;
+      ge += w >= v ? 1u : 0u;
+    }
+    const bool hit = (uint32_t)lane < cb && gt < krem && krem <= ge;
+    const int src_lane = __builtin_ctzll(__ballot(hit));
+    *T_out = (uint32_t)__builtin_amdgcn_readlane((int)v, src_lane);
+    *take_out = krem - (uint32_t)__builtin_amdgcn_readlane((int)gt, src_lane);
+    return;
+  }
+  // a crowded bin: its key range
+  uint32_t bmin = 0xffffffffu, bmax = 0u;
+  for_keys<kT>(src, n, [&](uint32_t kk) {
+    const bool in = fb(kk) == b;
+    bmin = min(bmin, in ? kk : 0xffffffffu);
+    bmax = max(bmax, in ? kk : 0u);
+  });
+  bmin = wave_umin(bmin);
+  bmax = wave_umax(bmax);
+  if (lane == 0) {
+    sm.wlo[wave] = bmin;
+    sm.whi[wave] = bmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    bmin = min(bmin, sm.wlo[w]);
+    bmax = max(bmax, sm.whi[w]);
+  }
+  // radix passes over the crowded bin's key range
+  lo = bmin;
+  uint32_t span = bmax - bmin;
+  int cur = 1;
   while (span != 0) {
     const int bits = 32 - __builtin_clz(span);
     const int shift = bits > 11 ? bits - 11 : 0;
@@ -169,8 +386,6 @@ __device__ __forceinline__ void radix_threshold(const Src& src, int n, int k, To
       if (kk >= lo && kk <= top) atomicAdd(&sm.hist[cur][(kk - lo) >> shift], 1u);
     });
     __syncthreads();
-    // thread t owns bins [2048 - kPer(t+1), 2048 - kPer*t): low t = high bins
-    const int hb = kTopkBins - kPer * threadIdx.x - 1;
     uint32_t local = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) local += sm.hist[cur][hb - j];
@@ -179,7 +394,7 @@ __device__ __forceinline__ void radix_threshold(const Src& src, int n, int k, To
     __syncthreads();
     uint32_t before = 0;
 #pragma unroll
-    for (int w = 0; w < TopkSmem<kT>::kW; ++w)
+    for (int w = 0; w < kW; ++w)
       if (w < wave) before += sm.wsum[0][w];
     const uint32_t above = before + incl - local;
     if (above < krem && above + local >= krem) {
@@ -195,28 +410,10 @@ __device__ __forceinline__ void radix_threshold(const Src& src, int n, int k, To
         cum += c;
       }
     }
-    if (first && k2 > 0 && above < (uint32_t)k2 && above + local >= (uint32_t)k2) {
-      uint32_t cum = above;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const uint32_t c = sm.hist[cur][hb - j];
-        if (cum + c >= (uint32_t)k2) {
-          sm.bound_lo = lo + ((uint32_t)(hb - j) << shift);
-          sm.bound_cnt = cum + c;
-          break;
-        }
-        cum += c;
-      }
-    }
     __syncthreads();
-    const uint32_t b = sm.sel_bin[cur];
+    const uint32_t bb = sm.sel_bin[cur];
     krem = sm.krem[cur];
-    if (first && k2 > 0) {
-      *L2_out = sm.bound_lo;
-      *g2_out = sm.bound_cnt;
-    }
-    first = false;
-    const uint32_t blo = lo + (b << shift);
+    const uint32_t blo = lo + (bb << shift);
     const uint32_t bspan = shift == 0 ? 0u : ((1u << shift) - 1u);
     span = min(bspan, top - blo);
     lo = blo;

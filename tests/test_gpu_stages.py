@@ -260,6 +260,43 @@ def test_index_topk_many_rows(C):
     _check_full(C, d, q_pos, 1, 128, what="many rows")
 
 
+def _shaped_scores_inputs(g, B, T, N, k0, q0, k1=None, q1=0.0):
+    """Indexer inputs whose scores are ReLU(q0 * k0[n] + q1 * k1[n]) exactly: head 0 carries
+    two dims, every other head and dim is zero (each product and sum is exact in fp32)."""
+    H, D = 64, 128
+    q = np.zeros((B, T, H, D), np.float32)
+    q[:, :, 0, 0] = q0
+    q[:, :, 0, 1] = q1
+    k = np.zeros((B, N, D), np.float32)
+    k[:, :, 0] = k0
+    if k1 is not None:
+        k[:, :, 1] = k1
+    k[:, :, 2:] = g.ints((B, N, D - 2), -3, 3, dtype="f32")  # met only by zero queries
+    w = np.ones((B, T, H), np.float32)
+    return {"q_idx": q, "w": w, "k_idx": k}
+
+
+def test_index_topk_score_shapes(C):
+    banner("index FULL top-512 on shaped scores: a large offset over a narrow range, and scores over 80 binades")
+    g = W.rng(23)
+    r = np.random.default_rng(23)
+    # 2^22 + 0.5 j, j < 128: 128 distinct values, 2^16 times the range below the offset, so the
+    # first pass's key ranges can miss keys of the boundary bin (the exact gather takes over)
+    for B, T, N, q_pos, what in ((1, 8, 16400, [[4000, 5000, 6000, 7000, 8000, 3000, 2500, 16384]], "rows"),
+                                 (4, 1, 65536, [[65536], [65536], [40000], [30001]], "chunked decode")):
+        k1 = r.integers(0, 128, size=(B, N)).astype(np.float32)
+        d = _shaped_scores_inputs(g, B, T, N, 2048.0, 2048.0, k1, 0.5)
+        _check_full(C, d, np.asarray(q_pos, np.int32), 1, 512, what=f"offset scores, {what}")
+    # 2^e (1 + j/128), e in [-40, 40]: the linear first pass puts almost every key in its
+    # lowest bin, and the radix passes resolve it
+    for B, T, N, q_pos, what in ((1, 8, 16400, [[16384, 9000, 5000, 16400, 700, 12000, 4096, 2048]], "rows"),
+                                 (2, 1, 65536, [[65536], [50000]], "chunked decode")):
+        e = r.integers(-40, 41, size=(B, N)).astype(np.float64)
+        k0 = (np.exp2(e) * (1.0 + r.integers(0, 128, size=(B, N)) / 128.0)).astype(np.float32)
+        d = _shaped_scores_inputs(g, B, T, N, k0, 1.0)
+        _check_full(C, d, np.asarray(q_pos, np.int32), 1, 512, what=f"wide scores, {what}")
+
+
 def test_reindex_reuse_and_hier(C):
     banner("hier pool + REINDEX + REUSE: B=2 N=20000, 64 blocks kept, k=128")
     g = W.rng(15)
