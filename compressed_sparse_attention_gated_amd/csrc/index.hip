@@ -29,6 +29,7 @@
 #include "internal.h"
 #include "topk_core.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace csa2 {
@@ -366,7 +367,7 @@ __device__ __forceinline__ void load_query_f4(const Dev& a, int row, int lane, i
 }
 
 // the MFMAs of one 32-entry tile (two sub-tiles x HB head blocks)
-template <int DI, int HB>
+template <int DI, int HB, int AF = 4>
 __device__ __forceinline__ void f4_mfma(const i32x8* areg, const int* sreg, const RawF4& r, int g, f32x4 (*acc)[HB]) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
@@ -375,7 +376,7 @@ __device__ __forceinline__ void f4_mfma(const i32x8* areg, const int* sreg, cons
     const i32x8 bop = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
-      acc[sub][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(areg[hb], bop, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4,
+      acc[sub][hb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(areg[hb], bop, f32x4{0.f, 0.f, 0.f, 0.f}, AF, 4,
                                                                       0, sreg[hb], 0, (int)r.s[sub]);
   }
 }
@@ -397,6 +398,92 @@ __device__ __forceinline__ float f4_epilogue(const f32x4 (*acc)[HB], const float
 }
 // pipeline depth of the MXFP4 x MXFP4 scans (a raw tile is 10 registers)
 constexpr int kPipeDepthF4 = 6;
+
+// ---------------------------------------------------------------- bf16 q_I as E4M3 x MXFP4 K_I
+// A bf16 q_I whose values are all E4M3 values at unit scale (zero, or |x| in [2^-6, 448]
+// with at most three mantissa bits: the integer-valued queries among them) goes to the same
+// scaled MFMA with an FP8 A operand (format 0, E8M0 scale 127).  An 8-bit A operand has
+// another lane layout than a 4-bit one (checked with a standalone probe): lane (n, g) holds
+// dims 16g .. 16g + 15 of row n in bytes 0..15 and dims 64 + 16g .. 64 + 16g + 15 in bytes
+// 16..31, against the B operand's dims 32g .. 32g + 31.  Every product is then the same exact
+// product as with bf16 operands, so the scores are those of the bf16 path; the per-tile
+// conversion of the MXFP4 keys to bf16 disappears.  Any other query takes the bf16 path.
+
+// the E4M3 byte of a bf16 value; clears `exact` when the value has none
+__device__ __forceinline__ uint32_t bf16_to_e4m3(uint32_t h, bool& exact) {
+  const uint32_t mag = h & 0x7fffu;
+  const int e = (int)(mag >> 7) - 127;
+  const uint32_t m = mag & 0x7fu;
+  const bool ok = mag == 0u || (e >= -6 && e <= 8 && (m & 0xfu) == 0u && !(e == 8 && (m >> 4) == 7u));
+  exact = exact && ok;
+  return mag == 0u ? 0u : (((h >> 8) & 0x80u) | ((uint32_t)(e + 7) << 3) | (m >> 4));
+}
+
+// Wave w < HB converts head block w of the query into the A-operand layout, staged in LDS
+// (stage: HB x 64 lanes x 8 words; flags: HB words).  Returns whether every value was exact
+// (block-uniform).  All threads must call it (one barrier); the stage is then read by
+// read_query_e4m3, and must not be overwritten before a barrier after that.
+template <int DI, int HB>
+__device__ __forceinline__ bool stage_query_e4m3(const Dev& a, int row, int lane, int wave, uint32_t* stage,
+                                                 uint32_t* flags) {
+  const int n = lane & 15, g = lane >> 4;
+  if (wave < HB) {
+    const int head = 16 * wave + n;
+    bool exact = true;
+    uint32_t wd[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int d0 = 64 * half + 16 * g;  // dims d0 .. d0 + 15 go to bytes 16 half .. + 15
+      if (head < a.H_I && d0 < DI) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.q_idx + ((size_t)row * a.H_I + head) * DI + d0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint4 v = src[q];  // dims d0 + 8q .. + 7, two bf16 per word
+          const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t lo = u[2 * i], hi = u[2 * i + 1];
+            wd[4 * half + 2 * q + i] = bf16_to_e4m3(lo & 0xffffu, exact) | (bf16_to_e4m3(lo >> 16, exact) << 8) |
+                                       (bf16_to_e4m3(hi & 0xffffu, exact) << 16) |
+                                       (bf16_to_e4m3(hi >> 16, exact) << 24);
+          }
+        }
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(stage + (wave * 64 + lane) * 8);
+    dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    const bool all = __ballot(!exact) == 0ull;
+    if (lane == 0) flags[wave] = all ? 1u : 0u;
+  }
+  __syncthreads();
+  bool all = true;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) all = all && flags[hb] != 0u;
+  return all;
+}
+template <int HB>
+__device__ __forceinline__ void read_query_e4m3(const uint32_t* stage, int lane, i32x8* areg) {
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const uint4* src = reinterpret_cast<const uint4*>(stage + (hb * 64 + lane) * 8);
+    const uint4 x = src[0], y = src[1];
+    areg[hb] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  }
+}
+
+// the head weights of the 16 x 16 result rows held by lane (n, g)
+template <int HB>
+__device__ __forceinline__ void load_w_f4(const Dev& a, int row, int lane, float (*wreg)[4]) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hr = 16 * hb + 4 * g + j;
+      wreg[hb][j] = hr < a.H_I ? a.w[(size_t)row * a.H_I + hr] : 0.f;
+    }
+}
 
 // ---------------------------------------------------------------- private-B scan
 template <int DI, int KF, int MT, bool kCand, bool kBlockMax>
@@ -466,6 +553,35 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
   }
 }
 
+// the MXFP4-K_I tiles t0, t0 + 128, ... below c1 through the scaled MFMA (A format AF),
+// each tile's epilogue one tile late; finish(score, tile) takes the scores
+template <int DI, int HB, int AF, class Finish>
+__device__ __forceinline__ void scan_tiles_f4(const Dev& a, int b, int t0, int c1, int lane, const i32x8* areg,
+                                              const int* sreg, const float (*wreg)[4], Finish finish) {
+  constexpr int kStride = 32 * kWaves;
+  const int n16 = lane & 15, g16 = lane >> 4;
+  f32x4 pacc[2][HB];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int ptb = t0;
+  auto load = [&](int tb, RawF4& raw) {
+    load_raw_f4<DI>(a, b, min(tb + n16, c1 - 1), min(tb + 16 + n16, c1 - 1), g16, raw);
+  };
+  tile_pipeline<kPipeDepthF4, RawF4>(t0, c1, kStride, load, [&](const RawF4& raw, int tb) {
+    f32x4 cacc[2][HB];
+    f4_mfma<DI, HB, AF>(areg, sreg, raw, g16, cacc);
+    finish(f4_epilogue<HB>(pacc, wreg, lane), ptb);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = cacc[sub][hb];
+    ptb = tb;
+  });
+  finish(f4_epilogue<HB>(pacc, wreg, lane), ptb);
+}
+
 // ---------------------------------------------------------------- fused scan + chunk top-k
 // Decode: workgroup (query, chunk) scans its chunk like scan_private but keeps the keys of
 // its scores in LDS, then selects the chunk's top-k there and writes (key, slot) pairs;
@@ -514,34 +630,35 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
     }
     if constexpr (kBlockMax) emit_block_max(a, row, lane, slot, c1, s);
   };
-  if (t0 < c1) {
+  // bf16 q_I with an MXFP4 K_I: the FP8 x FP4 MFMA when every q_I value is an E4M3 value
+  // (the staging uses the key array, before any key is written)
+  constexpr int HB8 = 2 * MT;
+  constexpr bool kTryF8 = KF == 1 && HB8 <= kWaves;
+  bool f8 = false;
+  if constexpr (kTryF8) {
+    f8 = stage_query_e4m3<DI, HB8>(a, row, lane, wave, skeys, sm.cand);
+    if (f8) {  // block-uniform
+      i32x8 areg8[HB8];
+      read_query_e4m3<HB8>(skeys, lane, areg8);
+      __syncthreads();  // the stage is read: keys may overwrite it
+      if (t0 < c1) {
+        int sreg[HB8];
+        float wreg[HB8][4];
+#pragma unroll
+        for (int hb = 0; hb < HB8; ++hb) sreg[hb] = 127;  // unit scale
+        load_w_f4<HB8>(a, row, lane, wreg);
+        scan_tiles_f4<DI, HB8, 0>(a, b, t0, c1, lane, areg8, sreg, wreg, finish);
+      }
+    }
+  }
+  if (!f8 && t0 < c1) {
     if constexpr (KF == 2) {
       constexpr int HB = 2 * MT;
       i32x8 areg[HB];
       int sreg[HB];
       float wreg[HB][4];
       load_query_f4<DI, HB>(a, row, lane, areg, sreg, wreg);
-      const int n16 = lane & 15, g16 = lane >> 4;
-      f32x4 pacc[2][HB];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int ptb = t0;
-      auto load = [&](int tb, RawF4& raw) {
-        load_raw_f4<DI>(a, b, min(tb + n16, c1 - 1), min(tb + 16 + n16, c1 - 1), g16, raw);
-      };
-      tile_pipeline<kPipeDepthF4, RawF4>(t0, c1, kStride, load, [&](const RawF4& raw, int tb) {
-        f32x4 cacc[2][HB];
-        f4_mfma<DI, HB>(areg, sreg, raw, g16, cacc);
-        finish(f4_epilogue<HB>(pacc, wreg, lane), ptb);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = cacc[sub][hb];
-        ptb = tb;
-      });
-      finish(f4_epilogue<HB>(pacc, wreg, lane), ptb);
+      scan_tiles_f4<DI, HB, 4>(a, b, t0, c1, lane, areg, sreg, wreg, finish);
     } else {
       bf16x8 areg[MT][DI / 16];
       float wreg[MT][16];
@@ -824,7 +941,9 @@ hipError_t launch_sel4(const Dev& d, dim3 grid, size_t lds, bool bm, bool sc, in
 template <int DI, int KF, int MT>
 hipError_t launch_sel3(const ScanArgs& s, const Dev& d, int k, int chunk, int nchunks, uint32_t* keys,
                        int32_t* slots, uint2* bounds, hipStream_t st) {
-  const size_t lds = ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15) + (size_t)chunk * 4;
+  // the key array also stages an E4M3 q_I (2 MT head blocks x 64 lanes x 32 bytes)
+  const size_t key_bytes = std::max((size_t)chunk * 4, KF == 1 ? (size_t)(2 * MT) * 64 * 32 : (size_t)0);
+  const size_t lds = ((sizeof(TopkSmem<kSelThreads>) + 15) & ~(size_t)15) + key_bytes;
   dim3 grid(s.B * s.T, nchunks);
   const bool bm = s.block_max != nullptr, sc = s.scores != nullptr;
   // the large register variant only for a bf16 K_I with 128 dims and 33..64 heads (the

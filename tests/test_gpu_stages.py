@@ -218,6 +218,28 @@ def test_index_mxfp4_query(C, HI, dI):
         np.testing.assert_array_equal(gi[b, 0], want, err_msg=f"reindex b={b}")
 
 
+@pytest.mark.parametrize("HI,dI", [(64, 128), (48, 64), (16, 32)])
+def test_index_e4m3_query_path(C, HI, dI):
+    """bf16 q_I with an MXFP4 K_I in the fused decode scan: a query whose every value is an
+    E4M3 value takes the FP8 x FP4 MFMA, any other the bf16 path; one launch holds both kinds
+    (integers; E4M3 values over 2^-1 .. 2^3 with three mantissa bits; multiples of 1/32; and
+    integers but for one value with six mantissa bits).  Every score is exact in fp32, so both
+    paths must give the oracle's scores and indices exactly."""
+    banner(f"index bf16 q_I (E4M3-exact and not) x MXFP4 K_I, fused decode: H_I={HI} d_I={dI}")
+    g = W.rng(70 + HI + dI)
+    r = np.random.default_rng(70 + HI + dI)
+    d = W.indexer_inputs(g, 4, 1, 9000, HI, dI, W.WORKLOADS[5].w_values, k_format="mxfp4")
+    shape = d["q_idx"].shape[2:]
+    e4m3 = np.exp2(r.integers(-1, 3, size=shape)) * (1 + r.integers(0, 8, size=shape) / 8.0)
+    d["q_idx"][1, 0] = (e4m3 * r.choice([-1.0, 1.0], size=shape)).astype(np.float32)
+    d["q_idx"][2, 0] = (r.integers(-127, 128, size=shape) / 32.0).astype(np.float32)  # bf16, mostly not E4M3
+    d["q_idx"][3, 0] = d["q_idx"][0, 0]
+    d["q_idx"][3, 0, HI // 2, dI // 2] = 1.0 + 1.0 / 64  # one value with a longer mantissa
+    kd = F.mxfp4_decode(d["k_codes"], d["k_scales"])
+    _check_full(C, d, np.array([[9000], [9000], [8191], [5000]], np.int32), 1, 256, k_dense=kd, mx=True,
+                what=f"e4m3 / bf16 q {HI}x{dI}")
+
+
 def test_index_full_mxfp4(C):
     banner("index FULL MXFP4 K_I decode B=2 N=3000 k=128 and prefill T=64")
     g = W.rng(13)
