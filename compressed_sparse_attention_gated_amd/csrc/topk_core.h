@@ -628,18 +628,38 @@ __device__ __forceinline__ void ordered_compact_regs(const KeyRegs<kT, kJ>& r, i
     }
   }
   __syncthreads();
-  const int nseg = kW * r.rows;
-  const uint32_t mine = (int)threadIdx.x < nseg ? sm.seg[threadIdx.x] : 0u;
-  uint32_t total;
-  const uint32_t ex = block_excl_scan<kT>(mine, &total, sm);
-  if ((int)threadIdx.x < nseg) sm.seg[threadIdx.x] = ex;
-  __syncthreads();
+  // Few segments (at most 32): every wave forms the offsets of its own segments from the
+  // segment totals, row by row, with a few broadcast reads - no block-wide scan and no second
+  // barrier.  More segments: one block scan over them.
+  constexpr bool kDirect = kW * kJ <= 32;
+  if constexpr (!kDirect) {
+    const int nseg = kW * r.rows;
+    const uint32_t mine = (int)threadIdx.x < nseg ? sm.seg[threadIdx.x] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<kT>(mine, &total, sm);
+    if ((int)threadIdx.x < nseg) sm.seg[threadIdx.x] = ex;
+    __syncthreads();
+  }
   const int i0 = 4 * (int)threadIdx.x;
   bool done = false;  // wave-uniform: every later row lies past the k-th selected key
+  uint32_t rowbase = 0;  // direct offsets: the totals of the rows before row j
 #pragma unroll
   for (int j = 0; j < kJ; ++j) {
     if (done || j >= r.rows) continue;
-    const uint32_t sg = sm.seg[kW * j + wave];
+    uint32_t sg;
+    if constexpr (kDirect) {
+      uint32_t before = 0, rowtot = 0;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const uint32_t v = sm.seg[kW * j + w];
+        before += w < wave ? v : 0u;
+        rowtot += v;
+      }
+      sg = rowbase + before;
+      rowbase += rowtot;
+    } else {
+      sg = sm.seg[kW * j + wave];
+    }
     uint32_t g = sg & 0xffffu, e = sg >> 16;
     if (g + min(e, take_eq) >= (uint32_t)k) {
       done = true;
