@@ -111,7 +111,9 @@ topk_single(Params p, int stage_cap, int defer) {
   TopkSmem<kT>& sm = *reinterpret_cast<TopkSmem<kT>*>(smem_raw);
   uint32_t* skeys = reinterpret_cast<uint32_t*>(smem_raw + smem_keys_off(sizeof(TopkSmem<kT>)));
   int32_t* sel = reinterpret_cast<int32_t*>(skeys + ((stage_cap + 3) & ~3));
-  const int r = blockIdx.x;
+  // the last rows first: in a causal prefill they are the longest, so the short ones fill
+  // the tail of the launch
+  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;
   const int n = row_len(p, r);
   int32_t* out = p.out_idx + (size_t)r * p.k;
   if (n <= p.k) {
