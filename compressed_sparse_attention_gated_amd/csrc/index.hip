@@ -367,6 +367,32 @@ __device__ __forceinline__ void load_query_f4(const Dev& a, int row, int lane, i
 }
 
 // the MFMAs of one 32-entry tile (two sub-tiles x HB head blocks)
+// The same tile through buffer loads: codes and scales of entries c0 + o0, c0 + o1 from
+// descriptors based at the chunk's first entry (one per workgroup, in scalar registers), so
+// each load needs only a 32-bit lane offset
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+struct F4Bufs {
+  __amdgpu_buffer_rsrc_t codes, scales;
+};
+template <int DI>
+__device__ __forceinline__ F4Bufs f4_bufs(const Dev& a, int b, int c0) {
+  const size_t e = (size_t)b * a.N + c0;
+  constexpr int kRawDword3 = 0x00020000;  // raw 32-bit data format
+  return F4Bufs{__builtin_amdgcn_make_buffer_rsrc((void*)(a.k_codes + e * (DI / 2)), (short)0, -1, kRawDword3),
+                __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_scales + e * (DI / 32)), (short)0, -1, kRawDword3)};
+}
+template <int DI>
+__device__ __forceinline__ void load_raw_f4_buf(const F4Bufs& fb, int o0, int o1, int g, RawF4& r) {
+  const int gg = min(g, DI / 32 - 1);
+  const int off[2] = {o0, o1};
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(fb.codes, off[sub] * (DI / 2) + 16 * gg, 0, 0);
+    r.c[sub] = make_uint4(v.x, v.y, v.z, v.w);
+    r.s[sub] = __builtin_amdgcn_raw_buffer_load_b8(fb.scales, off[sub] * (DI / 32) + gg, 0, 0);
+  }
+}
+
 template <int DI, int HB, int AF = 4>
 __device__ __forceinline__ void f4_mfma(const i32x8* areg, const int* sreg, const RawF4& r, int g, f32x4 (*acc)[HB]) {
 #pragma unroll
@@ -556,10 +582,12 @@ __global__ void __launch_bounds__(kPrivThreads) scan_private(Dev a, int chunk) {
 // the MXFP4-K_I tiles t0, t0 + 128, ... below c1 through the scaled MFMA (A format AF),
 // each tile's epilogue one tile late; finish(score, tile) takes the scores
 template <int DI, int HB, int AF, class Finish>
-__device__ __forceinline__ void scan_tiles_f4(const Dev& a, int b, int t0, int c1, int lane, const i32x8* areg,
-                                              const int* sreg, const float (*wreg)[4], Finish finish) {
+__device__ __forceinline__ void scan_tiles_f4(const Dev& a, int b, int c0, int t0, int c1, int lane,
+                                              const i32x8* areg, const int* sreg, const float (*wreg)[4],
+                                              Finish finish) {
   constexpr int kStride = 32 * kWaves;
   const int n16 = lane & 15, g16 = lane >> 4;
+  const F4Bufs fbuf = f4_bufs<DI>(a, b, c0);
   f32x4 pacc[2][HB];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
@@ -567,7 +595,7 @@ __device__ __forceinline__ void scan_tiles_f4(const Dev& a, int b, int t0, int c
     for (int hb = 0; hb < HB; ++hb) pacc[sub][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   int ptb = t0;
   auto load = [&](int tb, RawF4& raw) {
-    load_raw_f4<DI>(a, b, min(tb + n16, c1 - 1), min(tb + 16 + n16, c1 - 1), g16, raw);
+    load_raw_f4_buf<DI>(fbuf, min(tb + n16, c1 - 1) - c0, min(tb + 16 + n16, c1 - 1) - c0, g16, raw);
   };
   tile_pipeline<kPipeDepthF4, RawF4>(t0, c1, kStride, load, [&](const RawF4& raw, int tb) {
     f32x4 cacc[2][HB];
@@ -647,7 +675,7 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
 #pragma unroll
         for (int hb = 0; hb < HB8; ++hb) sreg[hb] = 127;  // unit scale
         load_w_f4<HB8>(a, row, lane, wreg);
-        scan_tiles_f4<DI, HB8, 0>(a, b, t0, c1, lane, areg8, sreg, wreg, finish);
+        scan_tiles_f4<DI, HB8, 0>(a, b, c0, t0, c1, lane, areg8, sreg, wreg, finish);
       }
     }
   }
@@ -658,7 +686,7 @@ __global__ void __launch_bounds__(kSelThreads) scan_select(Dev a, int chunk, int
       int sreg[HB];
       float wreg[HB][4];
       load_query_f4<DI, HB>(a, row, lane, areg, sreg, wreg);
-      scan_tiles_f4<DI, HB, 4>(a, b, t0, c1, lane, areg, sreg, wreg, finish);
+      scan_tiles_f4<DI, HB, 4>(a, b, c0, t0, c1, lane, areg, sreg, wreg, finish);
     } else {
       bf16x8 areg[MT][DI / 16];
       float wreg[MT][16];
